@@ -1,0 +1,120 @@
+"""Invariants of the seeded input generators (CPU only)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_311_amd import workloads as wl
+
+BS = wl.BLOCK_SIZE
+
+
+@pytest.mark.parametrize("key", list(wl.WORKLOADS))
+def test_metadata_invariants(key):
+    w = wl.WORKLOADS[key]
+    md = wl.draw_metadata(w, w.default_seed)
+    lens = md["context_lens"].astype(np.int64)
+    bt = md["block_tables"]
+    nb = md["num_blocks"]
+    assert bt.shape == (w.num_seqs, w.table_width)
+    assert lens.min() >= 1 and lens.max() <= w.max_len
+    used = []
+    for s, L in enumerate(lens):
+        n = -(-int(L) // BS)
+        row = bt[s]
+        assert (row[:n] >= 0).all() and (row[:n] < nb).all()
+        assert (row[n:] == -1).all()
+        used.extend(row[:n].tolist())
+    counts = np.bincount(np.asarray(used), minlength=nb)
+    if w.step == "cow":
+        # only prompt blocks are shared, each by at most `samples` sequences
+        assert counts.max() <= w.samples
+        assert (counts > 1).sum() == md["shared_blocks"]
+    else:
+        assert counts.max() == 1          # every block has one owner
+    # at most 15 empty slots per sequence; under 4% of the pool on every
+    # workload of realistic lengths (the 4-sequence tiny case is too short)
+    assert max(oracle.empty_slots(int(L)) for L in lens) <= BS - 1
+    if key != "tiny":
+        assert oracle.waste_fraction(lens) < 0.04
+    if w.pool[0] == "factor":
+        need = len(set(used))
+        assert nb == int(np.ceil(w.pool[1] * need)) or w.step == "cow"
+
+
+def test_tiny_pool_and_lengths():
+    w = wl.WORKLOADS["tiny"]
+    md = wl.draw_metadata(w, w.default_seed)
+    assert md["num_blocks"] == 64 and md["block_tables"].shape == (4, 7)
+    L = wl.draw_context_lens(w, np.random.default_rng(0), n=20000)
+    assert L.min() == 1 and L.max() == 100
+
+
+def test_lognormal_lengths():
+    w = wl.WORKLOADS["llama13b_conv"]
+    L = wl.draw_context_lens(w, np.random.default_rng(1), n=200000)
+    assert abs(np.median(L) - 600) < 10
+    assert L.max() == 4096 and L.min() >= 1
+    assert 0.004 < (L == 4096).mean() < 0.012
+
+
+def test_append_slots():
+    w = wl.WORKLOADS["llama13b_conv"]
+    md = wl.draw_metadata(w, w.default_seed)
+    lens, bt, slots = md["context_lens"], md["block_tables"], md["slot_mapping"]
+    assert len(np.unique(slots)) == len(slots)
+    for s in range(len(lens)):
+        pos = int(lens[s]) - 1
+        assert slots[s] == bt[s, pos // BS] * BS + pos % BS
+        blk, off = divmod(int(slots[s]), BS)
+        # the new token's slot is empty before the step, earlier ones full
+        assert not md["live_slots"][blk, off]
+        assert md["live_slots"][blk, :off].all()
+
+
+def test_cow_pairs_follow_reference_counts():
+    w = wl.WORKLOADS["sampling_cow"]
+    md = wl.draw_metadata(w, w.default_seed)
+    P = md["prompt_lens"]
+    pairs = md["cow_pairs"]
+    # samples 0..6 copy a shared partial last block, the 8th writes in place
+    assert len(pairs) == (w.samples - 1) * int((P % BS != 0).sum())
+    assert len(np.unique(pairs[:, 1])) == len(pairs)
+    assert not np.intersect1d(pairs[:, 0], pairs[:, 1]).size
+    # every private token's slot is distinct and not in a shared block
+    slots = md["slot_mapping"]
+    assert len(np.unique(slots)) == len(slots)
+    lens = md["context_lens"]
+    bt = md["block_tables"]
+    seq = md["token_seq"]
+    assert len(slots) == int(sum(lens[s] - P[s // w.samples]
+                                 for s in range(w.num_seqs)))
+    counts = np.bincount(bt[bt >= 0].ravel(), minlength=md["num_blocks"])
+    assert (counts[slots // BS] == 1).all()
+    for s in (0, 7, 100, 255):
+        first = int(np.flatnonzero(seq == s)[0])
+        pos = int(P[s // w.samples])
+        assert slots[first] == bt[s, pos // BS] * BS + pos % BS
+
+
+def test_tiny_batch_values_poisoned():
+    w = wl.WORKLOADS["tiny"]
+    b = wl.make_batch(w, device="cpu")
+    live = torch.from_numpy(b["live_slots"])
+    kc = b["key_cache"]
+    assert torch.isfinite(kc[live[:, None, :].expand(-1, w.num_kv_heads, -1)]).all()
+    assert torch.isnan(kc[(~live)[:, None, :].expand(-1, w.num_kv_heads, -1)]).all()
+    assert b["query"].shape == (4, 4, 64) and b["query"].dtype == torch.float32
+    # the same seed gives the same batch
+    b2 = wl.make_batch(w, device="cpu")
+    assert torch.equal(b["query"], b2["query"])
+    assert np.array_equal(wl.to_host(kc).view(np.uint32),
+                          wl.to_host(b2["key_cache"]).view(np.uint32))
+
+
+def test_bf16_to_host_bits():
+    t = torch.tensor([1.0, -2.0, float("inf")], dtype=torch.bfloat16)
+    h = wl.to_host(t)
+    assert h.dtype == np.uint16
+    assert h.tolist() == [0x3F80, 0xC000, 0x7F80]
