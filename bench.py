@@ -1,0 +1,309 @@
+"""Benchmark of the paged decode path on one MI355X.
+
+One step = one pass of the whole path over one seeded synthetic batch:
+copy_blocks (workloads with copy-on-write pairs), reshape_and_cache of the
+step's new tokens (one per sequence -- the token each sequence appends in
+this decode step -- or the private tokens of the sampling workload), then
+paged_attention_decode over every sequence.  Inputs are resident in HBM
+before the timed region; K steps are timed between two synchronizations.
+
+Prints ONE JSON line.  `value` is whole-step KV throughput in GB/s: the
+key/value bytes the attention must read (sum of context lengths x 2 x
+kv_heads x head_size x element bytes) divided by the step time.
+`roofline` covers the dominant kernel call, paged_attention_decode, timed
+with events on the launch stream; `cpu_baseline` times the float64 CPU
+oracle on a bounded sample of the same batch (single thread).
+
+    python bench.py [--steps K] [--warmup W] [--workload opt13b]
+                    [--also long_gqa,llama13b_conv,sampling_cow] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_311_amd", "csrc", "paged_attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="opt13b")
+    ap.add_argument("--also", default="long_gqa,llama13b_conv,sampling_cow")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--partition-size", type=int, default=0)
+    return ap.parse_args()
+
+
+def kv_bytes(w, lens):
+    eb = 4 if w.dtype == "f32" else 2
+    return int(np.asarray(lens, np.int64).sum()) * 2 * w.num_kv_heads * w.head_size * eb
+
+
+def decode_algorithmic_bytes(w, lens):
+    """Bytes the decode must move: K/V of every context token, q in, out,
+    the block-table entries it follows and the lengths."""
+    eb = 4 if w.dtype == "f32" else 2
+    lens = np.asarray(lens, np.int64)
+    qo = 2 * w.num_seqs * w.num_heads * w.head_size * eb
+    tables = 4 * int((-(-lens // 16)).sum()) + 4 * w.num_seqs
+    return kv_bytes(w, lens) + qo + tables
+
+
+class Step:
+    """Device-resident batch and the calls of one step (no allocation inside)."""
+
+    def __init__(self, w, seed, ps):
+        import torch
+        import paged_kv_cache_311_amd as pkv
+        from paged_kv_cache_311_amd import workloads as wl
+        self.pkv, self.torch, self.w = pkv, torch, w
+        dev = "cuda:0"
+        b = wl.make_batch(w, seed, dev)
+        self.b = b
+        lens = b["context_lens"]
+        self.lens = lens
+        self.bt = torch.from_numpy(b["block_tables"]).to(dev)
+        self.cl = torch.from_numpy(lens).to(dev)
+        self.out = torch.empty_like(b["query"])
+        self.ps = ps or w.partition_size
+        need = pkv.workspace_bytes(w.num_seqs, w.num_heads, w.head_size,
+                                   b["block_tables"].shape[1], self.ps)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if "slot_mapping" in b:
+            slots = b["slot_mapping"]
+            self.key, self.value = b["key"], b["value"]
+        else:  # plain decode workload: append token L-1 of every sequence
+            bt = b["block_tables"]
+            pos = lens.astype(np.int64) - 1
+            slots = bt[np.arange(len(lens)), pos // 16].astype(np.int64) * 16 + pos % 16
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed + 1)
+            shape = (w.num_seqs, w.num_kv_heads, w.head_size)
+            self.key = torch.randn(shape, generator=g, device=dev).to(b["query"].dtype)
+            self.value = torch.randn(shape, generator=g, device=dev).to(b["query"].dtype)
+        self.slots = torch.from_numpy(np.asarray(slots, np.int64)).to(dev)
+        pairs = b.get("cow_pairs")
+        self.pairs = (torch.from_numpy(pairs).to(dev)
+                      if pairs is not None and len(pairs) else None)
+        self.new_tokens = len(slots)
+
+    def updates(self):
+        b = self.b
+        if self.pairs is not None:
+            self.pkv.copy_blocks(b["key_cache"], b["value_cache"], self.pairs)
+        self.pkv.reshape_and_cache(self.key, self.value, self.slots, b["key_cache"],
+                                   b["value_cache"])
+
+    def decode(self):
+        b, w = self.b, self.w
+        self.pkv.paged_attention_decode(self.out, b["query"], b["key_cache"],
+                                        b["value_cache"], self.bt, self.cl, float(w.scale),
+                                        w.num_kv_heads, partition_size=self.ps,
+                                        workspace=self.ws)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.updates()
+            self.decode()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_start.record()
+        for i in range(steps):
+            self.updates()
+            ev[i][0].record()
+            self.decode()
+            ev[i][1].record()
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = t_start.elapsed_time(t_end) / steps
+        dec = np.asarray([a.elapsed_time(c) for a, c in ev])
+        return step_ms, dec, wall
+
+
+def measure(w, seed, steps, warmup, ps):
+    st = Step(w, seed, ps)
+    step_ms, dec_ms, wall = st.run(steps, warmup)
+    kvb = kv_bytes(w, st.lens)
+    algo = decode_algorithmic_bytes(w, st.lens)
+    dec_avg = float(dec_ms.mean())
+    r = {
+        "workload": w.key, "seed": seed, "seqs": w.num_seqs,
+        "heads": w.num_heads, "kv_heads": w.num_kv_heads, "head_size": w.head_size,
+        "dtype": w.dtype, "partition_size": st.ps,
+        "kv_tokens": int(st.lens.astype(np.int64).sum()), "kv_bytes_per_step": kvb,
+        "new_tokens_per_step": st.new_tokens,
+        "cow_pairs_per_step": 0 if st.pairs is None else int(st.pairs.shape[0]),
+        "ms_per_step": step_ms, "kv_GBps": kvb / (step_ms * 1e-3) / 1e9,
+        "decode_tokens_per_s": w.num_seqs / (step_ms * 1e-3),
+        "decode_call_ms_avg": dec_avg, "decode_call_ms_min": float(dec_ms.min()),
+        "decode_call_ms_max": float(dec_ms.max()),
+        "decode_algorithmic_bytes": algo,
+        "decode_GBps": algo / (dec_avg * 1e-3) / 1e9,
+        "host_wall_s": wall,
+    }
+    r["pct_of_hbm_peak"] = 100.0 * r["kv_GBps"] / HBM_PEAK_GBPS
+    r["decode_pct_of_hbm_peak"] = 100.0 * r["decode_GBps"] / HBM_PEAK_GBPS
+    return r, st
+
+
+def traffic_for_current_kernel(workload):
+    """HBM bytes per decode call from committed PMC counters, if the kernel
+    source is unchanged since they were taken (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = t.get("workloads", {}).get(workload)
+    if not entry or t.get("kernel_source_sha256") != h:
+        return None
+    return entry.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(st, budget_s):
+    """The float64 oracle, single thread, on the first sequences of the batch."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from paged_kv_cache_311_amd import workloads as wl
+    w, b = st.w, st.b
+    bt, lens = b["block_tables"], b["context_lens"]
+    n_max = min(w.num_seqs, 64)
+    ids = sorted({int(x) for s in range(n_max) for x in bt[s, :-(-int(lens[s]) // 16)]})
+    remap = {x: i for i, x in enumerate(ids)}
+    idx = st.torch.tensor(ids, dtype=st.torch.int64, device="cuda:0")
+    kc = wl.to_host(b["key_cache"].index_select(0, idx))
+    vc = wl.to_host(b["value_cache"].index_select(0, idx))
+    tables = np.full_like(bt[:n_max], -1)
+    for s in range(n_max):
+        n = -(-int(lens[s]) // 16)
+        tables[s, :n] = [remap[int(x)] for x in bt[s, :n]]
+    q = wl.to_host(b["query"])[:n_max]
+    done, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s in range(n_max):
+            oracle.decode_attention(q, kc, vc, tables, lens[:n_max], w.scale,
+                                    w.num_kv_heads, w.dtype, seqs=[s])
+            done += 1
+            t_used = time.perf_counter() - t0
+            if t_used >= budget_s:
+                break
+    kvb = kv_bytes(w, lens[:done])
+    return {
+        "value": kvb / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"float64 numpy oracle, one thread, first {done} of {w.num_seqs} "
+                   f"sequences of the {w.key} batch ({int(lens[:done].sum())} tokens, "
+                   f"{t_used:.1f} s)"),
+        "seconds": t_used, "decode_tokens_per_s": done / t_used,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(this path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import paged_kv_cache_311_amd as pkv
+    from paged_kv_cache_311_amd import workloads as wl
+    pkv.load_library()
+
+    w = wl.WORKLOADS[a.workload]
+    print(f"# measuring {w.key}", file=sys.stderr, flush=True)
+    main_r, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(st, a.cpu_seconds)
+    del st
+    torch.cuda.empty_cache()
+
+    others = {}
+    for key in [k for k in a.also.split(",") if k and k != w.key]:
+        print(f"# measuring {key}", file=sys.stderr, flush=True)
+        ow = wl.WORKLOADS[key]
+        r, st = measure(ow, ow.default_seed, a.steps, a.warmup, a.partition_size)
+        others[key] = r
+        del st
+        torch.cuda.empty_cache()
+
+    dec_ms = main_r["decode_call_ms_avg"]
+    achieved = main_r["decode_GBps"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_r["kv_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) K/V, random block placement, NaN-filled free slots)",
+        "config": {
+            "workload": (f"{w.key}: {w.num_seqs} seqs, {w.num_heads} heads / "
+                         f"{w.num_kv_heads} kv heads x {w.head_size}, {w.dtype}, "
+                         f"16-token blocks, lengths {w.lengths}, pool {w.pool}"),
+            "seqs": w.num_seqs, "kv_tokens": main_r["kv_tokens"],
+            "kv_bytes_per_step": main_r["kv_bytes_per_step"],
+            "partition_size": main_r["partition_size"], "seed": main_r["seed"],
+        },
+        "pct_of_hbm_peak": round(main_r["pct_of_hbm_peak"], 2),
+        "decode_tokens_per_s": round(main_r["decode_tokens_per_s"], 1),
+        "roofline": {
+            "kernel": "paged_attention_decode call (partition kernel + merge kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_for_current_kernel(w.key),
+            "algorithmic_bytes_per_call": main_r["decode_algorithmic_bytes"],
+            "avg_call_ms": round(dec_ms, 5),
+        },
+        "cpu_baseline": cpu,
+        "workloads": {w.key: main_r, **others},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

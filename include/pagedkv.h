@@ -1,0 +1,183 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache decode library for MI355X (gfx950).
+ *
+ * Three operations on a shared pool of fixed 16-token key/value blocks:
+ *
+ *   paged_attention_decode  one decode step of attention per (sequence,
+ *                           query head), reading keys and values through
+ *                           each sequence's block table;
+ *   reshape_and_cache       scatter new tokens' keys/values to their slots;
+ *   copy_blocks             block-level copy-on-write of shared blocks.
+ *
+ * Sources (titles of the pages this library follows):
+ *   [TEQ]  "Your GPU was mostly empty: how PagedAttention turned KV-cache
+ *          waste into 2-4x throughput" (blog.teqners.com)
+ *   [IV]   "vLLM and PagedAttention" (interviewsvector.com)
+ *   [AITJ] "PagedAttention KV cache memory management" (aitechjournal.org)
+ *   [VAS]  Vaswani et al., "Attention Is All You Need" (2017), eq. (1)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer argument is device memory owned by the caller
+ * (the library allocates nothing and keeps no state; calls are reentrant).
+ * All tensors are dense, row-major, with no padding between rows.
+ *
+ * Element types (`dtype`): PKV_F32, PKV_F16 (IEEE binary16), PKV_BF16.
+ * Queries, outputs, keys, values and both pools share one element type.
+ *
+ * Pool layout.  key_cache and value_cache are each
+ *     [num_blocks][num_kv_heads][block_size][head_size]
+ * so the 16 slots of one (block, kv head) are 16*head_size contiguous
+ * elements.  Token t of a sequence lives in physical block
+ * block_tables[s][t / 16] at slot t % 16.  The pages fix the block size
+ * at 16 tokens ([TEQ] "The OS already solved this in the 1960s") and the
+ * logical-to-physical block table ([AITJ] "How logical blocks, physical
+ * blocks and the block table work"); the element layout inside the pool
+ * is this library's choice.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Work is enqueued asynchronously; nothing synchronizes the host.
+ *
+ * Errors.  Every entry point returns PKV_OK (0) or a negative status, and
+ * validates its scalar arguments before touching the device: on a nonzero
+ * status nothing has been enqueued unless the status is PKV_ERR_HIP (the
+ * launch itself failed).  Device-side contents are not validated on the
+ * hot path; the kernels clamp what could address memory outside the
+ * arguments (block ids, slots, pair entries) and skip those entries, so a
+ * bad index gives wrong numbers for that sequence, never an out-of-bounds
+ * access.  pkv_status_string() names a status.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,  /* null pointer, size <= 0, Hq % Hkv != 0 ... */
+  PKV_ERR_UNSUPPORTED = -2,  /* block_size != 16, head_size not 64/128, dtype */
+  PKV_ERR_WORKSPACE = -3,    /* split-context workspace missing or too small */
+  PKV_ERR_HIP = -4           /* the HIP runtime reported a launch error */
+};
+
+/* ABI version of this header (bumped on any signature change). */
+int pkv_abi_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pkv_status_string(int status);
+
+/*
+ * paged_attention_decode
+ *
+ * For every sequence s and query head h, with L = context_lens[s] and
+ * kv head g = h / (num_heads / num_kv_heads):
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . k_t) v_t,  t = 0..L-1,
+ * where k_t, v_t are token t's key and value in kv head g, read from the
+ * pools through block_tables[s] ([VAS] eq. (1); the kernel "follows the
+ * block table while reading keys and values", [IV] "Architecture, step by
+ * step", step 3).  L counts every cached token, including the one written
+ * this step.  L = 0 gives out[s][h] = 0.  Slots at or past L and blocks
+ * past ceil(L/16) are never used, whatever they hold (NaN included).
+ *
+ *   out           [num_seqs][num_heads][head_size]     written
+ *   query         [num_seqs][num_heads][head_size]
+ *   key_cache     [num_blocks][num_kv_heads][16][head_size]
+ *   value_cache   same layout as key_cache
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries at
+ *                 n >= ceil(L/16) are ignored (any value)
+ *   context_lens  int32 [num_seqs]; values are clamped to
+ *                 [0, 16*max_blocks_per_seq]
+ *   scale         the softmax scale (typically 1/sqrt(head_size))
+ *   num_kv_heads  kv heads; num_heads must be a multiple of it
+ *   num_blocks    pool size in blocks; block ids outside [0, num_blocks)
+ *                 are clamped into it (wrong output, no fault)
+ *   partition_size  tokens per split-context partition: a multiple of 16
+ *                 in [16, 4096], or 0 for the default (512).  Sequences
+ *                 longer than one partition are computed per partition in
+ *                 float32 (max, sum, unnormalized output) and merged by a
+ *                 second kernel.
+ *   workspace     device scratch of at least
+ *                 paged_attention_workspace_bytes(...) bytes; may be NULL
+ *                 when that size is 0 (every sequence fits in one
+ *                 partition, i.e. 16*max_blocks_per_seq <= partition).
+ *
+ * Accumulation is float32 for every dtype; the output is rounded to
+ * nearest-even into `dtype`.
+ */
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, float scale,
+                           int num_kv_heads, int num_seqs, int num_heads,
+                           int head_size, int block_size, int max_blocks_per_seq,
+                           int64_t num_blocks, int partition_size,
+                           void* workspace, size_t workspace_bytes, int dtype,
+                           void* stream);
+
+/*
+ * Bytes of workspace paged_attention_decode needs for these sizes (0 when
+ * no sequence can span more than one partition).  Returns 0 as well for
+ * invalid sizes, which paged_attention_decode then rejects.
+ */
+size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
+                                       int head_size, int max_blocks_per_seq,
+                                       int block_size, int partition_size);
+
+/*
+ * reshape_and_cache
+ *
+ * Writes new tokens' keys and values into their slots of the pools: for
+ * each i with slot = slot_mapping[i] >= 0,
+ *     key_cache[slot / 16][g][slot % 16][:] = key[i][g][:]   for every g,
+ * and the same for value.  This is the write that prefill performs for the
+ * prompt and every decode step performs for its new token ([AITJ] "A
+ * request lifecycle: allocation, growth, sharing and release"); choosing
+ * the slot (and allocating a fresh block when the current one is full) is
+ * the caller's.  The copy is bit-exact.  A negative slot skips the token;
+ * a slot >= 16*num_blocks is skipped as well.  Two tokens with the same
+ * slot race (undefined which one lands).
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_size]
+ *   slot_mapping  int64 [num_tokens]
+ *   key_cache, value_cache  pools as above (modified in place)
+ *
+ * num_tokens = 0 is a valid no-op (key, value and slot_mapping may then be
+ * NULL).
+ */
+int reshape_and_cache(const void* key, const void* value,
+                      const int64_t* slot_mapping, void* key_cache,
+                      void* value_cache, int num_tokens, int num_kv_heads,
+                      int head_size, int block_size, int64_t num_blocks,
+                      int dtype, void* stream);
+
+/*
+ * copy_blocks
+ *
+ * Block-level copy-on-write ([TEQ] "Paging's second gift: copy-on-write"):
+ * for each pair (src, dst) = (src_dst_pairs[2i], src_dst_pairs[2i+1]) the
+ * whole block -- all kv heads, all 16 slots -- is copied, bit-exact, in both
+ * pools:  key_cache[dst] = key_cache[src], value_cache[dst] = value_cache[src].
+ * Pairs are applied as if at once: destinations must be distinct and no
+ * destination may also be a source (else the result is undefined).  A pair
+ * with an entry outside [0, num_blocks) is skipped.  Deciding which block
+ * to copy (the reference count) is the caller's.
+ *
+ *   src_dst_pairs  int64 [num_pairs][2], device memory
+ *
+ * num_pairs = 0 is a valid no-op (src_dst_pairs may then be NULL).
+ */
+int copy_blocks(void* key_cache, void* value_cache, const int64_t* src_dst_pairs,
+                int num_pairs, int num_kv_heads, int head_size, int block_size,
+                int64_t num_blocks, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

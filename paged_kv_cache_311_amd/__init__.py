@@ -1,1 +1,221 @@
-"""Paged KV-cache decode path for MI355X (gfx950): HIP kernels behind a C ABI."""
+"""Paged KV-cache decode path for MI355X (gfx950): HIP kernels behind a C ABI.
+
+The three operations -- paged_attention_decode, reshape_and_cache and
+copy_blocks -- run entirely in the HIP kernels of libpagedkv.so (declared
+in include/pagedkv.h).  This module only marshals torch tensors (device
+memory and the current stream) into the C calls and raises on a nonzero
+status.  There is no fallback: if the library is missing or was not built,
+every call raises.
+
+`validate=True` on any call copies the index arguments to the host and
+checks them first (block ids inside the pool, lengths inside the table,
+distinct slots, copy-on-write pairs that do not overlap); the kernels
+themselves only clamp such values to stay inside the buffers.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import workloads  # noqa: F401  (seeded input generators)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+BLOCK_SIZE = 16
+DEFAULT_PARTITION = 512
+
+_lib = None
+
+
+class PagedKVError(RuntimeError):
+    """A nonzero status returned by the C library."""
+
+
+def _declare(lib):
+    c_int, c_i64, c_sz, c_f, vp = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                   ctypes.c_float, ctypes.c_void_p)
+    lib.pkv_abi_version.restype = c_int
+    lib.pkv_abi_version.argtypes = []
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [c_int]
+    lib.paged_attention_decode.restype = c_int
+    lib.paged_attention_decode.argtypes = [
+        vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
+        c_i64, c_int, vp, c_sz, c_int, vp]
+    lib.paged_attention_workspace_bytes.restype = c_sz
+    lib.paged_attention_workspace_bytes.argtypes = [c_int] * 6
+    lib.reshape_and_cache.restype = c_int
+    lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
+                                      c_i64, c_int, vp]
+    lib.copy_blocks.restype = c_int
+    lib.copy_blocks.argtypes = [vp, vp, vp, c_int, c_int, c_int, c_int, c_i64, c_int, vp]
+    return lib
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load_library(path=LIB_PATH):
+    """Load libpagedkv.so once (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- torch's HIP runtime must be the one bound
+    if not os.path.exists(path):
+        raise PagedKVError(
+            f"{path} is missing: build it with `python -m "
+            "paged_kv_cache_311_amd.build_lib` (or __graft_entry__.build())")
+    lib = _declare(ctypes.CDLL(path))
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise PagedKVError(f"two HIP runtimes are loaded: {sorted(runtimes)}")
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream_of(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check(rc):
+    if rc != 0:
+        raise PagedKVError(f"{_lib.pkv_status_string(rc).decode()} (status {rc})")
+
+
+def _all_cuda_contiguous(*ts):
+    for t in ts:
+        _need(t.is_cuda, "every tensor must be on the GPU")
+        _need(t.is_contiguous(), "every tensor must be contiguous")
+
+
+def workspace_bytes(num_seqs, num_heads, head_size, max_blocks_per_seq,
+                    partition_size=0):
+    """Workspace bytes paged_attention_decode needs (0: none)."""
+    return int(load_library().paged_attention_workspace_bytes(
+        num_seqs, num_heads, head_size, max_blocks_per_seq, BLOCK_SIZE,
+        partition_size))
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
+                           context_lens, scale, num_kv_heads, partition_size=0,
+                           workspace=None, validate=False):
+    """One decode step of paged attention, written into `out` [S, Hq, D].
+
+    key_cache / value_cache: [num_blocks, num_kv_heads, 16, head_size];
+    block_tables int32 [S, W]; context_lens int32 [S]; query/out [S, Hq, D].
+    `workspace` (uint8 device tensor) is allocated here if needed and None.
+    """
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens)
+    code = _dtype_code(query)
+    for t in (out, key_cache, value_cache):
+        _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, Hq, D = query.shape
+    NB, Hkv, bs, D2 = key_cache.shape
+    _need(tuple(out.shape) == (S, Hq, D), "out must match query")
+    _need(tuple(value_cache.shape) == tuple(key_cache.shape), "pools must match")
+    _need(D2 == D and Hkv == num_kv_heads, "pool shape does not match query")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables [S, W]")
+    _need(tuple(context_lens.shape) == (S,), "context_lens [S]")
+    W = block_tables.shape[1]
+    if validate:
+        _validate_tables(block_tables, context_lens, NB)
+    need = int(lib.paged_attention_workspace_bytes(S, Hq, D, W, bs, partition_size))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.paged_attention_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), int(num_kv_heads), S, Hq, D, bs, W, NB,
+        int(partition_size), ws_ptr, ws_len, code, _stream_of(query)))
+    return out
+
+
+def reshape_and_cache(key, value, slot_mapping, key_cache, value_cache, validate=False):
+    """Scatter key/value [T, Hkv, D] into the pools at slot_mapping (int64 [T])."""
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(key, value, slot_mapping, key_cache, value_cache)
+    code = _dtype_code(key)
+    for t in (value, key_cache, value_cache):
+        _need(t.dtype == key.dtype, "keys, values and pools must share a dtype")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    T, Hkv, D = key.shape
+    NB, Hkv2, bs, D2 = key_cache.shape
+    _need(tuple(value.shape) == (T, Hkv, D) and tuple(slot_mapping.shape) == (T,),
+          "key/value [T, Hkv, D], slot_mapping [T]")
+    _need(Hkv2 == Hkv and D2 == D and tuple(value_cache.shape) == tuple(key_cache.shape),
+          "pool shape does not match the new tokens")
+    if validate:
+        s = slot_mapping.cpu().numpy()
+        live = s[s >= 0]
+        _need(len(np.unique(live)) == len(live), "duplicate slot")
+        _need(not len(live) or live.max() < NB * bs, "slot outside the pool")
+    _check(lib.reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache),
+        T, Hkv, D, bs, NB, code, _stream_of(key)))
+
+
+def copy_blocks(key_cache, value_cache, src_dst_pairs, validate=False):
+    """Copy whole blocks src -> dst in both pools (src_dst_pairs int64 [N, 2])."""
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(key_cache, value_cache, src_dst_pairs)
+    code = _dtype_code(key_cache)
+    _need(value_cache.dtype == key_cache.dtype and
+          tuple(value_cache.shape) == tuple(key_cache.shape), "pools must match")
+    _need(src_dst_pairs.dtype == torch.int64 and src_dst_pairs.dim() == 2 and
+          src_dst_pairs.shape[1] == 2, "src_dst_pairs must be int64 [N, 2]")
+    NB, Hkv, bs, D = key_cache.shape
+    if validate:
+        pr = src_dst_pairs.cpu().numpy()
+        _need(len(np.unique(pr[:, 1])) == len(pr), "a destination repeats")
+        _need(not np.intersect1d(pr[:, 0], pr[:, 1]).size, "a destination is a source")
+        _need(not len(pr) or (pr.min() >= 0 and pr.max() < NB), "block id outside pool")
+    _check(lib.copy_blocks(
+        _ptr(key_cache), _ptr(value_cache), _ptr(src_dst_pairs), src_dst_pairs.shape[0],
+        Hkv, D, bs, NB, code, _stream_of(key_cache)))
+
+
+def _validate_tables(block_tables, context_lens, num_blocks):
+    bt = block_tables.cpu().numpy()
+    lens = context_lens.cpu().numpy()
+    _need((lens >= 0).all(), "negative context length")
+    _need((lens <= bt.shape[1] * BLOCK_SIZE).all(), "context length exceeds the table")
+    for s, L in enumerate(lens):
+        ids = bt[s, :-(-int(L) // BLOCK_SIZE)] if L else bt[s, :0]
+        _need(not len(ids) or (ids.min() >= 0 and ids.max() < num_blocks),
+              f"sequence {s}: block id outside the pool")

@@ -1,0 +1,140 @@
+// Device-side helpers shared by the gfx950 kernels: element traits,
+// 16-byte vector access, DPP row reductions and MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlockSize = 16;   // tokens per physical block
+constexpr int kWave = 64;        // CDNA wavefront width
+
+// ---------------------------------------------------------------- traits --
+template <int DT> struct Elt;
+template <> struct Elt<PKV_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPer16B = 4;
+};
+template <> struct Elt<PKV_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPer16B = 8;
+};
+template <> struct Elt<PKV_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPer16B = 8;
+};
+
+// Widen the e-th element of a 16-byte chunk to float.
+template <int DT>
+__device__ __forceinline__ float elem_to_float(const u32x4& v, int e);
+
+template <>
+__device__ __forceinline__ float elem_to_float<PKV_F32>(const u32x4& v, int e) {
+  // copy the element to a scalar first: a bit_cast applied directly to a
+  // vector-element lvalue reads the vector's first element instead
+  const uint32_t x = v[e];
+  return __builtin_bit_cast(float, x);
+}
+template <>
+__device__ __forceinline__ float elem_to_float<PKV_F16>(const u32x4& v, int e) {
+  uint32_t w = v[e >> 1];
+  uint16_t h = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+template <>
+__device__ __forceinline__ float elem_to_float<PKV_BF16>(const u32x4& v, int e) {
+  uint32_t w = v[e >> 1];
+  // a bfloat16 is the upper half of a binary32: placing it there is exact
+  uint32_t f = (e & 1) ? (w & 0xffff0000u) : (w << 16);
+  return __builtin_bit_cast(float, f);
+}
+
+// Round float to the storage type (nearest-even) and return its bits.
+template <int DT> __device__ __forceinline__ uint32_t float_to_bits(float x);
+template <> __device__ __forceinline__ uint32_t float_to_bits<PKV_F32>(float x) {
+  return __builtin_bit_cast(uint32_t, x);
+}
+template <> __device__ __forceinline__ uint32_t float_to_bits<PKV_F16>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <> __device__ __forceinline__ uint32_t float_to_bits<PKV_BF16>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
+  if constexpr (Elt<DT>::kBytes == 4) {
+    reinterpret_cast<float*>(base)[idx] = x;
+  } else {
+    reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)float_to_bits<DT>(x);
+  }
+}
+
+// ------------------------------------------------------------ 16-B access --
+__device__ __forceinline__ float lane_float(const u32x4& v, int e) {
+  const uint32_t x = v[e];
+  return __builtin_bit_cast(float, x);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ------------------------------------------------------------------ DPP --
+// Row = 16 consecutive lanes.  Control codes of the gfx9 DPP encoding.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i in each 8-lane half
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i in each row
+constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                         0xf, 0xf, false));
+}
+
+// Max / sum over the 16 lanes of each row; every lane gets the row result.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f<kDppQuadXor1>(x);
+  x += dpp_f<kDppQuadXor2>(x);
+  x += dpp_f<kDppRowHalfMirror>(x);
+  x += dpp_f<kDppRowMirror>(x);
+  return x;
+}
+
+// Sum of x over the lanes whose index differs from this lane's only in
+// bits >= log2(STRIDE) (STRIDE in {8,16,32}): lanes that share lane % STRIDE.
+template <int STRIDE>
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+  if constexpr (STRIDE <= 8) x += dpp_f<kDppRowRor8>(x);
+  if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16, kWave);
+  x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float uniform(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+}  // namespace pkv

@@ -105,6 +105,8 @@ def draw_context_lens(w, rng, n=None):
         return np.clip(np.rint(x), 1, cap).astype(np.int64)
     if kind == "fixed":
         return np.full(n, w.lengths[1], dtype=np.int64)
+    if kind == "list":  # explicit lengths, for edge-case tests
+        return np.asarray(w.lengths[1], dtype=np.int64)
     raise ValueError(f"no plain length draw for {kind!r}")
 
 
@@ -173,7 +175,7 @@ def _pool_blocks(w, need):
         if w.pool[1] < need:
             raise ValueError("fixed pool too small for the drawn lengths")
         return int(w.pool[1])
-    return int(np.ceil(w.pool[1] * need))
+    return max(1, int(np.ceil(w.pool[1] * need)))
 
 
 def _table_array(tables, width):
@@ -218,7 +220,7 @@ def draw_metadata(w, seed):
         tables, filled, slots = [], [], []
         for L in lens:
             L = int(L)
-            cached = L if w.step == "decode" else L - 1
+            cached = L if w.step == "decode" else max(L - 1, 0)
             t = mgr.allocate_for(cached)
             if w.step == "append":
                 slot, pair = mgr.append_slot(t, cached)
@@ -347,3 +349,13 @@ def to_host(t):
 def kv_token_count(md):
     """Tokens attended in one decode step (sum of context lengths)."""
     return int(np.asarray(md["context_lens"], dtype=np.int64).sum())
+
+
+def custom(lens, num_heads, num_kv_heads, head_size, dtype, max_len=None,
+           pool_factor=1.25, partition_size=512):
+    """A decode workload with explicit context lengths (edge-case tests)."""
+    lens = tuple(int(x) for x in lens)
+    max_len = max(max(lens), 1) if max_len is None else max_len
+    return Workload("custom", 0, len(lens), num_heads, num_kv_heads, head_size,
+                    dtype, ("list", lens), ("factor", pool_factor), "decode",
+                    max_len, partition_size)
