@@ -68,7 +68,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);
+int pkv_abi_version(void);  /* 2 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -98,18 +98,23 @@ const char* pkv_status_string(int status);
  *   num_kv_heads  kv heads; num_heads must be a multiple of it
  *   num_blocks    pool size in blocks; block ids outside [0, num_blocks)
  *                 are clamped into it (wrong output, no fault)
- *   partition_size  tokens per split-context partition: a multiple of 16
- *                 in [16, 4096], or 0 for the default (512).  Sequences
- *                 longer than one partition are computed per partition in
- *                 float32 (max, sum, unnormalized output) and merged by a
- *                 second kernel.
+ *   partition_size  0 (default): every sequence's context is split wherever
+ *                 the load balance puts it; otherwise the most tokens one
+ *                 piece of a split context may hold, a multiple of 16 in
+ *                 [16, 4096].  Pieces are computed in float32 (running max,
+ *                 sum, unnormalized output) and merged exactly as one
+ *                 softmax over the whole context.
  *   workspace     device scratch of at least
- *                 paged_attention_workspace_bytes(...) bytes; may be NULL
- *                 when that size is 0 (every sequence fits in one
- *                 partition, i.e. 16*max_blocks_per_seq <= partition).
+ *                 paged_attention_workspace_bytes(...) bytes, 16-byte
+ *                 aligned; caller-owned, contents need no initialization.
+ *
+ * Work is balanced over the GPU: the grid holds as many waves as the chip
+ * keeps resident, each streaming an equal share of all (block, kv head)
+ * tiles of the batch, whatever the mix of context lengths.
  *
  * Accumulation is float32 for every dtype; the output is rounded to
- * nearest-even into `dtype`.
+ * nearest-even into `dtype`.  num_seqs * max_blocks_per_seq * (num_heads /
+ * heads per workgroup) must be below 2^31.
  */
 int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            const void* value_cache, const int32_t* block_tables,
@@ -121,13 +126,17 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            void* stream);
 
 /*
- * Bytes of workspace paged_attention_decode needs for these sizes (0 when
- * no sequence can span more than one partition).  Returns 0 as well for
- * invalid sizes, which paged_attention_decode then rejects.
+ * Bytes of workspace paged_attention_decode needs for these sizes: room
+ * for two float32 partial states (head_size + 2 floats per query head of a
+ * workgroup) for each of the at most max(8192, tiles / partition tiles)
+ * ranges a launch can form.  Depends only on the arguments (no device
+ * query).  Returns 0 for invalid sizes, which paged_attention_decode then
+ * rejects.
  */
 size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
-                                       int head_size, int max_blocks_per_seq,
-                                       int block_size, int partition_size);
+                                       int num_kv_heads, int head_size,
+                                       int max_blocks_per_seq, int block_size,
+                                       int partition_size);
 
 /*
  * reshape_and_cache

@@ -24,7 +24,6 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 BLOCK_SIZE = 16
-DEFAULT_PARTITION = 512
 
 _lib = None
 
@@ -45,7 +44,7 @@ def _declare(lib):
         vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
         c_i64, c_int, vp, c_sz, c_int, vp]
     lib.paged_attention_workspace_bytes.restype = c_sz
-    lib.paged_attention_workspace_bytes.argtypes = [c_int] * 6
+    lib.paged_attention_workspace_bytes.argtypes = [c_int] * 7
     lib.reshape_and_cache.restype = c_int
     lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
                                       c_i64, c_int, vp]
@@ -117,11 +116,11 @@ def _all_cuda_contiguous(*ts):
         _need(t.is_contiguous(), "every tensor must be contiguous")
 
 
-def workspace_bytes(num_seqs, num_heads, head_size, max_blocks_per_seq,
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq,
                     partition_size=0):
-    """Workspace bytes paged_attention_decode needs (0: none)."""
+    """Workspace bytes paged_attention_decode needs."""
     return int(load_library().paged_attention_workspace_bytes(
-        num_seqs, num_heads, head_size, max_blocks_per_seq, BLOCK_SIZE,
+        num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq, BLOCK_SIZE,
         partition_size))
 
 
@@ -152,7 +151,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
     W = block_tables.shape[1]
     if validate:
         _validate_tables(block_tables, context_lens, NB)
-    need = int(lib.paged_attention_workspace_bytes(S, Hq, D, W, bs, partition_size))
+    need = int(lib.paged_attention_workspace_bytes(S, Hq, Hkv, D, W, bs, partition_size))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)

@@ -139,7 +139,7 @@ extern "C" int copy_blocks(void* key_cache, void* value_cache, const int64_t* sr
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-extern "C" int pkv_abi_version(void) { return 1; }
+extern "C" int pkv_abi_version(void) { return 2; }
 
 extern "C" const char* pkv_status_string(int status) {
   switch (status) {

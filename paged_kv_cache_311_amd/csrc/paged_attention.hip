@@ -8,26 +8,34 @@
 // dot-product attention (Vaswani et al. 2017, eq. 1); paging only changes
 // where each token's key and value are fetched from.
 //
-// Work decomposition
-//   workgroup  = (sequence, group of GC query heads sharing one kv head,
-//                 partition of `partition_size` logical tokens); 4 waves.
-//   wave       = every 4th block of the partition; per block it loads the
-//                 (block, kv head) key tile and value tile (16 x head_size
-//                 contiguous elements each), prefetching the next block's
-//                 tiles while it computes on the current ones.
-//   QK         = one MFMA chain per tile: the key tile is the B operand as
-//                 loaded (lane l holds token l%16), the query rows are
-//                 replicated so every lane receives the logits of its own
-//                 token for all heads of the group.
-//   softmax    = online, in log2 units, wave-uniform running max per head
-//                 (DPP row reduction), rescaling the accumulator only when
-//                 the max grows.
-//   PV         = VALU FMA in float32 over value tiles loaded as contiguous
-//                 1 KiB rows per instruction; the probabilities reach the
-//                 value layout through a 16 x GC LDS buffer per wave.
-//   merge      = the 4 waves' (max, sum, acc) through LDS; a sequence that
-//                 fits in one partition writes its output directly, longer
-//                 ones write float32 partials merged by a second kernel.
+// Work decomposition (balanced, persistent)
+//   tile      = one (block, kv head) pair of one sequence: 16 tokens x
+//               head_size contiguous elements of K and the same of V.
+//   segment   = all tiles of one (sequence, group of GC query heads that
+//               share a kv head); segments are laid end to end in
+//               sequence-major order, giving T tiles in total.
+//   range     = qt consecutive tiles of that flattened order; the grid is
+//               sized to what the chip holds resident and every wave takes
+//               ranges v, v + NWV, ...  so each wave streams the same number
+//               of bytes whatever the length mix (no empty or straggling
+//               workgroups).
+//   piece     = the part of one segment inside one range.  A wave keeps an
+//               online softmax per piece; a piece that is a whole segment
+//               writes the output directly, a piece of a split segment
+//               writes float32 partials (running max, sum, unnormalized
+//               accumulator) merged by a second kernel.
+//
+// Per tile (one wave):
+//   QK  = MFMA chain: the key tile is the B operand exactly as loaded (lane
+//         l holds token l%16), the query rows are replicated so every lane
+//         receives the logits of its own token for all heads of the group.
+//   softmax = online, in log2 units; the running max per head is wave
+//         uniform (DPP row reduction) and the accumulator is rescaled only
+//         when it grows.
+//   PV  = VALU FMA in float32 over value tiles loaded as contiguous 1 KiB
+//         rows per instruction; probabilities reach the value layout through
+//         a 16 x GC LDS buffer owned by the wave.
+//   The next tile's K and V are loaded while the current one is computed.
 //
 // Masking: tokens at or beyond the context length in the last block are
 // excluded by select (logit -inf, value zeroed), never by multiplying
@@ -37,14 +45,21 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "pkv_device.h"
 
 namespace pkv {
 
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeThreads = kDecodeWaves * kWave;
-constexpr int kDefaultPartition = 512;
-constexpr int kMaxPartition = 4096;   // 256 blocks: 64 per wave, one id per lane
+constexpr int kWavesPerWG = 4;
+constexpr int kThreads = kWavesPerWG * kWave;
+constexpr int kMaxWGs = 2048;                   // at most 8192 resident waves
+constexpr int kMaxWaves = kMaxWGs * kWavesPerWG;
+constexpr int kMinTilesPerRange = 4;
+constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
+constexpr int kMergeThreads = kWave;
+constexpr int kMergeWGs = 2048;
 
 template <int DT, int D, int GC>
 struct DecodeCfg {
@@ -63,12 +78,99 @@ struct DecodeCfg {
   static_assert(GC == 1 || GC == 2 || GC == 4 || GC == 8, "heads per workgroup");
 };
 
+struct DecodeParams {
+  void* out;
+  const char* query;
+  const char* kcache;
+  const char* vcache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float scale_log2;
+  int num_seqs, num_heads, num_kv_heads, max_blocks;
+  int64_t num_blocks;
+  int tile_cap;        // max tiles per range (0: no cap)
+  float* part_ml;      // [r_max][2][GC][2]  running max (log2 units), sum
+  float* part_acc;     // [r_max][2][GC][D]  unnormalized accumulator
+};
+
 struct Tile {
   // K in MFMA-B layout (lane l: token l%16, chunks (l/16) + 4m), V as
   // contiguous 1-KiB slices (lane l: bytes ld*1024 + 16l of the tile).
   u32x4 k[8];
   u32x4 v[8];
 };
+
+// ------------------------------------------------------ wave utilities --
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int sread(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int clamp_len(int L, int max_tokens) {
+  return L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
+}
+
+__device__ __forceinline__ int blocks_of(int L) { return (L + kBlockSize - 1) / kBlockSize; }
+
+// Tiles of every segment, summed over all sequences (wave-uniform).
+__device__ int total_tiles(const DecodeParams& p, int head_groups, int lane) {
+  const int max_tokens = p.max_blocks * kBlockSize;
+  int acc = 0;
+  for (int base = 0; base < p.num_seqs; base += kWave) {
+    const int s = base + lane;
+    if (s < p.num_seqs) acc += blocks_of(clamp_len(p.context_lens[s], max_tokens));
+  }
+  return sread(wave_sum_i(acc)) * head_groups;
+}
+
+// Tiles per range and number of ranges for T tiles over nwaves waves.
+__device__ __forceinline__ void range_shape(int T, int nwaves, int cap, int& qt, int& R) {
+  qt = (T + nwaves - 1) / nwaves;
+  qt = qt < kMinTilesPerRange ? kMinTilesPerRange : qt;
+  if (cap > 0 && qt > cap) qt = cap;
+  R = T == 0 ? 0 : (T + qt - 1) / qt;
+}
+
+// Move (s, excl) forward to the sequence whose tiles contain flattened
+// position x: excl = first flattened tile of sequence s.  Monotone: the
+// search resumes from the caller's (s, excl).
+__device__ void locate(const DecodeParams& p, int head_groups, int lane, int x, int& s_io,
+                       int& excl_io) {
+  const int max_tokens = p.max_blocks * kBlockSize;
+  int base = s_io;
+  int carry = excl_io;
+  while (base < p.num_seqs) {
+    const int s = base + lane;
+    const int v = s < p.num_seqs
+                      ? blocks_of(clamp_len(p.context_lens[s], max_tokens)) * head_groups
+                      : 0;
+    const int incl = wave_incl_scan_i(v, lane) + carry;
+    const int excl = incl - v;
+    const unsigned long long hit = __ballot(s < p.num_seqs && excl <= x && x < incl);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      s_io = base + l;
+      excl_io = __shfl(excl, l, kWave);
+      return;
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+    base += kWave;
+  }
+  s_io = p.num_seqs;
+  excl_io = carry;
+}
 
 template <int DT, int NLD>
 __device__ __forceinline__ floatx4 qk_mfma(const u32x4 (&q)[NLD], const Tile& t) {
@@ -84,281 +186,363 @@ __device__ __forceinline__ floatx4 qk_mfma(const u32x4 (&q)[NLD], const Tile& t)
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_float(q[m], e),
-                                                   lane_float(t.k[m], e), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_float(q[m], e), lane_float(t.k[m], e),
+                                                   acc, 0, 0, 0);
     }
   }
   return acc;
 }
 
+// Store kEpc floats as one 16-byte chunk of the output type.
+template <int DT>
+__device__ __forceinline__ void store_chunk(char* dst, const float* x) {
+  u32x4 v;
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = float_to_bits<DT>(x[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = float_to_bits<DT>(x[2 * i]) | (float_to_bits<DT>(x[2 * i + 1]) << 16);
+  }
+  store16(dst, v);
+}
+
+// ------------------------------------------------------------ main kernel --
 template <int DT, int D, int GC>
-__global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(
-    void* __restrict__ out, const char* __restrict__ query,
-    const char* __restrict__ kcache, const char* __restrict__ vcache,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    float scale_log2, int num_kv_heads, int num_heads, int max_blocks,
-    int64_t num_blocks, int partition_size, int num_parts,
-    float* __restrict__ part_acc, float* __restrict__ part_m, float* __restrict__ part_s) {
+__global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodeParams p) {
   using C = DecodeCfg<DT, D, GC>;
   constexpr int NLD = C::kNld;
+  constexpr int EPC = C::kEpc;
 
-  __shared__ float sm_p[kDecodeWaves][kBlockSize * GC];
-  __shared__ float sm_m[kDecodeWaves][GC];
-  __shared__ float sm_s[kDecodeWaves][GC];
-  __shared__ float sm_acc[kDecodeWaves][GC][D];
+  __shared__ float sm_p[kWavesPerWG][kBlockSize * GC];
 
-  const int head_groups = num_heads / GC;
-  const int wg = blockIdx.x;
-  const int p = wg % num_parts;
-  const int hg = (wg / num_parts) % head_groups;
-  const int s = wg / (num_parts * head_groups);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = tid >> 6;
-  const int h0 = hg * GC;
-  const int kvh = h0 / (num_heads / num_kv_heads);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  // XCD-aware wave numbering: workgroups are dealt round-robin to the 8
+  // XCDs, so give each XCD a contiguous block of wave ids (and therefore of
+  // the flattened tile order) to keep shared table rows in one L2.
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int per_xcd = nwg >> 3;
+  const int wg_l = (nwg & 7) == 0 ? xcd * per_xcd + (blockIdx.x >> 3) : blockIdx.x;
+  const int v = wg_l * kWavesPerWG + w;
+  const int nwaves = nwg * kWavesPerWG;
 
-  int L = context_lens[s];
-  L = L < 0 ? 0 : (L > max_blocks * kBlockSize ? max_blocks * kBlockSize : L);
-  const int tok0 = p * partition_size;
-  if (tok0 >= L) {
-    if (p == 0) {  // empty sequence: the output is zero
-      for (int i = tid; i < GC * D; i += kDecodeThreads)
-        store_elem<DT>(out, ((int64_t)s * num_heads + h0) * D + i, 0.f);
+  const int head_groups = p.num_heads / GC;
+  const int group = p.num_heads / p.num_kv_heads;
+  const int max_tokens = p.max_blocks * kBlockSize;
+  const int T = total_tiles(p, head_groups, lane);
+
+  // sequences with no cached token: their output is zero
+  for (int base = 0; base < p.num_seqs; base += kWave) {
+    const int s = base + lane;
+    unsigned long long z = __ballot(s < p.num_seqs && s % nwaves == v &&
+                                    clamp_len(p.context_lens[s], max_tokens) == 0);
+    while (z) {
+      const int l = __ffsll((long long)z) - 1;
+      z &= z - 1;
+      const int64_t row0 = (int64_t)(base + l) * p.num_heads * D;
+      for (int i = lane; i < p.num_heads * D; i += kWave) store_elem<DT>(p.out, row0 + i, 0.f);
     }
-    return;
-  }
-  const int tok1 = min(L, tok0 + partition_size);
-  const int blk0 = tok0 / kBlockSize;
-  const int nblk = (tok1 - tok0 + kBlockSize - 1) / kBlockSize;
-  const int cnt = nblk > w ? (nblk - w + kDecodeWaves - 1) / kDecodeWaves : 0;
-
-  // physical ids of this wave's blocks: lane i holds block blk0 + w + 4i
-  int my_id = 0;
-  if (lane < cnt) {
-    int64_t b = block_tables[(int64_t)s * max_blocks + blk0 + w + kDecodeWaves * lane];
-    b = b < 0 ? 0 : (b >= num_blocks ? num_blocks - 1 : b);
-    my_id = (int)b;
   }
 
-  // query rows as MFMA A operands: row r of chain c is head c*4 + r % kGcq
+  int qt, R;
+  range_shape(T, nwaves, p.tile_cap, qt, R);
+  if (v >= R) return;
+
+  float* pw = sm_p[w];
   const int row = lane & 15;
   const int jg = lane >> 4;
-  u32x4 qa[C::kNqg][NLD];
-#pragma unroll
-  for (int c = 0; c < C::kNqg; ++c) {
-    const int head = h0 + c * 4 + (row % C::kGcq);
-    const char* qrow = query + ((int64_t)s * num_heads + head) * C::kRowB;
-#pragma unroll
-    for (int m = 0; m < NLD; ++m) qa[c][m] = load16(qrow + (jg + 4 * m) * 16);
-  }
-
-  const int64_t head_stride = (int64_t)C::kTileB;               // bytes per kv head
-  const int64_t block_stride = (int64_t)num_kv_heads * C::kTileB;
   const uint32_t koff_lane = (uint32_t)(row * C::kRowB + jg * 16);
   const uint32_t voff_lane = (uint32_t)(lane * 16);
+  const int64_t block_stride = (int64_t)p.num_kv_heads * C::kTileB;
 
-  auto load_tile = [&](Tile& t, int n) {
-    const int id = __builtin_amdgcn_readlane(my_id, n);
-    const char* kb = kcache + (int64_t)id * block_stride + kvh * head_stride;
-    const char* vb = vcache + (int64_t)id * block_stride + kvh * head_stride;
-#pragma unroll
-    for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
-#pragma unroll
-    for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
-  };
+  int ls = 0, lexcl = 0;  // locate cursor
+  for (int r = v; r < R; r += nwaves) {
+    const int x0 = r * qt;
+    const int x1 = min(x0 + qt, T);
+    locate(p, head_groups, lane, x0, ls, lexcl);
+    int s = ls;
+    int L = clamp_len(p.context_lens[s], max_tokens);
+    int nb = blocks_of(L);
+    int local = x0 - lexcl;
+    int hg = local / nb;
+    int n0 = local - hg * nb;
+    int x = x0;
+    bool first_piece = true;
+    while (x < x1) {
+      const int n1 = min(nb, n0 + (x1 - x));
+      const int cnt = n1 - n0;
+      const bool complete = n0 == 0 && n1 == nb;
+      const int h0 = hg * GC;
+      const int kvh = h0 / group;
 
-  float m_run[GC], l_run[GC], acc[GC][C::kEpc];
+      // query rows as MFMA A operands: row r of chain c is head c*4 + r % kGcq
+      u32x4 qa[C::kNqg][NLD];
 #pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+      for (int c = 0; c < C::kNqg; ++c) {
+        const int head = h0 + c * 4 + (row % C::kGcq);
+        const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowB;
 #pragma unroll
-    for (int e = 0; e < C::kEpc; ++e) acc[g][e] = 0.f;
-  }
-  float* pw = sm_p[w];
-
-  auto compute_tile = [&](const Tile& t, int n) {
-    const int lb = blk0 + w + kDecodeWaves * n;
-    const int valid = L - lb * kBlockSize;  // >= 1; < 16 only in the last block
-    float sc[GC];
-#pragma unroll
-    for (int c = 0; c < C::kNqg; ++c) {
-      floatx4 r = qk_mfma<DT, NLD>(qa[c], t);
-#pragma unroll
-      for (int i = 0; i < C::kGcq; ++i) sc[c * 4 + i] = r[i] * scale_log2;
-    }
-    if (row >= valid) {
-#pragma unroll
-      for (int g = 0; g < GC; ++g) sc[g] = -INFINITY;
-    }
-    float pr[GC];
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      const float tmax = uniform(row_max16(sc[g]));
-      if (tmax > m_run[g]) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - tmax);
-        l_run[g] *= alpha;
-#pragma unroll
-        for (int e = 0; e < C::kEpc; ++e) acc[g][e] *= alpha;
-        m_run[g] = tmax;
+        for (int m = 0; m < NLD; ++m) qa[c][m] = load16(qrow + (jg + 4 * m) * 16);
       }
-      pr[g] = __builtin_amdgcn_exp2f(sc[g] - m_run[g]);
-      l_run[g] += pr[g];
-    }
-    if (lane < kBlockSize) {
+
+      float m_run[GC], l_run[GC], acc[GC][EPC];
 #pragma unroll
-      for (int g = 0; g < GC; ++g) pw[lane * GC + g] = pr[g];
-    }
-    __builtin_amdgcn_wave_barrier();
+      for (int g = 0; g < GC; ++g) {
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.f;
 #pragma unroll
-    for (int ld = 0; ld < NLD; ++ld) {
-      const int tok = ld * C::kTpl + lane / C::kNch;
-      float pv[GC];
-#pragma unroll
-      for (int g = 0; g < GC; ++g) pv[g] = pw[tok * GC + g];
-      u32x4 vv = t.v[ld];
-      if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < C::kEpc; ++e) {
-        const float f = elem_to_float<DT>(vv, e);
-#pragma unroll
-        for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], f, acc[g][e]);
+        for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
       }
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
 
-  // two register tiles, alternating: load n+1 while computing n
-  Tile ta, tb;
-  if (cnt > 0) load_tile(ta, 0);
-  for (int n = 0; n < cnt; n += 2) {
-    if (n + 1 < cnt) load_tile(tb, n + 1);
-    compute_tile(ta, n);
-    if (n + 1 < cnt) {
-      if (n + 2 < cnt) load_tile(ta, n + 2);
-      compute_tile(tb, n + 1);
-    }
-  }
+      const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
+      const char* kbase = p.kcache + (int64_t)kvh * C::kTileB;
+      const char* vbase = p.vcache + (int64_t)kvh * C::kTileB;
 
-  // wave totals: sum over the 16 token lanes; acc over lanes sharing a chunk
+      // the piece's tiles in windows of 64 (one block id per lane)
+      for (int c0 = 0; c0 < cnt; c0 += kWave) {
+        const int wcnt = min(kWave, cnt - c0);
+        int my_id = 0;
+        if (lane < wcnt) {
+          int64_t b = bt_row[n0 + c0 + lane];
+          b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
+          my_id = (int)b;
+        }
+        auto load_tile = [&](Tile& t, int i) {
+          const int64_t off = (int64_t)__builtin_amdgcn_readlane(my_id, i) * block_stride;
+          const char* kb = kbase + off;
+          const char* vb = vbase + off;
 #pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    l_run[g] = row_sum16(l_run[g]);
+          for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
 #pragma unroll
-    for (int e = 0; e < C::kEpc; ++e) acc[g][e] = sum_over_lane_groups<C::kNch>(acc[g][e]);
-  }
-  if (lane == 0) {
+          for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
+        };
+        auto compute_tile = [&](const Tile& t, int i) {
+          const int valid = L - (n0 + c0 + i) * kBlockSize;  // >= 1; < 16 only last block
+          float sc[GC];
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      sm_m[w][g] = m_run[g];
-      sm_s[w][g] = l_run[g];
-    }
-  }
-  if (lane < C::kNch) {
+          for (int c = 0; c < C::kNqg; ++c) {
+            const floatx4 rr = qk_mfma<DT, NLD>(qa[c], t);
 #pragma unroll
-    for (int g = 0; g < GC; ++g)
+            for (int j = 0; j < C::kGcq; ++j) sc[c * 4 + j] = rr[j] * p.scale_log2;
+          }
+          if (row >= valid) {
 #pragma unroll
-      for (int e = 0; e < C::kEpc; ++e) sm_acc[w][g][lane * C::kEpc + e] = acc[g][e];
-  }
-  __syncthreads();
+            for (int g = 0; g < GC; ++g) sc[g] = -INFINITY;
+          }
+          float pr[GC];
+#pragma unroll
+          for (int g = 0; g < GC; ++g) {
+            const float tmax = uniform(row_max16(sc[g]));
+            if (tmax > m_run[g]) {
+              const float alpha = __builtin_amdgcn_exp2f(m_run[g] - tmax);
+              l_run[g] *= alpha;
+#pragma unroll
+              for (int e = 0; e < EPC; ++e) acc[g][e] *= alpha;
+              m_run[g] = tmax;
+            }
+            pr[g] = __builtin_amdgcn_exp2f(sc[g] - m_run[g]);
+            l_run[g] += pr[g];
+          }
+          if (lane < kBlockSize) {
+#pragma unroll
+            for (int g = 0; g < GC; ++g) pw[lane * GC + g] = pr[g];
+          }
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int ld = 0; ld < NLD; ++ld) {
+            const int tok = ld * C::kTpl + lane / C::kNch;
+            float pv[GC];
+#pragma unroll
+            for (int g = 0; g < GC; ++g) pv[g] = pw[tok * GC + g];
+            u32x4 vv = t.v[ld];
+            if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+              const float f = elem_to_float<DT>(vv, e);
+#pragma unroll
+              for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], f, acc[g][e]);
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        };
 
-  const bool single = L <= partition_size;
-  for (int i = tid; i < GC * D; i += kDecodeThreads) {
-    const int g = i / D;
-    const int d = i % D;
-    float M = sm_m[0][g];
+        // two register tiles, alternating: load i+1 while computing i
+        Tile ta, tb;
+        load_tile(ta, 0);
+        for (int i = 0; i < wcnt; i += 2) {
+          if (i + 1 < wcnt) load_tile(tb, i + 1);
+          compute_tile(ta, i);
+          if (i + 1 < wcnt) {
+            if (i + 2 < wcnt) load_tile(ta, i + 2);
+            compute_tile(tb, i + 1);
+          }
+        }
+      }
+
+      // piece totals: l over the 16 token lanes; acc over lanes sharing a chunk
 #pragma unroll
-    for (int v = 1; v < kDecodeWaves; ++v) M = fmaxf(M, sm_m[v][g]);
-    float S = 0.f, O = 0.f;
+      for (int g = 0; g < GC; ++g) {
+        l_run[g] = row_sum16(l_run[g]);
 #pragma unroll
-    for (int v = 0; v < kDecodeWaves; ++v) {
-      const float wt = __builtin_amdgcn_exp2f(sm_m[v][g] - M);  // idle wave: 0
-      S = fmaf(sm_s[v][g], wt, S);
-      O = fmaf(sm_acc[v][g][d], wt, O);
-    }
-    const int h = h0 + g;
-    if (single) {
-      store_elem<DT>(out, ((int64_t)s * num_heads + h) * D + d, O / S);
-    } else {
-      const int64_t slot = ((int64_t)s * num_heads + h) * num_parts + p;
-      part_acc[slot * D + d] = O;
-      if (d == 0) {
-        part_m[slot] = M;
-        part_s[slot] = S;
+        for (int e = 0; e < EPC; ++e) acc[g][e] = sum_over_lane_groups<C::kNch>(acc[g][e]);
+      }
+      if (complete) {
+        if (lane < C::kNch) {
+#pragma unroll
+          for (int g = 0; g < GC; ++g) {
+            const float inv = 1.f / l_run[g];
+            float o[EPC];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o[e] = acc[g][e] * inv;
+            char* dst = (char*)p.out +
+                        (((int64_t)s * p.num_heads + h0 + g) * D + lane * EPC) * C::kEsz;
+            store_chunk<DT>(dst, o);
+          }
+        }
+      } else {
+        const int64_t slot = (int64_t)r * 2 + (first_piece ? 0 : 1);
+        if (lane < C::kNch) {
+#pragma unroll
+          for (int g = 0; g < GC; ++g) {
+            float* dst = p.part_acc + (slot * GC + g) * D + lane * EPC;
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4)
+              store16(dst + e, u32x4{__builtin_bit_cast(uint32_t, acc[g][e]),
+                                     __builtin_bit_cast(uint32_t, acc[g][e + 1]),
+                                     __builtin_bit_cast(uint32_t, acc[g][e + 2]),
+                                     __builtin_bit_cast(uint32_t, acc[g][e + 3])});
+          }
+        }
+        if (lane == 0) {
+#pragma unroll
+          for (int g = 0; g < GC; ++g) {
+            p.part_ml[(slot * GC + g) * 2 + 0] = m_run[g];
+            p.part_ml[(slot * GC + g) * 2 + 1] = l_run[g];
+          }
+        }
+      }
+
+      // next piece: the next segment (next head group, or next sequence
+      // that has a cached token)
+      x += cnt;
+      first_piece = false;
+      n0 = 0;
+      if (x < x1) {
+        if (++hg == head_groups) {
+          hg = 0;
+          do {
+            ++s;
+            L = clamp_len(p.context_lens[s], max_tokens);
+          } while (L == 0);
+          nb = blocks_of(L);
+        }
       }
     }
   }
 }
 
-// Merge of the per-partition float32 states of sequences longer than one
-// partition: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) s_p.
-template <int DT, int D>
-__global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(
-    void* __restrict__ out, const int32_t* __restrict__ context_lens, int num_heads,
-    int max_blocks, int partition_size, int num_parts, const float* __restrict__ part_acc,
-    const float* __restrict__ part_m, const float* __restrict__ part_s) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  int L = context_lens[s];
-  L = L < 0 ? 0 : (L > max_blocks * kBlockSize ? max_blocks * kBlockSize : L);
-  const int np = (L + partition_size - 1) / partition_size;
-  if (np <= 1) return;
-  const int64_t base = ((int64_t)s * num_heads + h) * num_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, part_m[base + p]);
-  constexpr int DPL = D / kWave;
-  float O[DPL];
+// ----------------------------------------------------------- merge kernel --
+// Segments split across ranges: combine their pieces,
+//   out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
+// The segment is merged by the first range boundary that falls strictly
+// inside it; every other boundary skips.
+template <int DT, int D, int GC>
+__global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
+    const DecodeParams p, int nwaves) {
+  const int lane = threadIdx.x;
+  const int head_groups = p.num_heads / GC;
+  const int max_tokens = p.max_blocks * kBlockSize;
+  const int T = total_tiles(p, head_groups, lane);
+  int qt, R;
+  range_shape(T, nwaves, p.tile_cap, qt, R);
+  int ls = 0, lexcl = 0;
+  for (int r = 1 + blockIdx.x; r < R; r += gridDim.x) {
+    const int x = r * qt;
+    locate(p, head_groups, lane, x, ls, lexcl);
+    const int s = ls;
+    const int nb = blocks_of(clamp_len(p.context_lens[s], max_tokens));
+    const int hg = (x - lexcl) / nb;
+    const int P = lexcl + hg * nb;  // first flattened tile of the segment
+    if (P == x || (r - 1) * qt > P) continue;  // not the first inner boundary
+    const int rf = r - 1;
+    const int rl = (P + nb - 1) / qt;
+    constexpr int EPL = GC * D / kMergeThreads > 0 ? GC * D / kMergeThreads : 1;
+    for (int i0 = 0; i0 < GC * D; i0 += kMergeThreads * EPL) {
+      float O[EPL], S[EPL], M[EPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
-  float S = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float wt = __builtin_amdgcn_exp2f(part_m[base + p] - M);
-    S = fmaf(wt, part_s[base + p], S);
-    const float* a = part_acc + (base + p) * D;
+      for (int j = 0; j < EPL; ++j) {
+        O[j] = 0.f;
+        S[j] = 0.f;
+        M[j] = -INFINITY;
+      }
+      for (int k = rf; k <= rl; ++k) {
+        const int64_t slot = (int64_t)k * 2 + ((k == rf && P != rf * qt) ? 1 : 0);
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) O[i] = fmaf(wt, a[threadIdx.x + i * kWave], O[i]);
+        for (int j = 0; j < EPL; ++j) {
+          const int i = i0 + j * kMergeThreads + lane;
+          if (i >= GC * D) continue;
+          const int g = i / D;
+          const float mk = p.part_ml[(slot * GC + g) * 2 + 0];
+          const float lk = p.part_ml[(slot * GC + g) * 2 + 1];
+          const float ak = p.part_acc[(slot * GC + g) * D + (i - g * D)];
+          const float Mn = fmaxf(M[j], mk);
+          const float a = __builtin_amdgcn_exp2f(M[j] - Mn);
+          const float b = __builtin_amdgcn_exp2f(mk - Mn);
+          S[j] = S[j] * a + lk * b;
+          O[j] = O[j] * a + ak * b;
+          M[j] = Mn;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int i = i0 + j * kMergeThreads + lane;
+        if (i >= GC * D) continue;
+        const int g = i / D;
+        store_elem<DT>(p.out, ((int64_t)s * p.num_heads + hg * GC + g) * D + (i - g * D),
+                       O[j] / S[j]);
+      }
+    }
   }
-  const float inv = 1.f / S;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i)
-    store_elem<DT>(out, ((int64_t)s * num_heads + h) * D + threadIdx.x + i * kWave, O[i] * inv);
 }
 
-struct DecodeArgs {
-  void* out;
-  const void* query;
-  const void* kcache;
-  const void* vcache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  float scale_log2;
-  int num_kv_heads, num_seqs, num_heads, max_blocks;
-  int64_t num_blocks;
-  int partition_size, num_parts;
-  float *part_acc, *part_m, *part_s;
-};
+// ------------------------------------------------------------------ host --
+// Resident workgroups of a kernel on the current device (memoized: the
+// answer depends only on the device and the kernel's resources).
+static int resident_workgroups(const void* kernel) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::vector<std::pair<std::pair<int, const void*>, int>> memo;
+  std::lock_guard<std::mutex> lock(mu);
+  for (auto& e : memo)
+    if (e.first.first == dev && e.first.second == kernel) return e.second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+    return 0;
+  int n = cus * (per_cu > 0 ? per_cu : 1);
+  n = n > kMaxWGs ? kMaxWGs : n;
+  memo.push_back({{dev, kernel}, n});
+  return n;
+}
 
 template <int DT, int D, int GC>
-static hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const int64_t nwg = (int64_t)a.num_parts * (a.num_heads / GC) * a.num_seqs;
-  hipLaunchKernelGGL((paged_decode_kernel<DT, D, GC>), dim3((unsigned)nwg),
-                     dim3(kDecodeThreads), 0, st, a.out, (const char*)a.query,
-                     (const char*)a.kcache, (const char*)a.vcache, a.block_tables,
-                     a.context_lens, a.scale_log2, a.num_kv_heads, a.num_heads,
-                     a.max_blocks, a.num_blocks, a.partition_size, a.num_parts,
-                     a.part_acc, a.part_m, a.part_s);
-  if (a.num_parts > 1) {
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<DT, D>),
-                       dim3(a.num_heads, a.num_seqs), dim3(kWave), 0, st, a.out,
-                       a.context_lens, a.num_heads, a.max_blocks, a.partition_size,
-                       a.num_parts, a.part_acc, a.part_m, a.part_s);
-  }
+static hipError_t launch_decode(const DecodeParams& a, hipStream_t st) {
+  const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, D, GC>);
+  const int nwg = resident_workgroups(k);
+  if (nwg <= 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL((paged_decode_kernel<DT, D, GC>), dim3(nwg), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3(kMergeWGs),
+                     dim3(kMergeThreads), 0, st, a, nwg * kWavesPerWG);
   return hipGetLastError();
 }
 
 template <int DT, int D>
-static hipError_t dispatch_gc(const DecodeArgs& a, int gc, hipStream_t st) {
+static hipError_t dispatch_gc(const DecodeParams& a, int gc, hipStream_t st) {
   switch (gc) {
     case 1: return launch_decode<DT, D, 1>(a, st);
     case 2: return launch_decode<DT, D, 2>(a, st);
@@ -368,37 +552,44 @@ static hipError_t dispatch_gc(const DecodeArgs& a, int gc, hipStream_t st) {
 }
 
 template <int DT>
-static hipError_t dispatch_d(const DecodeArgs& a, int d, int gc, hipStream_t st) {
+static hipError_t dispatch_d(const DecodeParams& a, int d, int gc, hipStream_t st) {
   return d == 64 ? dispatch_gc<DT, 64>(a, gc, st) : dispatch_gc<DT, 128>(a, gc, st);
 }
 
-static int resolve_partition(int partition_size) {
-  return partition_size == 0 ? kDefaultPartition : partition_size;
+static int heads_per_wg(int num_heads, int num_kv_heads) {
+  const int group = num_heads / num_kv_heads;
+  return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
 }
 
-static int num_partitions(int max_blocks_per_seq, int partition) {
-  const int64_t max_tokens = (int64_t)max_blocks_per_seq * kBlockSize;
-  return (int)((max_tokens + partition - 1) / partition);
+// Largest number of ranges any launch can form (partials are 2 per range).
+static int64_t max_ranges(int64_t max_tiles, int tile_cap) {
+  int64_t r = kMaxWaves;
+  if (tile_cap > 0) {
+    const int64_t rc = (max_tiles + tile_cap - 1) / tile_cap;
+    r = rc > r ? rc : r;
+  }
+  return r;
 }
 
 static bool partition_ok(int ps) {
-  return ps >= kBlockSize && ps <= kMaxPartition && ps % kBlockSize == 0;
+  return ps == 0 || (ps >= kBlockSize && ps <= kMaxPartition && ps % kBlockSize == 0);
 }
 
 }  // namespace pkv
 
 extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
-                                                  int head_size, int max_blocks_per_seq,
-                                                  int block_size, int partition_size) {
+                                                  int num_kv_heads, int head_size,
+                                                  int max_blocks_per_seq, int block_size,
+                                                  int partition_size) {
   using namespace pkv;
-  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_blocks_per_seq <= 0 ||
-      block_size != kBlockSize)
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+      head_size <= 0 || max_blocks_per_seq <= 0 || block_size != kBlockSize ||
+      !partition_ok(partition_size))
     return 0;
-  const int ps = resolve_partition(partition_size);
-  if (!partition_ok(ps)) return 0;
-  const int np = num_partitions(max_blocks_per_seq, ps);
-  if (np <= 1) return 0;
-  return (size_t)num_seqs * num_heads * np * (head_size + 2) * sizeof(float);
+  const int gc = heads_per_wg(num_heads, num_kv_heads);
+  const int64_t max_tiles = (int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc);
+  const int64_t r = max_ranges(max_tiles, partition_size / kBlockSize);
+  return (size_t)r * 2 * gc * (head_size + 2) * sizeof(float);
 }
 
 extern "C" int paged_attention_decode(void* out, const void* query, const void* key_cache,
@@ -418,46 +609,39 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   if (head_size != 64 && head_size != 128) return PKV_ERR_UNSUPPORTED;
-  const int ps = resolve_partition(partition_size);
-  if (!partition_ok(ps)) return PKV_ERR_INVALID_ARG;
-  if (((uintptr_t)query | (uintptr_t)key_cache | (uintptr_t)value_cache) & 15u)
-    return PKV_ERR_INVALID_ARG;  // tiles and query rows are read 16 bytes at a time
-  if ((int64_t)max_blocks_per_seq * kBlockSize > INT32_MAX) return PKV_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PKV_OK;
-
-  const int np = num_partitions(max_blocks_per_seq, ps);
-  const int group = num_heads / num_kv_heads;
-  const int gc = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-  // grid.x * block must fit in 32 bits
-  if ((int64_t)np * (num_heads / gc) * num_seqs > (int64_t)(UINT32_MAX / kDecodeThreads))
+  if (!partition_ok(partition_size)) return PKV_ERR_INVALID_ARG;
+  if (((uintptr_t)query | (uintptr_t)key_cache | (uintptr_t)value_cache | (uintptr_t)out) &
+      15u)
+    return PKV_ERR_INVALID_ARG;  // rows are read and written 16 bytes at a time
+  const int gc = heads_per_wg(num_heads, num_kv_heads);
+  // flattened tile positions are 32-bit
+  if ((int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc) > INT32_MAX)
     return PKV_ERR_INVALID_ARG;
-  if ((int64_t)num_seqs > 65535 && np > 1) return PKV_ERR_INVALID_ARG;  // merge grid.y
+  if (num_seqs == 0) return PKV_OK;
+  const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                                      head_size, max_blocks_per_seq,
+                                                      block_size, partition_size);
+  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 15u) return PKV_ERR_INVALID_ARG;
 
-  DecodeArgs a{};
+  DecodeParams a{};
   a.out = out;
-  a.query = query;
-  a.kcache = key_cache;
-  a.vcache = value_cache;
+  a.query = (const char*)query;
+  a.kcache = (const char*)key_cache;
+  a.vcache = (const char*)value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.scale_log2 = scale * 1.4426950408889634f;  // exp(x) = 2^(x log2 e)
-  a.num_kv_heads = num_kv_heads;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.partition_size = ps;
-  a.num_parts = np;
-  if (np > 1) {
-    const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, head_size,
-                                                        max_blocks_per_seq, block_size, ps);
-    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-    float* ws = (float*)workspace;
-    const size_t rows = (size_t)num_seqs * num_heads * np;
-    a.part_acc = ws;
-    a.part_m = ws + rows * head_size;
-    a.part_s = a.part_m + rows;
-  }
+  a.tile_cap = partition_size / kBlockSize;
+  const int64_t r = max_ranges((int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc),
+                               a.tile_cap);
+  a.part_ml = (float*)workspace;
+  a.part_acc = a.part_ml + r * 2 * gc * 2;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e;

@@ -22,7 +22,8 @@ sampling over a shared prompt, long contexts):
                  blocks, 1..64 private tokens per sample; a shared, partly
                  filled last block is copied before a sample writes to it.
   long_gqa       32 query heads over 8 kv heads of 128, bf16, 16 seqs of
-                 32,768 tokens, pool 1.25x the need, 512-token partitions.
+                 32,768 tokens, pool 1.25x the need; contexts are split
+                 into pieces merged through float32 (max, sum) states.
 
 Every slot that holds no token -- unused blocks and the tail of each
 sequence's last block -- is filled with NaN, so any stray read shows up in
@@ -52,7 +53,7 @@ class Workload:
     pool: tuple             # ("blocks", n) | ("factor", f)
     step: str               # "decode" | "append" | "cow"
     max_len: int            # longest possible context (sets the table width)
-    partition_size: int = 512
+    partition_size: int = 0   # cap on tokens per piece of a split context (0: none)
     prompts: int = 0
     samples: int = 0
 

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -56,15 +56,20 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     f = lib.paged_attention_workspace_bytes
-    # 64 seqs x 40 heads, 2048-token tables, 512-token partitions -> 4 parts
-    assert f(64, 40, 128, 128, 16, 0) == 64 * 40 * 4 * (128 + 2) * 4
-    assert f(64, 40, 128, 128, 16, 512) == f(64, 40, 128, 128, 16, 0)
-    assert f(16, 32, 128, 2048, 16, 512) == 16 * 32 * 64 * 130 * 4
-    assert f(4, 4, 64, 32, 16, 512) == 0          # one partition: no workspace
-    assert f(4, 4, 64, 33, 16, 512) == 4 * 4 * 2 * 66 * 4
-    assert f(4, 4, 64, 33, 8, 512) == 0           # unsupported block size
-    assert f(4, 4, 64, 33, 16, 24) == 0           # not a multiple of 16
-    assert f(4, 4, 64, 33, 16, 8192) == 0         # beyond the largest partition
+    # two float32 states (head_size + 2 floats per head of a workgroup) for
+    # each of max(8192, tiles / tiles-per-piece-cap) ranges
+    assert f(64, 40, 40, 128, 128, 16, 0) == 8192 * 2 * 1 * 130 * 4
+    # 64 x 2048-token tables, 40 kv heads, 512-token cap: 327680 / 32 ranges
+    assert f(64, 40, 40, 128, 128, 16, 512) == 10240 * 2 * 1 * 130 * 4
+    # grouped heads: 4 query heads per kv head share a workgroup
+    assert f(16, 32, 8, 128, 2048, 16, 0) == 8192 * 2 * 4 * 130 * 4
+    assert f(16, 32, 8, 128, 2048, 16, 512) == 8192 * 2 * 4 * 130 * 4
+    assert f(16, 32, 8, 128, 2048, 16, 16) == 262144 * 2 * 4 * 130 * 4
+    assert f(4, 12, 2, 64, 8, 16, 0) == 8192 * 2 * 2 * 66 * 4      # group 6 -> 2
+    assert f(4, 4, 4, 64, 33, 8, 0) == 0          # unsupported block size
+    assert f(4, 4, 4, 64, 33, 16, 24) == 0        # not a multiple of 16
+    assert f(4, 4, 4, 64, 33, 16, 8192) == 0      # beyond the largest cap
+    assert f(4, 6, 4, 64, 33, 16, 0) == 0         # 6 query heads over 4 kv heads
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
@@ -94,9 +99,13 @@ def test_decode_argument_validation(lib):
     assert decode(lib, dtype=3) == UNSUPPORTED
     assert decode(lib, ps=24) == INVALID
     assert decode(lib, ps=8192) == INVALID
+    assert decode(lib, ps=-16) == INVALID
     assert decode(lib, query=FAKE + 8) == INVALID         # not 16-byte aligned
-    assert decode(lib, W=64) == WORKSPACE                 # 1024 tokens > 512
-    assert decode(lib, W=64, ws=FAKE, wsb=16) == WORKSPACE
+    assert decode(lib, out=FAKE + 2) == INVALID           # rows stored 16 B at a time
+    assert decode(lib, S=1 << 20, W=1 << 12) == INVALID   # tile positions beyond 2^31
+    assert decode(lib) == WORKSPACE                       # workspace is required
+    assert decode(lib, ws=FAKE, wsb=16) == WORKSPACE      # ... and must be large enough
+    assert decode(lib, ws=FAKE + 8, wsb=1 << 40) == INVALID   # ... and 16-B aligned
     assert decode(lib, S=0) == OK                         # empty batch: no launch
 
 

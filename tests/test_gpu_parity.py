@@ -96,7 +96,7 @@ def test_full_size_sampled(gpu_lib, key):
     full_step_and_check(b, seqs=seqs)
 
 
-@pytest.mark.parametrize("ps", [16, 48, 128, 256, 512, 1024, 4096])
+@pytest.mark.parametrize("ps", [0, 16, 48, 128, 256, 512, 1024, 4096])
 def test_partition_sizes(gpu_lib, ps):
     w = dataclasses.replace(W["opt13b"], num_seqs=6)
     b = wl.make_batch(w, 4242, DEV)
@@ -164,7 +164,30 @@ def test_split_matches_single_pass_closely(gpu_lib):
     b = wl.make_batch(w, 31337, DEV)
     a = run_decode(b, partition_size=512).float()
     c = run_decode(b, partition_size=4096).float()
+    d = run_decode(b, partition_size=0).float()
     assert (a - c).abs().max().item() <= TOL["bf16"]
+    assert (a - d).abs().max().item() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("ps", [0, 512])
+def test_long_gqa_reduced_with_cap(gpu_lib, ps):
+    """The 32K-token grouped-query workload at both piece policies."""
+    w = dataclasses.replace(W["long_gqa"], num_seqs=2, partition_size=ps)
+    b = wl.make_batch(w, 555, DEV)
+    full_step_and_check(b)
+
+
+def test_many_short_sequences_and_empties(gpu_lib):
+    """More sequences than one scan window (64), with empty ones mixed in."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(0, 40, size=300)
+    lens[::7] = 0
+    w = wl.custom(lens, 8, 8, 128, "f16", max_len=48, partition_size=0)
+    b = wl.make_batch(w, 4, DEV)
+    kc0, vc0 = clone_pools(b)
+    out = run_decode(b)
+    ref = oracle_decode_subset(b, kc0, vc0, list(range(len(lens))))
+    assert_close(out, ref, "f16", "300 short sequences")
 
 
 def test_workspace_too_small_raises(gpu_lib):
