@@ -126,12 +126,14 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            void* stream);
 
 /*
- * Bytes of workspace paged_attention_decode needs for these sizes: room
- * for two float32 partial states (head_size + 2 floats per query head of a
- * workgroup) for each of the at most max(8192, tiles / partition tiles)
- * ranges a launch can form.  Depends only on the arguments (no device
- * query).  Returns 0 for invalid sizes, which paged_attention_decode then
- * rejects.
+ * Bytes of workspace paged_attention_decode needs for these sizes.  A call
+ * splits the batch's (block, kv head) tiles into at most
+ * ranges = max(8192, tiles / (partition_size / 16)) equal ranges; the
+ * workspace holds a 256-byte header, a 16-byte descriptor per range and two
+ * float32 partial states per range (head_size + 2 floats for each query head
+ * of a group), each part rounded up to 256 bytes.  Depends only on the
+ * arguments (no device query).  Returns 0 for invalid sizes, which
+ * paged_attention_decode then rejects.
  */
 size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
                                        int num_kv_heads, int head_size,

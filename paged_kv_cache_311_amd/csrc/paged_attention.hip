@@ -23,7 +23,10 @@
 //               online softmax per piece; a piece that is a whole segment
 //               writes the output directly, a piece of a split segment
 //               writes float32 partials (running max, sum, unnormalized
-//               accumulator) merged by a second kernel.
+//               accumulator).  The range holding a split segment's last
+//               tile names that segment in a per-range descriptor, and a
+//               second, light kernel merges the pieces of every segment a
+//               descriptor names (one wave each).
 //
 // Per tile (one wave):
 //   QK  = MFMA chain: the key tile is the B operand exactly as loaded (lane
@@ -58,8 +61,7 @@ constexpr int kMaxWGs = 2048;                   // at most 8192 resident waves
 constexpr int kMaxWaves = kMaxWGs * kWavesPerWG;
 constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
-constexpr int kMergeThreads = kWave;
-constexpr int kMergeWGs = 2048;
+constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
 
 template <int DT, int D, int GC>
 struct DecodeCfg {
@@ -76,6 +78,10 @@ struct DecodeCfg {
   static_assert(kNld * 4 == kNch, "key tile: 4 lane groups x kNld chunks per row");
   static_assert(kNch >= 8 && kNch <= 32, "lane-group reduction assumes 8..32 chunks");
   static_assert(GC == 1 || GC == 2 || GC == 4 || GC == 8, "heads per workgroup");
+  // Waves per SIMD the register allocator must leave room for: 3 where the
+  // kernel fits in 168 VGPRs without spilling (16-bit K/V up to 4 heads per
+  // group, and 64-wide float32), otherwise whatever it needs.
+  static constexpr int kMinWaves = (GC <= 4 && (kEsz == 2 || D == 64)) ? 3 : 1;
 };
 
 struct DecodeParams {
@@ -89,6 +95,8 @@ struct DecodeParams {
   int num_seqs, num_heads, num_kv_heads, max_blocks;
   int64_t num_blocks;
   int tile_cap;        // max tiles per range (0: no cap)
+  int* header;         // [2]  ranges R, tiles per range qt (this call)
+  int4* desc;          // [r_max]  split segment ending in range r: s, hg, P, nb
   float* part_ml;      // [r_max][2][GC][2]  running max (log2 units), sum
   float* part_acc;     // [r_max][2][GC][D]  unnormalized accumulator
 };
@@ -160,12 +168,14 @@ __device__ void locate(const DecodeParams& p, int head_groups, int lane, int x, 
     const int excl = incl - v;
     const unsigned long long hit = __ballot(s < p.num_seqs && excl <= x && x < incl);
     if (hit) {
+      // readlane keeps the results in scalar registers, so everything
+      // derived from them (addresses included) stays wave-uniform
       const int l = __ffsll((long long)hit) - 1;
       s_io = base + l;
-      excl_io = __shfl(excl, l, kWave);
+      excl_io = __builtin_amdgcn_readlane(excl, l);
       return;
     }
-    carry = __shfl(incl, kWave - 1, kWave);
+    carry = __builtin_amdgcn_readlane(incl, kWave - 1);
     base += kWave;
   }
   s_io = p.num_seqs;
@@ -208,9 +218,169 @@ __device__ __forceinline__ void store_chunk(char* dst, const float* x) {
   store16(dst, v);
 }
 
+// ------------------------------------------------------- split merging --
+template <int DT>
+__device__ __forceinline__ void store4(char* dst, const floatx4& v) {
+  if constexpr (DT == PKV_F32) {
+    store16(dst, u32x4{bits_of(v[0]), bits_of(v[1]), bits_of(v[2]), bits_of(v[3])});
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{float_to_bits<DT>(v[0]) | (float_to_bits<DT>(v[1]) << 16),
+              float_to_bits<DT>(v[2]) | (float_to_bits<DT>(v[3]) << 16)};
+  }
+}
+
+// Merging the pieces k = 0..np-1 of a split segment (ranges rf..rf+np-1):
+//   out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
+// A wave folds a subset of the pieces into a running (max, sum, acc)
+// state; every lane owns 16-byte chunks of the [GC][D] accumulator.
+template <int D, int GC>
+struct FoldState {
+  static constexpr int kChunks = GC * D / 4;
+  static constexpr int kCpl = (kChunks + kWave - 1) / kWave;
+  float M[GC], S[GC];
+  floatx4 O[kCpl];
+};
+
+struct Split {
+  int s, hg, P, nb, rf, np;
+  bool rf_tail;  // range rf's piece of this segment sits in its second slot
+};
+
+__device__ __forceinline__ Split split_of(const int4& d, int qt) {
+  Split x;
+  x.s = d.x;
+  x.hg = d.y;
+  x.P = d.z;
+  x.nb = d.w;
+  x.rf = x.P / qt;
+  x.np = (x.P + x.nb - 1) / qt - x.rf + 1;
+  x.rf_tail = x.P != x.rf * qt;
+  return x;
+}
+
+template <int D, int GC>
+__device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int kstep,
+                            int lane, FoldState<D, GC>& st) {
+  using F = FoldState<D, GC>;
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    st.M[g] = -INFINITY;
+    st.S[g] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < F::kCpl; ++j) st.O[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = k0; k < sp.np; k += kstep) {
+    const int64_t sl = (int64_t)(sp.rf + k) * 2 + ((k == 0 && sp.rf_tail) ? 1 : 0);
+    float a[GC], b[GC];
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      const float mk = p.part_ml[(sl * GC + g) * 2 + 0];
+      const float lk = p.part_ml[(sl * GC + g) * 2 + 1];
+      const float Mn = fmaxf(st.M[g], mk);
+      a[g] = __builtin_amdgcn_exp2f(st.M[g] - Mn);
+      b[g] = __builtin_amdgcn_exp2f(mk - Mn);
+      st.S[g] = st.S[g] * a[g] + lk * b[g];
+      st.M[g] = Mn;
+    }
+#pragma unroll
+    for (int j = 0; j < F::kCpl; ++j) {
+      const int c = lane + j * kWave;
+      if (c < F::kChunks) {
+        const int g = c * 4 / D;
+        float ag = a[0], bg = b[0];
+#pragma unroll
+        for (int gg = 1; gg < GC; ++gg) {
+          ag = g == gg ? a[gg] : ag;
+          bg = g == gg ? b[gg] : bg;
+        }
+        const u32x4 x = load16(p.part_acc + sl * GC * D + c * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.O[j][e] = fmaf(st.O[j][e], ag, bg * float_of(x[e]));
+      }
+    }
+  }
+}
+
+template <int DT, int D, int GC>
+__device__ __forceinline__ void store_merged(const DecodeParams& p, const Split& sp, int c,
+                                             const floatx4& o, float inv) {
+  char* dst = (char*)p.out +
+              (((int64_t)sp.s * p.num_heads + sp.hg * GC) * D + c * 4) * Elt<DT>::kBytes;
+  store4<DT>(dst, o * inv);
+}
+
+// A segment of few pieces: one wave folds them all and writes the output.
+template <int DT, int D, int GC>
+__device__ void merge_by_wave(const DecodeParams& p, const Split& sp, int lane) {
+  using F = FoldState<D, GC>;
+  F st;
+  fold_pieces<D, GC>(p, sp, 0, 1, lane, st);
+#pragma unroll
+  for (int j = 0; j < F::kCpl; ++j) {
+    const int c = lane + j * kWave;
+    if (c < F::kChunks) {
+      const int g = c * 4 / D;
+      float sg = st.S[0];
+#pragma unroll
+      for (int gg = 1; gg < GC; ++gg) sg = g == gg ? st.S[gg] : sg;
+      store_merged<DT, D, GC>(p, sp, c, st.O[j], 1.f / sg);
+    }
+  }
+}
+
+// A segment of many pieces: wave w folds pieces w, w+4, ...; the four wave
+// states are then combined through LDS.
+template <int D, int GC>
+struct MergeSmem {
+  float m[kWavesPerWG][GC];
+  float l[kWavesPerWG][GC];
+  floatx4 o[kWavesPerWG][GC * D / 4];
+};
+
+template <int DT, int D, int GC>
+__device__ void merge_by_workgroup(const DecodeParams& p, const Split& sp, int lane, int w,
+                                   MergeSmem<D, GC>& sm) {
+  using F = FoldState<D, GC>;
+  F st;
+  fold_pieces<D, GC>(p, sp, w, kWavesPerWG, lane, st);
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      sm.m[w][g] = st.M[g];
+      sm.l[w][g] = st.S[g];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < F::kCpl; ++j) {
+    const int c = lane + j * kWave;
+    if (c < F::kChunks) sm.o[w][c] = st.O[j];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < F::kChunks; c += kThreads) {
+    const int g = c * 4 / D;
+    float Mx = sm.m[0][g];
+#pragma unroll
+    for (int v = 1; v < kWavesPerWG; ++v) Mx = fmaxf(Mx, sm.m[v][g]);
+    float Sx = 0.f;
+    floatx4 Ox = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWavesPerWG; ++v) {
+      const float wt = __builtin_amdgcn_exp2f(sm.m[v][g] - Mx);  // idle wave: 0
+      Sx = fmaf(sm.l[v][g], wt, Sx);
+      Ox += sm.o[v][c] * wt;
+    }
+    store_merged<DT, D, GC>(p, sp, c, Ox, 1.f / Sx);
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------ main kernel --
 template <int DT, int D, int GC>
-__global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads, (DecodeCfg<DT, D, GC>::kMinWaves)) void
+paged_decode_kernel(const DecodeParams p) {
   using C = DecodeCfg<DT, D, GC>;
   constexpr int NLD = C::kNld;
   constexpr int EPC = C::kEpc;
@@ -218,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodePara
   __shared__ float sm_p[kWavesPerWG][kBlockSize * GC];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x >> 6;
+  const int w = sread(threadIdx.x >> 6);  // wave index, known uniform to the compiler
   // XCD-aware wave numbering: workgroups are dealt round-robin to the 8
   // XCDs, so give each XCD a contiguous block of wave ids (and therefore of
   // the flattened tile order) to keep shared table rows in one L2.
@@ -249,6 +419,10 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodePara
 
   int qt, R;
   range_shape(T, nwaves, p.tile_cap, qt, R);
+  if (v == 0 && lane == 0) {
+    p.header[0] = R;
+    p.header[1] = qt;
+  }
   if (v >= R) return;
 
   float* pw = sm_p[w];
@@ -277,6 +451,11 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodePara
       const bool complete = n0 == 0 && n1 == nb;
       const int h0 = hg * GC;
       const int kvh = h0 / group;
+      if (first_piece && lane == 0) {
+        // a range's first piece is the last piece of a split segment exactly
+        // when the segment began in an earlier range and ends in this one
+        p.desc[r] = (n0 > 0 && n1 == nb) ? int4{s, hg, x - n0, nb} : int4{-1, 0, 0, 0};
+      }
 
       // query rows as MFMA A operands: row r of chain c is head c*4 + r % kGcq
       u32x4 qa[C::kNqg][NLD];
@@ -410,10 +589,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodePara
             float* dst = p.part_acc + (slot * GC + g) * D + lane * EPC;
 #pragma unroll
             for (int e = 0; e < EPC; e += 4)
-              store16(dst + e, u32x4{__builtin_bit_cast(uint32_t, acc[g][e]),
-                                     __builtin_bit_cast(uint32_t, acc[g][e + 1]),
-                                     __builtin_bit_cast(uint32_t, acc[g][e + 2]),
-                                     __builtin_bit_cast(uint32_t, acc[g][e + 3])});
+              store16(dst + e, u32x4{bits_of(acc[g][e]), bits_of(acc[g][e + 1]),
+                                     bits_of(acc[g][e + 2]), bits_of(acc[g][e + 3])});
           }
         }
         if (lane == 0) {
@@ -445,65 +622,31 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(const DecodePara
 }
 
 // ----------------------------------------------------------- merge kernel --
-// Segments split across ranges: combine their pieces,
-//   out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
-// The segment is merged by the first range boundary that falls strictly
-// inside it; every other boundary skips.
+// Workgroups take four ranges at a time; a range whose descriptor names a
+// split segment gets that segment's pieces merged into its output.
 template <int DT, int D, int GC>
-__global__ __launch_bounds__(kMergeThreads) void paged_decode_merge_kernel(
-    const DecodeParams p, int nwaves) {
-  const int lane = threadIdx.x;
-  const int head_groups = p.num_heads / GC;
-  const int max_tokens = p.max_blocks * kBlockSize;
-  const int T = total_tiles(p, head_groups, lane);
-  int qt, R;
-  range_shape(T, nwaves, p.tile_cap, qt, R);
-  int ls = 0, lexcl = 0;
-  for (int r = 1 + blockIdx.x; r < R; r += gridDim.x) {
-    const int x = r * qt;
-    locate(p, head_groups, lane, x, ls, lexcl);
-    const int s = ls;
-    const int nb = blocks_of(clamp_len(p.context_lens[s], max_tokens));
-    const int hg = (x - lexcl) / nb;
-    const int P = lexcl + hg * nb;  // first flattened tile of the segment
-    if (P == x || (r - 1) * qt > P) continue;  // not the first inner boundary
-    const int rf = r - 1;
-    const int rl = (P + nb - 1) / qt;
-    constexpr int EPL = GC * D / kMergeThreads > 0 ? GC * D / kMergeThreads : 1;
-    for (int i0 = 0; i0 < GC * D; i0 += kMergeThreads * EPL) {
-      float O[EPL], S[EPL], M[EPL];
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        O[j] = 0.f;
-        S[j] = 0.f;
-        M[j] = -INFINITY;
+__global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const DecodeParams p) {
+  __shared__ MergeSmem<D, GC> sm;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = sread(threadIdx.x >> 6);
+  const int R = p.header[0];
+  const int qt = p.header[1];
+  for (int base = blockIdx.x * kWavesPerWG; base < R; base += gridDim.x * kWavesPerWG) {
+    // each wave merges its own range's segment if it has few pieces ...
+    const int r = base + w;
+    if (r < R) {
+      const int4 d = p.desc[r];
+      if (d.x >= 0) {
+        const Split sp = split_of(d, qt);
+        if (sp.np <= kSoloPieces) merge_by_wave<DT, D, GC>(p, sp, lane);
       }
-      for (int k = rf; k <= rl; ++k) {
-        const int64_t slot = (int64_t)k * 2 + ((k == rf && P != rf * qt) ? 1 : 0);
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-          const int i = i0 + j * kMergeThreads + lane;
-          if (i >= GC * D) continue;
-          const int g = i / D;
-          const float mk = p.part_ml[(slot * GC + g) * 2 + 0];
-          const float lk = p.part_ml[(slot * GC + g) * 2 + 1];
-          const float ak = p.part_acc[(slot * GC + g) * D + (i - g * D)];
-          const float Mn = fmaxf(M[j], mk);
-          const float a = __builtin_amdgcn_exp2f(M[j] - Mn);
-          const float b = __builtin_amdgcn_exp2f(mk - Mn);
-          S[j] = S[j] * a + lk * b;
-          O[j] = O[j] * a + ak * b;
-          M[j] = Mn;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int i = i0 + j * kMergeThreads + lane;
-        if (i >= GC * D) continue;
-        const int g = i / D;
-        store_elem<DT>(p.out, ((int64_t)s * p.num_heads + hg * GC + g) * D + (i - g * D),
-                       O[j] / S[j]);
-      }
+    }
+    // ... and the four waves together take those with many
+    for (int v = 0; v < kWavesPerWG && base + v < R; ++v) {
+      const int4 d = p.desc[base + v];
+      if (d.x < 0) continue;
+      const Split sp = split_of(d, qt);
+      if (sp.np > kSoloPieces) merge_by_workgroup<DT, D, GC>(p, sp, lane, w, sm);
     }
   }
 }
@@ -536,8 +679,8 @@ static hipError_t launch_decode(const DecodeParams& a, hipStream_t st) {
   const int nwg = resident_workgroups(k);
   if (nwg <= 0) return hipErrorInvalidDevice;
   hipLaunchKernelGGL((paged_decode_kernel<DT, D, GC>), dim3(nwg), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3(kMergeWGs),
-                     dim3(kMergeThreads), 0, st, a, nwg * kWavesPerWG);
+  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -571,6 +714,23 @@ static int64_t max_ranges(int64_t max_tiles, int tile_cap) {
   return r;
 }
 
+// Workspace: header [2 ints], range descriptors [r][4 ints], then (max,
+// sum) [r][2][gc][2] and accumulators [r][2][gc][head_size] in float32;
+// each part 256-B aligned.  Every call writes what it reads.
+struct WorkspaceLayout {
+  size_t header, desc, part_ml, part_acc, total;
+};
+static WorkspaceLayout workspace_layout(int64_t r, int gc, int head_size) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WorkspaceLayout l;
+  l.header = 0;
+  l.desc = 256;
+  l.part_ml = up(l.desc + (size_t)r * 16);
+  l.part_acc = up(l.part_ml + (size_t)r * 2 * gc * 2 * sizeof(float));
+  l.total = up(l.part_acc + (size_t)r * 2 * gc * head_size * sizeof(float));
+  return l;
+}
+
 static bool partition_ok(int ps) {
   return ps == 0 || (ps >= kBlockSize && ps <= kMaxPartition && ps % kBlockSize == 0);
 }
@@ -589,7 +749,7 @@ extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
   const int gc = heads_per_wg(num_heads, num_kv_heads);
   const int64_t max_tiles = (int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc);
   const int64_t r = max_ranges(max_tiles, partition_size / kBlockSize);
-  return (size_t)r * 2 * gc * (head_size + 2) * sizeof(float);
+  return workspace_layout(r, gc, head_size).total;
 }
 
 extern "C" int paged_attention_decode(void* out, const void* query, const void* key_cache,
@@ -640,8 +800,11 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   a.tile_cap = partition_size / kBlockSize;
   const int64_t r = max_ranges((int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc),
                                a.tile_cap);
-  a.part_ml = (float*)workspace;
-  a.part_acc = a.part_ml + r * 2 * gc * 2;
+  const WorkspaceLayout wl = workspace_layout(r, gc, head_size);
+  a.header = (int*)((char*)workspace + wl.header);
+  a.desc = (int4*)((char*)workspace + wl.desc);
+  a.part_ml = (float*)((char*)workspace + wl.part_ml);
+  a.part_acc = (float*)((char*)workspace + wl.part_acc);
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e;

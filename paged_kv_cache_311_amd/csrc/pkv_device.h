@@ -32,16 +32,20 @@ template <> struct Elt<PKV_BF16> {
   static constexpr int kPer16B = 8;
 };
 
+// Bit casts through by-value scalars.  clang's __builtin_bit_cast applied
+// directly to an element of an ext_vector_type lvalue (v[i]) reads the
+// vector's first element whatever i is, so vector elements are always
+// passed through these by value.
+__device__ __forceinline__ uint32_t bits_of(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float float_of(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // Widen the e-th element of a 16-byte chunk to float.
 template <int DT>
 __device__ __forceinline__ float elem_to_float(const u32x4& v, int e);
 
 template <>
 __device__ __forceinline__ float elem_to_float<PKV_F32>(const u32x4& v, int e) {
-  // copy the element to a scalar first: a bit_cast applied directly to a
-  // vector-element lvalue reads the vector's first element instead
-  const uint32_t x = v[e];
-  return __builtin_bit_cast(float, x);
+  return float_of(v[e]);
 }
 template <>
 __device__ __forceinline__ float elem_to_float<PKV_F16>(const u32x4& v, int e) {
@@ -79,10 +83,7 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
 }
 
 // ------------------------------------------------------------ 16-B access --
-__device__ __forceinline__ float lane_float(const u32x4& v, int e) {
-  const uint32_t x = v[e];
-  return __builtin_bit_cast(float, x);
-}
+__device__ __forceinline__ float lane_float(const u32x4& v, int e) { return float_of(v[e]); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

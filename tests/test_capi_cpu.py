@@ -54,18 +54,26 @@ def test_status_strings(lib):
     assert lib.pkv_status_string(123) == b"unknown status"
 
 
+def expected_workspace(ranges, gc, head_size):
+    """The documented layout: a 256-B header, 16-B range descriptors, then
+    (max, sum) and accumulator partials for 2 pieces per range, each part
+    rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    return (256 + up(ranges * 16) + up(ranges * 2 * gc * 2 * 4)
+            + up(ranges * 2 * gc * head_size * 4))
+
+
 def test_workspace_bytes(lib):
     f = lib.paged_attention_workspace_bytes
-    # two float32 states (head_size + 2 floats per head of a workgroup) for
-    # each of max(8192, tiles / tiles-per-piece-cap) ranges
-    assert f(64, 40, 40, 128, 128, 16, 0) == 8192 * 2 * 1 * 130 * 4
+    # ranges = max(8192, tiles / tiles-per-piece cap)
+    assert f(64, 40, 40, 128, 128, 16, 0) == expected_workspace(8192, 1, 128)
     # 64 x 2048-token tables, 40 kv heads, 512-token cap: 327680 / 32 ranges
-    assert f(64, 40, 40, 128, 128, 16, 512) == 10240 * 2 * 1 * 130 * 4
+    assert f(64, 40, 40, 128, 128, 16, 512) == expected_workspace(10240, 1, 128)
     # grouped heads: 4 query heads per kv head share a workgroup
-    assert f(16, 32, 8, 128, 2048, 16, 0) == 8192 * 2 * 4 * 130 * 4
-    assert f(16, 32, 8, 128, 2048, 16, 512) == 8192 * 2 * 4 * 130 * 4
-    assert f(16, 32, 8, 128, 2048, 16, 16) == 262144 * 2 * 4 * 130 * 4
-    assert f(4, 12, 2, 64, 8, 16, 0) == 8192 * 2 * 2 * 66 * 4      # group 6 -> 2
+    assert f(16, 32, 8, 128, 2048, 16, 0) == expected_workspace(8192, 4, 128)
+    assert f(16, 32, 8, 128, 2048, 16, 512) == expected_workspace(8192, 4, 128)
+    assert f(16, 32, 8, 128, 2048, 16, 16) == expected_workspace(262144, 4, 128)
+    assert f(4, 12, 2, 64, 8, 16, 0) == expected_workspace(8192, 2, 64)   # group 6 -> 2
     assert f(4, 4, 4, 64, 33, 8, 0) == 0          # unsupported block size
     assert f(4, 4, 4, 64, 33, 16, 24) == 0        # not a multiple of 16
     assert f(4, 4, 4, 64, 33, 16, 8192) == 0      # beyond the largest cap
