@@ -108,7 +108,7 @@ class Step:
         self.ps = w.partition_size if ps is None else ps
         need = pkv.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
                                    b["block_tables"].shape[1], self.ps)
-        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
         if "slot_mapping" in b:
             slots = b["slot_mapping"]
             self.key, self.value = b["key"], b["value"]

@@ -73,6 +73,11 @@ int pkv_abi_version(void);  /* 2 */
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
 
+/* Identifier of the sources this library was built from (a sha256 in hex,
+ * static storage).  A binding compares it with its own sources to refuse a
+ * library left over from older ones. */
+const char* pkv_build_id(void);
+
 /*
  * paged_attention_decode
  *

@@ -39,6 +39,8 @@ def _declare(lib):
     lib.pkv_abi_version.argtypes = []
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [c_int]
+    lib.pkv_build_id.restype = ctypes.c_char_p
+    lib.pkv_build_id.argtypes = []
     lib.paged_attention_decode.restype = c_int
     lib.paged_attention_decode.argtypes = [
         vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -65,8 +67,12 @@ def _hip_runtimes_mapped():
     return paths
 
 
-def load_library(path=LIB_PATH):
-    """Load libpagedkv.so once (after torch, so both share one HIP runtime)."""
+def load_library(path=LIB_PATH, check_build=True):
+    """Load libpagedkv.so once (after torch, so both share one HIP runtime).
+
+    Refuses a library whose build id differs from the digest of the sources
+    beside it: a stale build never runs.
+    """
     global _lib
     if _lib is not None:
         return _lib
@@ -76,6 +82,13 @@ def load_library(path=LIB_PATH):
             f"{path} is missing: build it with `python -m "
             "paged_kv_cache_311_amd.build_lib` (or __graft_entry__.build())")
     lib = _declare(ctypes.CDLL(path))
+    if check_build:
+        from .build_lib import source_digest
+        built, now = lib.pkv_build_id().decode(), source_digest()
+        if built != now:
+            raise PagedKVError(
+                f"{path} was built from other sources (build id {built[:12]}, sources "
+                f"{now[:12]}): rebuild it with `python -m paged_kv_cache_311_amd.build_lib`")
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:
         raise PagedKVError(f"two HIP runtimes are loaded: {sorted(runtimes)}")
@@ -153,7 +166,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
         _validate_tables(block_tables, context_lens, NB)
     need = int(lib.paged_attention_workspace_bytes(S, Hq, Hkv, D, W, bs, partition_size))
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.paged_attention_decode(

@@ -6,6 +6,8 @@ instructions are disabled for device code.  Usable as a script:
     python -m paged_kv_cache_311_amd.build_lib
 """
 
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -25,6 +27,23 @@ FLAGS = [
 ]
 
 
+def source_digest():
+    """sha256 of every source and header the library is built from, and of
+    the compile flags.  Built into the library (pkv_build_id) and checked by
+    the binding at load time, so a library older than its sources never
+    runs."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) +
+                   glob.glob(os.path.join(CSRC, "*.h")) +
+                   [os.path.join(HERE, "..", "include", "pagedkv.h")])
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(FLAGS[:-1]).encode())  # flags other than the include path
+    return h.hexdigest()
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only target feature: harmless
@@ -40,9 +59,11 @@ def build(verbose=False):
     """Compile every HIP source and link the shared library (always rebuilds)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
 
+    stamp = f'-DPKV_BUILD_ID="{source_digest()}"'
+
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
-        warn = _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        warn = _run([HIPCC, *FLAGS, stamp, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and warn.strip():
             print(warn, file=sys.stderr)
         return obj

@@ -139,7 +139,13 @@ extern "C" int copy_blocks(void* key_cache, void* value_cache, const int64_t* sr
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+#ifndef PKV_BUILD_ID
+#define PKV_BUILD_ID "unstamped"
+#endif
+
 extern "C" int pkv_abi_version(void) { return 2; }
+
+extern "C" const char* pkv_build_id(void) { return PKV_BUILD_ID; }
 
 extern "C" const char* pkv_status_string(int status) {
   switch (status) {

@@ -137,6 +137,24 @@ def test_cache_ops_argument_validation(lib):
     assert c(FAKE, FAKE, FAKE, 0, 2, 128, 16, 8, 2, 0) == OK
 
 
+def test_library_build_id_matches_sources(lib):
+    from paged_kv_cache_311_amd.build_lib import source_digest
+    assert lib.pkv_build_id().decode() == source_digest()
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    """A library built from other sources than those beside it never loads."""
+    import shutil
+    import paged_kv_cache_311_amd as pkv
+    from paged_kv_cache_311_amd import build_lib
+    copy = tmp_path / "libpagedkv_copy.so"
+    shutil.copy(pkv.LIB_PATH, copy)
+    monkeypatch.setattr(pkv, "_lib", None)
+    monkeypatch.setattr(build_lib, "source_digest", lambda: "0" * 64)
+    with pytest.raises(pkv.PagedKVError, match="built from other sources"):
+        pkv.load_library(str(copy))
+
+
 def test_binding_raises_without_library(tmp_path, monkeypatch):
     import paged_kv_cache_311_amd as pkv
     monkeypatch.setattr(pkv, "_lib", None)

@@ -229,3 +229,23 @@ def test_padding_slots_are_skipped(gpu_lib):
     ek, ev, _ = oracle_pool(b, kc0, vc0, ids)
     assert gather_blocks(b["key_cache"], ids).tobytes() == ek.tobytes()
     assert gather_blocks(b["value_cache"], ids).tobytes() == ev.tobytes()
+
+
+def test_workspace_reused_across_calls(gpu_lib):
+    """One zero-filled workspace serves consecutive calls of different shapes:
+    each call leaves the range counter at zero for the next."""
+    w1 = dataclasses.replace(W["opt13b"], num_seqs=8)
+    w2 = wl.custom([5, 700, 33, 1200], 32, 8, 128, "bf16", max_len=2048)
+    ws = torch.zeros(max(pkv.workspace_bytes(8, 40, 40, 128, 128),
+                         pkv.workspace_bytes(4, 32, 8, 128, 128)),
+                     dtype=torch.uint8, device=DEV)
+    for w, seed in ((w1, 1), (w2, 2), (w1, 3), (w2, 4)):
+        b = wl.make_batch(w, seed, DEV)
+        kc0, vc0 = clone_pools(b)
+        out = torch.empty_like(b["query"])
+        pkv.paged_attention_decode(out, b["query"], b["key_cache"], b["value_cache"],
+                                   dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
+                                   float(w.scale), w.num_kv_heads, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle_decode_subset(b, kc0, vc0, list(range(w.num_seqs)))
+        assert_close(out, ref, w.dtype, f"reuse {w.key} seed {seed}")
