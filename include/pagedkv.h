@@ -112,10 +112,13 @@ const char* pkv_build_id(void);
  *   workspace     device scratch of at least
  *                 paged_attention_workspace_bytes(...) bytes, 16-byte
  *                 aligned; caller-owned, contents need no initialization.
+ *                 Calls that use one workspace must not overlap (one
+ *                 stream, or ordered).
  *
- * Work is balanced over the GPU: the grid holds as many waves as the chip
- * keeps resident, each streaming an equal share of all (block, kv head)
- * tiles of the batch, whatever the mix of context lengths.
+ * Work is balanced over the GPU: the grid holds two waves per SIMD, each
+ * streaming an equal share of all (block, kv head) tiles of the batch,
+ * whatever the mix of context lengths.  Batches of more than 2048
+ * sequences run as consecutive launches of 2048.
  *
  * Accumulation is float32 for every dtype; the output is rounded to
  * nearest-even into `dtype`.  num_seqs * max_blocks_per_seq * (num_heads /
@@ -131,9 +134,9 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            void* stream);
 
 /*
- * Bytes of workspace paged_attention_decode needs for these sizes.  A call
- * splits the batch's (block, kv head) tiles into at most
- * ranges = max(8192, tiles / (partition_size / 16)) equal ranges; the
+ * Bytes of workspace paged_attention_decode needs for these sizes.  One
+ * launch (at most 2048 sequences) splits its (block, kv head) tiles into at
+ * most ranges = max(4096, tiles / (partition_size / 16)) equal ranges; the
  * workspace holds a 256-byte header, a 16-byte descriptor per range and two
  * float32 partial states per range (head_size + 2 floats for each query head
  * of a group), each part rounded up to 256 bytes.  Depends only on the

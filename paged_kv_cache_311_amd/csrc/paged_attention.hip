@@ -14,11 +14,13 @@
 //   segment   = all tiles of one (sequence, group of GC query heads that
 //               share a kv head); segments are laid end to end in
 //               sequence-major order, giving T tiles in total.
-//   range     = qt consecutive tiles of that flattened order; the grid is
-//               sized to what the chip holds resident and every wave takes
-//               ranges v, v + NWV, ...  so each wave streams the same number
-//               of bytes whatever the length mix (no empty or straggling
-//               workgroups).
+//   range     = an equal share of consecutive tiles of that flattened
+//               order.  The grid holds two resident waves per SIMD and
+//               every wave takes ranges v, v + NWV, ...  so each wave
+//               streams the same number of bytes whatever the length mix
+//               (no empty or straggling workgroups).  With two waves per
+//               SIMD rather than more, the hardware's preference for the
+//               oldest wave leaves less of a spread in finishing times.
 //   piece     = the part of one segment inside one range.  A wave keeps an
 //               online softmax per piece; a piece that is a whole segment
 //               writes the output directly, a piece of a split segment
@@ -57,8 +59,9 @@ namespace pkv {
 
 constexpr int kWavesPerWG = 4;
 constexpr int kThreads = kWavesPerWG * kWave;
-constexpr int kMaxWGs = 2048;                   // at most 8192 resident waves
+constexpr int kMaxWGs = 1024;                   // at most 4 waves per SIMD
 constexpr int kMaxWaves = kMaxWGs * kWavesPerWG;
+constexpr int kWavesPerSimd = 2;                // resident waves the grid is sized for
 constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
 constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
@@ -78,10 +81,13 @@ struct DecodeCfg {
   static_assert(kNld * 4 == kNch, "key tile: 4 lane groups x kNld chunks per row");
   static_assert(kNch >= 8 && kNch <= 32, "lane-group reduction assumes 8..32 chunks");
   static_assert(GC == 1 || GC == 2 || GC == 4 || GC == 8, "heads per workgroup");
-  // Waves per SIMD the register allocator must leave room for: 3 where the
-  // kernel fits in 168 VGPRs without spilling (16-bit K/V up to 4 heads per
-  // group, and 64-wide float32), otherwise whatever it needs.
-  static constexpr int kMinWaves = (GC <= 4 && (kEsz == 2 || D == 64)) ? 3 : 1;
+  // Waves per SIMD the register allocator must leave room for: 3 (168
+  // VGPRs) where the kernel fits without spilling (one head per group with
+  // 16-bit K/V or 64-wide rows, two heads with 64-wide rows), 2 (256 VGPRs)
+  // for up to four heads per group, otherwise whatever it needs.
+  static constexpr bool kNarrow = kEsz == 2 || D == 64;
+  static constexpr int kMinWaves =
+      kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1);
 };
 
 struct DecodeParams {
@@ -95,10 +101,10 @@ struct DecodeParams {
   int num_seqs, num_heads, num_kv_heads, max_blocks;
   int64_t num_blocks;
   int tile_cap;        // max tiles per range (0: no cap)
-  int* header;         // [2]  ranges R, tiles per range qt (this call)
-  int4* desc;          // [r_max]  split segment ending in range r: s, hg, P, nb
-  float* part_ml;      // [r_max][2][GC][2]  running max (log2 units), sum
-  float* part_acc;     // [r_max][2][GC][D]  unnormalized accumulator
+  int* header;         // [2]  ranges R and tiles per range q of this call
+  int4* desc;          // [R]  split segment ending in range r: s, hg, P, nb
+  float* part_ml;      // [R][2][GC][2]  running max (log2 units), sum
+  float* part_acc;     // [R][2][GC][D]  unnormalized accumulator
 };
 
 struct Tile {
@@ -132,54 +138,83 @@ __device__ __forceinline__ int clamp_len(int L, int max_tokens) {
 
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlockSize - 1) / kBlockSize; }
 
-// Tiles of every segment, summed over all sequences (wave-uniform).
-__device__ int total_tiles(const DecodeParams& p, int head_groups, int lane) {
-  const int max_tokens = p.max_blocks * kBlockSize;
-  int acc = 0;
-  for (int base = 0; base < p.num_seqs; base += kWave) {
-    const int s = base + lane;
-    if (s < p.num_seqs) acc += blocks_of(clamp_len(p.context_lens[s], max_tokens));
-  }
-  return sread(wave_sum_i(acc)) * head_groups;
-}
+// Sequences one launch covers: their segment table lives in LDS.  The
+// host splits larger batches into consecutive launches.
+constexpr int kLdsSeqs = 2048;
 
-// Tiles per range and number of ranges for T tiles over nwaves waves.
-__device__ __forceinline__ void range_shape(int T, int nwaves, int cap, int& qt, int& R) {
-  qt = (T + nwaves - 1) / nwaves;
-  qt = qt < kMinTilesPerRange ? kMinTilesPerRange : qt;
-  if (cap > 0 && qt > cap) qt = cap;
-  R = T == 0 ? 0 : (T + qt - 1) / qt;
-}
-
-// Move (s, excl) forward to the sequence whose tiles contain flattened
-// position x: excl = first flattened tile of sequence s.  Monotone: the
-// search resumes from the caller's (s, excl).
-__device__ void locate(const DecodeParams& p, int head_groups, int lane, int x, int& s_io,
-                       int& excl_io) {
+// Segment table of this launch's sequences, built in LDS by every thread of
+// the workgroup: len[s] = clamped context length, incl[s] = tiles of
+// sequences 0..s (blocks x head groups), summed.  Returns T = incl[S-1].
+__device__ int build_segment_table(const DecodeParams& p, int head_groups, int* incl, int* len,
+                                   int* wsum, int lane, int w) {
+  const int S = p.num_seqs;
   const int max_tokens = p.max_blocks * kBlockSize;
-  int base = s_io;
-  int carry = excl_io;
-  while (base < p.num_seqs) {
-    const int s = base + lane;
-    const int v = s < p.num_seqs
-                      ? blocks_of(clamp_len(p.context_lens[s], max_tokens)) * head_groups
-                      : 0;
-    const int incl = wave_incl_scan_i(v, lane) + carry;
-    const int excl = incl - v;
-    const unsigned long long hit = __ballot(s < p.num_seqs && excl <= x && x < incl);
-    if (hit) {
-      // readlane keeps the results in scalar registers, so everything
-      // derived from them (addresses included) stays wave-uniform
-      const int l = __ffsll((long long)hit) - 1;
-      s_io = base + l;
-      excl_io = __builtin_amdgcn_readlane(excl, l);
-      return;
+  const int per = (S + kThreads - 1) / kThreads;  // sequences per thread, contiguous
+  const int s0 = threadIdx.x * per;
+  int sum = 0;
+  for (int k = 0; k < per; ++k) {
+    const int s = s0 + k;
+    if (s < S) {
+      const int L = clamp_len(p.context_lens[s], max_tokens);
+      len[s] = L;
+      sum += blocks_of(L) * head_groups;
     }
-    carry = __builtin_amdgcn_readlane(incl, kWave - 1);
-    base += kWave;
   }
-  s_io = p.num_seqs;
-  excl_io = carry;
+  const int inc = wave_incl_scan_i(sum, lane);
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  int run = inc - sum;
+  int total = 0;
+#pragma unroll
+  for (int j = 0; j < kWavesPerWG; ++j) {
+    const int t = wsum[j];
+    run += j < w ? t : 0;
+    total += t;
+  }
+  for (int k = 0; k < per; ++k) {
+    const int s = s0 + k;
+    if (s < S) {
+      run += blocks_of(len[s]) * head_groups;
+      incl[s] = run;
+    }
+  }
+  __syncthreads();
+  return sread(total);
+}
+
+// Sequence whose tiles hold flattened position x < T: the first s with
+// incl[s] > x.
+__device__ __forceinline__ int seq_of(const int* incl, int S, int x) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (incl[mid] > x) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// How the T flattened tiles are cut into ranges: R ranges of q tiles (the
+// last one shorter), range r covering tiles [r q, min((r + 1) q, T)).  Wave
+// v takes ranges v, v + NWV, ...  Both kernels derive the same map.
+struct RangeMap {
+  int q, R, T;
+  __device__ __forceinline__ int start(int r) const { return r * q; }
+  __device__ __forceinline__ int end(int r) const { return min((r + 1) * q, T); }
+  __device__ __forceinline__ int of(int x) const { return x / q; }
+};
+
+// An equal share of the tiles per wave (at least kMinTilesPerRange, at
+// most the tiles-per-piece cap when there is one).
+__device__ RangeMap plan_ranges(int T, int nwaves, int cap) {
+  RangeMap m;
+  m.T = T;
+  int q = T / nwaves + (T % nwaves != 0);
+  q = q < kMinTilesPerRange ? kMinTilesPerRange : q;
+  if (cap > 0 && q > cap) q = cap;
+  m.q = q;
+  m.R = T / q + (T % q != 0);
+  return m;
 }
 
 template <int DT, int NLD>
@@ -248,15 +283,15 @@ struct Split {
   bool rf_tail;  // range rf's piece of this segment sits in its second slot
 };
 
-__device__ __forceinline__ Split split_of(const int4& d, int qt) {
+__device__ __forceinline__ Split split_of(const int4& d, const RangeMap& m) {
   Split x;
   x.s = d.x;
   x.hg = d.y;
   x.P = d.z;
   x.nb = d.w;
-  x.rf = x.P / qt;
-  x.np = (x.P + x.nb - 1) / qt - x.rf + 1;
-  x.rf_tail = x.P != x.rf * qt;
+  x.rf = m.of(x.P);
+  x.np = m.of(x.P + x.nb - 1) - x.rf + 1;
+  x.rf_tail = x.P != m.start(x.rf);
   return x;
 }
 
@@ -378,6 +413,69 @@ __device__ void merge_by_workgroup(const DecodeParams& p, const Split& sp, int l
 }
 
 // ------------------------------------------------------------ main kernel --
+constexpr int kPrepAhead = 3;   // tiles left in a window when the next one is prepared
+
+// Window::info, per tile: head group (bits 0-15), valid tokens (16-20), flags.
+constexpr int kPieceFirst = 1 << 21;
+constexpr int kPieceLast = 1 << 22;
+constexpr int kSegStart = 1 << 23;
+constexpr int kSegEnd = 1 << 24;
+constexpr int kRangeFirst = 1 << 25;
+
+__device__ __forceinline__ int pick(bool c, int a, int b) { return c ? a : b; }
+
+// Up to 64 consecutive tiles of one range, lane j describing tile x + j.
+struct Window {
+  int r, x, cnt;    // range, first flattened tile, tiles (wave-uniform)
+  int ends_range;   // the range's last tile lies in this window
+  int id;           // lane j: physical block (clamped into the pool)
+  int s;            // lane j: sequence
+  int info;         // lane j: head group, valid tokens, flags
+};
+
+// Where the tiles x .. x + 63 of range r are: sequence, head group and
+// block of each (segment table in LDS) and the block id (one gather from
+// the block table).  The lane of the range's first tile also writes the
+// range's descriptor.
+__device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const int* incl,
+                                 const int* len, int head_groups, int r, int xw, int lane) {
+  Window wd;
+  const int x0 = m.start(r);
+  const int x1 = m.end(r);
+  wd.r = r;
+  wd.x = xw;
+  wd.cnt = min(kWave, x1 - xw);
+  wd.ends_range = xw + wd.cnt == x1;
+  wd.id = 0;
+  wd.s = 0;
+  wd.info = 0;
+  const int x = xw + lane;
+  if (lane < wd.cnt) {
+    const int s = seq_of(incl, p.num_seqs, x);
+    const int excl = s > 0 ? incl[s - 1] : 0;
+    const int nb = (incl[s] - excl) / head_groups;
+    const int local = x - excl;
+    const int hg = local / nb;
+    const int n = local - hg * nb;
+    int64_t b = p.block_tables[(int64_t)s * p.max_blocks + n];
+    b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
+    wd.id = (int)b;
+    wd.s = s;
+    int f = hg | (min(kBlockSize, len[s] - n * kBlockSize) << 16);
+    if (n == 0) f |= kSegStart | kPieceFirst;
+    if (n == nb - 1) f |= kSegEnd | kPieceLast;
+    if (x == x1 - 1) f |= kPieceLast;
+    if (x == x0) {
+      f |= kRangeFirst | kPieceFirst;
+      // a range's first piece is the last piece of a split segment exactly
+      // when the segment began in an earlier range and ends in this one
+      p.desc[r] = (n > 0 && nb - n <= x1 - x0) ? int4{s, hg, x - n, nb} : int4{-1, 0, 0, 0};
+    }
+    wd.info = f;
+  }
+  return wd;
+}
+
 template <int DT, int D, int GC>
 __global__ __launch_bounds__(kThreads, (DecodeCfg<DT, D, GC>::kMinWaves)) void
 paged_decode_kernel(const DecodeParams p) {
@@ -386,6 +484,9 @@ paged_decode_kernel(const DecodeParams p) {
   constexpr int EPC = C::kEpc;
 
   __shared__ float sm_p[kWavesPerWG][kBlockSize * GC];
+  __shared__ int sm_incl[kLdsSeqs];
+  __shared__ int sm_len[kLdsSeqs];
+  __shared__ int sm_wsum[kWavesPerWG];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = sread(threadIdx.x >> 6);  // wave index, known uniform to the compiler
@@ -401,14 +502,13 @@ paged_decode_kernel(const DecodeParams p) {
 
   const int head_groups = p.num_heads / GC;
   const int group = p.num_heads / p.num_kv_heads;
-  const int max_tokens = p.max_blocks * kBlockSize;
-  const int T = total_tiles(p, head_groups, lane);
+  const int T = build_segment_table(p, head_groups, sm_incl, sm_len, sm_wsum, lane, w);
 
   // sequences with no cached token: their output is zero
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int s = base + lane;
-    unsigned long long z = __ballot(s < p.num_seqs && s % nwaves == v &&
-                                    clamp_len(p.context_lens[s], max_tokens) == 0);
+    const bool empty = s < p.num_seqs && sm_incl[s] == (s > 0 ? sm_incl[s - 1] : 0);
+    unsigned long long z = __ballot(empty && s % nwaves == v);
     while (z) {
       const int l = __ffsll((long long)z) - 1;
       z &= z - 1;
@@ -417,13 +517,13 @@ paged_decode_kernel(const DecodeParams p) {
     }
   }
 
-  int qt, R;
-  range_shape(T, nwaves, p.tile_cap, qt, R);
+  const RangeMap map = plan_ranges(T, nwaves, p.tile_cap);
   if (v == 0 && lane == 0) {
-    p.header[0] = R;
-    p.header[1] = qt;
+    p.header[0] = map.R;
+    p.header[1] = map.q;
   }
-  if (v >= R) return;
+  const int r0 = v;
+  if (r0 >= map.R) return;
 
   float* pw = sm_p[w];
   const int row = lane & 15;
@@ -432,42 +532,72 @@ paged_decode_kernel(const DecodeParams p) {
   const uint32_t voff_lane = (uint32_t)(lane * 16);
   const int64_t block_stride = (int64_t)p.num_kv_heads * C::kTileB;
 
-  int ls = 0, lexcl = 0;  // locate cursor
-  for (int r = v; r < R; r += nwaves) {
-    const int x0 = r * qt;
-    const int x1 = min(x0 + qt, T);
-    locate(p, head_groups, lane, x0, ls, lexcl);
-    int s = ls;
-    int L = clamp_len(p.context_lens[s], max_tokens);
-    int nb = blocks_of(L);
-    int local = x0 - lexcl;
-    int hg = local / nb;
-    int n0 = local - hg * nb;
-    int x = x0;
-    bool first_piece = true;
-    while (x < x1) {
-      const int n1 = min(nb, n0 + (x1 - x));
-      const int cnt = n1 - n0;
-      const bool complete = n0 == 0 && n1 == nb;
-      const int h0 = hg * GC;
-      const int kvh = h0 / group;
-      if (first_piece && lane == 0) {
-        // a range's first piece is the last piece of a split segment exactly
-        // when the segment began in an earlier range and ends in this one
-        p.desc[r] = (n0 > 0 && n1 == nb) ? int4{s, hg, x - n0, nb} : int4{-1, 0, 0, 0};
-      }
-
-      // query rows as MFMA A operands: row r of chain c is head c*4 + r % kGcq
-      u32x4 qa[C::kNqg][NLD];
+  // query rows as MFMA A operands: row r of chain c is head c*4 + r % kGcq
+  using QRegs = u32x4[C::kNqg][NLD];
+  auto load_q = [&](QRegs& q, int s, int hg) {
 #pragma unroll
-      for (int c = 0; c < C::kNqg; ++c) {
-        const int head = h0 + c * 4 + (row % C::kGcq);
-        const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowB;
+    for (int c = 0; c < C::kNqg; ++c) {
+      const int head = hg * GC + c * 4 + (row % C::kGcq);
+      const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowB;
 #pragma unroll
-        for (int m = 0; m < NLD; ++m) qa[c][m] = load16(qrow + (jg + 4 * m) * 16);
-      }
+      for (int m = 0; m < NLD; ++m) q[c][m] = load16(qrow + (jg + 4 * m) * 16);
+    }
+  };
+  auto load_tile = [&](Tile& t, int id, int hg) {
+    const int64_t off = (int64_t)id * block_stride + (int64_t)(hg * GC / group) * C::kTileB;
+    const char* kb = p.kcache + off;
+    const char* vb = p.vcache + off;
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
+  };
 
-      float m_run[GC], l_run[GC], acc[GC][EPC];
+  // the wave's stream of tiles: windows cw (being computed) and nw (next)
+  Window cw = prepare_window(p, map, sm_incl, sm_len, head_groups, r0, map.start(r0), lane);
+  Window nw = cw;
+  bool have_nw = false;
+  bool no_more = false;  // no range after the current one
+  int ci = 0;
+
+  // q of the current piece (the next piece's, once the current piece's
+  // last tile is computed)
+  QRegs qa;
+
+  // the current piece
+  float m_run[GC], l_run[GC], acc[GC][EPC];
+  bool pc_seg_start = false;
+  int pc_slot = 0;
+
+  auto step = [&](const Tile& tc, Tile& tn) __attribute__((always_inline)) -> bool {
+    // 1. look ahead: prepare the next window (of this range or the next)
+    if (!have_nw && !no_more && cw.cnt - ci <= kPrepAhead) {
+      const int r2 = cw.ends_range ? cw.r + nwaves : cw.r;
+      // both flags set on both paths: a store through a selected address
+      // would keep them in memory
+      have_nw = r2 < map.R;
+      no_more = r2 >= map.R;
+      if (r2 < map.R)
+        nw = prepare_window(p, map, sm_incl, sm_len, head_groups, r2,
+                            cw.ends_range ? map.start(r2) : cw.x + cw.cnt, lane);
+    }
+
+    // 2. issue the loads of the next tile
+    const int info = __builtin_amdgcn_readlane(cw.info, ci);
+    const int s = __builtin_amdgcn_readlane(cw.s, ci);
+    const int hg = info & 0xffff;
+    const int valid = (info >> 16) & 31;  // >= 1; < 16 only in a sequence's last block
+    const bool in_cw = ci + 1 < cw.cnt;
+    const bool more = in_cw || have_nw;
+    // by value: a conditional over the two windows' fields would select
+    // addresses and keep the windows in memory
+    const int j = in_cw ? ci + 1 : 0;
+    const int info_n = __builtin_amdgcn_readlane(pick(in_cw, cw.info, nw.info), j);
+    const int s_n = __builtin_amdgcn_readlane(pick(in_cw, cw.s, nw.s), j);
+    if (more) load_tile(tn, __builtin_amdgcn_readlane(pick(in_cw, cw.id, nw.id), j), info_n & 0xffff);
+
+    // 3. compute the current tile
+    if (info & kPieceFirst) {
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
         m_run[g] = -INFINITY;
@@ -475,92 +605,58 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
       }
-
-      const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
-      const char* kbase = p.kcache + (int64_t)kvh * C::kTileB;
-      const char* vbase = p.vcache + (int64_t)kvh * C::kTileB;
-
-      // the piece's tiles in windows of 64 (one block id per lane)
-      for (int c0 = 0; c0 < cnt; c0 += kWave) {
-        const int wcnt = min(kWave, cnt - c0);
-        int my_id = 0;
-        if (lane < wcnt) {
-          int64_t b = bt_row[n0 + c0 + lane];
-          b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
-          my_id = (int)b;
+      pc_seg_start = (info & kSegStart) != 0;
+      pc_slot = cw.r * 2 + ((info & kRangeFirst) ? 0 : 1);
+    }
+    {
+      float sc[GC];
+#pragma unroll
+      for (int c = 0; c < C::kNqg; ++c) {
+        const floatx4 rr = qk_mfma<DT, NLD>(qa[c], tc);
+#pragma unroll
+        for (int j = 0; j < C::kGcq; ++j) sc[c * 4 + j] = rr[j] * p.scale_log2;
+      }
+      if (row >= valid) {
+#pragma unroll
+        for (int g = 0; g < GC; ++g) sc[g] = -INFINITY;
+      }
+      float pr[GC];
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        const float tmax = uniform(row_max16(sc[g]));
+        if (tmax > m_run[g]) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[g] - tmax);
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[g][e] *= alpha;
+          m_run[g] = tmax;
         }
-        auto load_tile = [&](Tile& t, int i) {
-          const int64_t off = (int64_t)__builtin_amdgcn_readlane(my_id, i) * block_stride;
-          const char* kb = kbase + off;
-          const char* vb = vbase + off;
+        pr[g] = __builtin_amdgcn_exp2f(sc[g] - m_run[g]);
+        l_run[g] += pr[g];
+      }
+      if (lane < kBlockSize) {
 #pragma unroll
-          for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
+        for (int g = 0; g < GC; ++g) pw[lane * GC + g] = pr[g];
+      }
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-          for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
-        };
-        auto compute_tile = [&](const Tile& t, int i) {
-          const int valid = L - (n0 + c0 + i) * kBlockSize;  // >= 1; < 16 only last block
-          float sc[GC];
+      for (int ld = 0; ld < NLD; ++ld) {
+        const int tok = ld * C::kTpl + lane / C::kNch;
+        float pv[GC];
 #pragma unroll
-          for (int c = 0; c < C::kNqg; ++c) {
-            const floatx4 rr = qk_mfma<DT, NLD>(qa[c], t);
+        for (int g = 0; g < GC; ++g) pv[g] = pw[tok * GC + g];
+        u32x4 vv = tc.v[ld];
+        if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int j = 0; j < C::kGcq; ++j) sc[c * 4 + j] = rr[j] * p.scale_log2;
-          }
-          if (row >= valid) {
+        for (int e = 0; e < EPC; ++e) {
+          const float f = elem_to_float<DT>(vv, e);
 #pragma unroll
-            for (int g = 0; g < GC; ++g) sc[g] = -INFINITY;
-          }
-          float pr[GC];
-#pragma unroll
-          for (int g = 0; g < GC; ++g) {
-            const float tmax = uniform(row_max16(sc[g]));
-            if (tmax > m_run[g]) {
-              const float alpha = __builtin_amdgcn_exp2f(m_run[g] - tmax);
-              l_run[g] *= alpha;
-#pragma unroll
-              for (int e = 0; e < EPC; ++e) acc[g][e] *= alpha;
-              m_run[g] = tmax;
-            }
-            pr[g] = __builtin_amdgcn_exp2f(sc[g] - m_run[g]);
-            l_run[g] += pr[g];
-          }
-          if (lane < kBlockSize) {
-#pragma unroll
-            for (int g = 0; g < GC; ++g) pw[lane * GC + g] = pr[g];
-          }
-          __builtin_amdgcn_wave_barrier();
-#pragma unroll
-          for (int ld = 0; ld < NLD; ++ld) {
-            const int tok = ld * C::kTpl + lane / C::kNch;
-            float pv[GC];
-#pragma unroll
-            for (int g = 0; g < GC; ++g) pv[g] = pw[tok * GC + g];
-            u32x4 vv = t.v[ld];
-            if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-              const float f = elem_to_float<DT>(vv, e);
-#pragma unroll
-              for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], f, acc[g][e]);
-            }
-          }
-          __builtin_amdgcn_wave_barrier();
-        };
-
-        // two register tiles, alternating: load i+1 while computing i
-        Tile ta, tb;
-        load_tile(ta, 0);
-        for (int i = 0; i < wcnt; i += 2) {
-          if (i + 1 < wcnt) load_tile(tb, i + 1);
-          compute_tile(ta, i);
-          if (i + 1 < wcnt) {
-            if (i + 2 < wcnt) load_tile(ta, i + 2);
-            compute_tile(tb, i + 1);
-          }
+          for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], f, acc[g][e]);
         }
       }
-
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (info & kPieceLast) {
       // piece totals: l over the 16 token lanes; acc over lanes sharing a chunk
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
@@ -568,7 +664,8 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = sum_over_lane_groups<C::kNch>(acc[g][e]);
       }
-      if (complete) {
+      const int h0 = hg * GC;
+      if (pc_seg_start && (info & kSegEnd)) {  // a whole segment: final output
         if (lane < C::kNch) {
 #pragma unroll
           for (int g = 0; g < GC; ++g) {
@@ -581,8 +678,8 @@ paged_decode_kernel(const DecodeParams p) {
             store_chunk<DT>(dst, o);
           }
         }
-      } else {
-        const int64_t slot = (int64_t)r * 2 + (first_piece ? 0 : 1);
+      } else {  // a piece of a split segment: float32 partials
+        const int64_t slot = pc_slot;
         if (lane < C::kNch) {
 #pragma unroll
           for (int g = 0; g < GC; ++g) {
@@ -601,23 +698,33 @@ paged_decode_kernel(const DecodeParams p) {
           }
         }
       }
-
-      // next piece: the next segment (next head group, or next sequence
-      // that has a cached token)
-      x += cnt;
-      first_piece = false;
-      n0 = 0;
-      if (x < x1) {
-        if (++hg == head_groups) {
-          hg = 0;
-          do {
-            ++s;
-            L = clamp_len(p.context_lens[s], max_tokens);
-          } while (L == 0);
-          nb = blocks_of(L);
-        }
-      }
     }
+
+    // 4. the next tile opens a piece: its q goes into the registers this
+    // tile has finished with, and arrives with that tile's own data
+    if (more && (info_n & kPieceFirst)) load_q(qa, s_n, info_n & 0xffff);
+
+    // 5. advance
+    if (++ci == cw.cnt) {
+      if (!have_nw) return false;
+      cw = nw;
+      have_nw = false;
+      ci = 0;
+    }
+    return true;
+  };
+
+  // two register tiles, alternating: the next tile is in flight while the
+  // current one is computed, across piece, window and range boundaries
+  Tile ta, tb;
+  {
+    const int info = __builtin_amdgcn_readlane(cw.info, 0);
+    load_tile(ta, __builtin_amdgcn_readlane(cw.id, 0), info & 0xffff);
+    load_q(qa, __builtin_amdgcn_readlane(cw.s, 0), info & 0xffff);
+  }
+  for (;;) {
+    if (!step(ta, tb)) break;
+    if (!step(tb, ta)) break;
   }
 }
 
@@ -629,15 +736,18 @@ __global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const Deco
   __shared__ MergeSmem<D, GC> sm;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = sread(threadIdx.x >> 6);
+  RangeMap m;
   const int R = p.header[0];
-  const int qt = p.header[1];
+  m.R = R;
+  m.q = p.header[1];
+  m.T = 0;  // range ends are not needed here
   for (int base = blockIdx.x * kWavesPerWG; base < R; base += gridDim.x * kWavesPerWG) {
     // each wave merges its own range's segment if it has few pieces ...
     const int r = base + w;
     if (r < R) {
       const int4 d = p.desc[r];
       if (d.x >= 0) {
-        const Split sp = split_of(d, qt);
+        const Split sp = split_of(d, m);
         if (sp.np <= kSoloPieces) merge_by_wave<DT, D, GC>(p, sp, lane);
       }
     }
@@ -645,7 +755,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const Deco
     for (int v = 0; v < kWavesPerWG && base + v < R; ++v) {
       const int4 d = p.desc[base + v];
       if (d.x < 0) continue;
-      const Split sp = split_of(d, qt);
+      const Split sp = split_of(d, m);
       if (sp.np > kSoloPieces) merge_by_workgroup<DT, D, GC>(p, sp, lane, w, sm);
     }
   }
@@ -667,6 +777,8 @@ static int resident_workgroups(const void* kernel) {
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
     return 0;
+  // a workgroup puts one wave on each SIMD of its CU
+  if (per_cu > kWavesPerSimd) per_cu = kWavesPerSimd;
   int n = cus * (per_cu > 0 ? per_cu : 1);
   n = n > kMaxWGs ? kMaxWGs : n;
   memo.push_back({{dev, kernel}, n});
@@ -747,7 +859,8 @@ extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
       !partition_ok(partition_size))
     return 0;
   const int gc = heads_per_wg(num_heads, num_kv_heads);
-  const int64_t max_tiles = (int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc);
+  const int per_launch = num_seqs < kLdsSeqs ? num_seqs : kLdsSeqs;
+  const int64_t max_tiles = (int64_t)per_launch * max_blocks_per_seq * (num_heads / gc);
   const int64_t r = max_ranges(max_tiles, partition_size / kBlockSize);
   return workspace_layout(r, gc, head_size).total;
 }
@@ -774,8 +887,10 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
       15u)
     return PKV_ERR_INVALID_ARG;  // rows are read and written 16 bytes at a time
   const int gc = heads_per_wg(num_heads, num_kv_heads);
-  // flattened tile positions are 32-bit
-  if ((int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc) > INT32_MAX)
+  if (num_heads / gc > 0xFFFF) return PKV_ERR_INVALID_ARG;  // head group: 16 bits
+  // flattened tile positions within one launch are 32-bit
+  const int per_launch = num_seqs < kLdsSeqs ? num_seqs : kLdsSeqs;
+  if ((int64_t)per_launch * max_blocks_per_seq * (num_heads / gc) > INT32_MAX)
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
@@ -798,8 +913,9 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.tile_cap = partition_size / kBlockSize;
-  const int64_t r = max_ranges((int64_t)num_seqs * max_blocks_per_seq * (num_heads / gc),
+  const int64_t r = max_ranges((int64_t)per_launch * max_blocks_per_seq * (num_heads / gc),
                                a.tile_cap);
+  if (r > INT32_MAX) return PKV_ERR_INVALID_ARG;
   const WorkspaceLayout wl = workspace_layout(r, gc, head_size);
   a.header = (int*)((char*)workspace + wl.header);
   a.desc = (int4*)((char*)workspace + wl.desc);
@@ -807,11 +923,24 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   a.part_acc = (float*)((char*)workspace + wl.part_acc);
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // start from a clean error state
-  hipError_t e;
-  switch (dtype) {
-    case PKV_F32: e = dispatch_d<PKV_F32>(a, head_size, gc, st); break;
-    case PKV_F16: e = dispatch_d<PKV_F16>(a, head_size, gc, st); break;
-    default: e = dispatch_d<PKV_BF16>(a, head_size, gc, st); break;
+  // one launch (decode + merge) per kLdsSeqs sequences, in stream order;
+  // they share the workspace, which each launch leaves ready for the next
+  const int esz = dtype == PKV_F32 ? 4 : 2;
+  const int64_t row = (int64_t)num_heads * head_size * esz;
+  for (int s0 = 0; s0 < num_seqs; s0 += kLdsSeqs) {
+    DecodeParams b = a;
+    b.num_seqs = num_seqs - s0 < kLdsSeqs ? num_seqs - s0 : kLdsSeqs;
+    b.out = (char*)out + s0 * row;
+    b.query = (const char*)query + s0 * row;
+    b.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
+    b.context_lens = context_lens + s0;
+    hipError_t e;
+    switch (dtype) {
+      case PKV_F32: e = dispatch_d<PKV_F32>(b, head_size, gc, st); break;
+      case PKV_F16: e = dispatch_d<PKV_F16>(b, head_size, gc, st); break;
+      default: e = dispatch_d<PKV_BF16>(b, head_size, gc, st); break;
+    }
+    if (e != hipSuccess) return PKV_ERR_HIP;
   }
-  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return PKV_OK;
 }

@@ -65,15 +65,17 @@ def expected_workspace(ranges, gc, head_size):
 
 def test_workspace_bytes(lib):
     f = lib.paged_attention_workspace_bytes
-    # ranges = max(8192, tiles / tiles-per-piece cap)
-    assert f(64, 40, 40, 128, 128, 16, 0) == expected_workspace(8192, 1, 128)
+    # ranges = max(4096, tiles of one launch / tiles-per-piece cap)
+    assert f(64, 40, 40, 128, 128, 16, 0) == expected_workspace(4096, 1, 128)
     # 64 x 2048-token tables, 40 kv heads, 512-token cap: 327680 / 32 ranges
     assert f(64, 40, 40, 128, 128, 16, 512) == expected_workspace(10240, 1, 128)
     # grouped heads: 4 query heads per kv head share a workgroup
-    assert f(16, 32, 8, 128, 2048, 16, 0) == expected_workspace(8192, 4, 128)
+    assert f(16, 32, 8, 128, 2048, 16, 0) == expected_workspace(4096, 4, 128)
     assert f(16, 32, 8, 128, 2048, 16, 512) == expected_workspace(8192, 4, 128)
     assert f(16, 32, 8, 128, 2048, 16, 16) == expected_workspace(262144, 4, 128)
-    assert f(4, 12, 2, 64, 8, 16, 0) == expected_workspace(8192, 2, 64)   # group 6 -> 2
+    assert f(4, 12, 2, 64, 8, 16, 0) == expected_workspace(4096, 2, 64)   # group 6 -> 2
+    # more than 2048 sequences run as launches of 2048: sized for one launch
+    assert f(5000, 40, 40, 128, 128, 16, 16) == expected_workspace(2048 * 128 * 40, 1, 128)
     assert f(4, 4, 4, 64, 33, 8, 0) == 0          # unsupported block size
     assert f(4, 4, 4, 64, 33, 16, 24) == 0        # not a multiple of 16
     assert f(4, 4, 4, 64, 33, 16, 8192) == 0      # beyond the largest cap
@@ -110,7 +112,9 @@ def test_decode_argument_validation(lib):
     assert decode(lib, ps=-16) == INVALID
     assert decode(lib, query=FAKE + 8) == INVALID         # not 16-byte aligned
     assert decode(lib, out=FAKE + 2) == INVALID           # rows stored 16 B at a time
-    assert decode(lib, S=1 << 20, W=1 << 12) == INVALID   # tile positions beyond 2^31
+    # tile positions of one launch (2048 sequences at most) beyond 2^31
+    assert decode(lib, S=1 << 11, W=1 << 20) == INVALID
+    assert decode(lib, Hq=1 << 17, hkv=1 << 17) == INVALID   # head groups beyond 16 bits
     assert decode(lib) == WORKSPACE                       # workspace is required
     assert decode(lib, ws=FAKE, wsb=16) == WORKSPACE      # ... and must be large enough
     assert decode(lib, ws=FAKE + 8, wsb=1 << 40) == INVALID   # ... and 16-B aligned
