@@ -101,6 +101,7 @@ struct DecodeParams {
   int num_seqs, num_heads, num_kv_heads, max_blocks;
   int64_t num_blocks;
   int tile_cap;        // max tiles per range (0: no cap)
+  int r_max;           // ranges the workspace holds
   int* header;         // [2]  ranges R and tiles per range q of this call
   int4* desc;          // [R]  split segment ending in range r: s, hg, P, nb
   float* part_ml;      // [R][2][GC][2]  running max (log2 units), sum
@@ -295,10 +296,20 @@ __device__ __forceinline__ Split split_of(const int4& d, const RangeMap& m) {
   return x;
 }
 
+// Slot of piece k's partials (range rf + k; the first range's piece may be
+// that range's second).
+__device__ __forceinline__ int64_t piece_slot(const Split& sp, int k) {
+  return (int64_t)(sp.rf + k) * 2 + ((k == 0 && sp.rf_tail) ? 1 : 0);
+}
+
+// Fold pieces k0, k0 + kstep, ... < np into `st`.  Loads go out in batches
+// with no wait between them (indices past the end are clamped to piece k0
+// and skipped when folding), so a batch costs one memory round trip.
 template <int D, int GC>
 __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int kstep,
                             int lane, FoldState<D, GC>& st) {
   using F = FoldState<D, GC>;
+  constexpr int kBatch = F::kCpl == 1 ? 8 : 4;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     st.M[g] = -INFINITY;
@@ -306,34 +317,52 @@ __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int 
   }
 #pragma unroll
   for (int j = 0; j < F::kCpl; ++j) st.O[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = k0; k < sp.np; k += kstep) {
-    const int64_t sl = (int64_t)(sp.rf + k) * 2 + ((k == 0 && sp.rf_tail) ? 1 : 0);
-    float a[GC], b[GC];
+  for (int kb = k0; kb < sp.np; kb += kBatch * kstep) {
+    float ml[kBatch][GC][2];
+    u32x4 ac[kBatch][F::kCpl];
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      const float mk = p.part_ml[(sl * GC + g) * 2 + 0];
-      const float lk = p.part_ml[(sl * GC + g) * 2 + 1];
-      const float Mn = fmaxf(st.M[g], mk);
-      a[g] = __builtin_amdgcn_exp2f(st.M[g] - Mn);
-      b[g] = __builtin_amdgcn_exp2f(mk - Mn);
-      st.S[g] = st.S[g] * a[g] + lk * b[g];
-      st.M[g] = Mn;
+    for (int b = 0; b < kBatch; ++b) {
+      const int k = kb + b * kstep;
+      const int64_t sl = piece_slot(sp, k < sp.np ? k : k0);
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        ml[b][g][0] = p.part_ml[(sl * GC + g) * 2 + 0];
+        ml[b][g][1] = p.part_ml[(sl * GC + g) * 2 + 1];
+      }
+#pragma unroll
+      for (int j = 0; j < F::kCpl; ++j) {
+        const int c = min(lane + j * kWave, F::kChunks - 1);
+        ac[b][j] = load16(p.part_acc + sl * GC * D + c * 4);
+      }
     }
+    // keep the whole batch's loads ahead of the folding (the scheduler
+    // would otherwise interleave them, one round trip per piece)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < F::kCpl; ++j) {
-      const int c = lane + j * kWave;
-      if (c < F::kChunks) {
-        const int g = c * 4 / D;
-        float ag = a[0], bg = b[0];
+    for (int b = 0; b < kBatch; ++b) {
+      if (kb + b * kstep >= sp.np) break;
+      float a[GC], bb[GC];
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        const float mk = ml[b][g][0];
+        const float Mn = fmaxf(st.M[g], mk);
+        a[g] = __builtin_amdgcn_exp2f(st.M[g] - Mn);
+        bb[g] = __builtin_amdgcn_exp2f(mk - Mn);
+        st.S[g] = st.S[g] * a[g] + ml[b][g][1] * bb[g];
+        st.M[g] = Mn;
+      }
+#pragma unroll
+      for (int j = 0; j < F::kCpl; ++j) {
+        const int g = min(lane + j * kWave, F::kChunks - 1) * 4 / D;
+        float ag = a[0], bg = bb[0];
 #pragma unroll
         for (int gg = 1; gg < GC; ++gg) {
           ag = g == gg ? a[gg] : ag;
-          bg = g == gg ? b[gg] : bg;
+          bg = g == gg ? bb[gg] : bg;
         }
-        const u32x4 x = load16(p.part_acc + sl * GC * D + c * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.O[j][e] = fmaf(st.O[j][e], ag, bg * float_of(x[e]));
+        for (int e = 0; e < 4; ++e)
+          st.O[j][e] = fmaf(st.O[j][e], ag, bg * float_of(ac[b][j][e]));
       }
     }
   }
@@ -730,34 +759,43 @@ paged_decode_kernel(const DecodeParams p) {
 
 // ----------------------------------------------------------- merge kernel --
 // Workgroups take four ranges at a time; a range whose descriptor names a
-// split segment gets that segment's pieces merged into its output.
+// split segment gets that segment's pieces merged into its output.  A wave
+// loads its range's descriptor together with the header (the workspace
+// holds r_max descriptors, so the load is in bounds before R is known).
 template <int DT, int D, int GC>
 __global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const DecodeParams p) {
   __shared__ MergeSmem<D, GC> sm;
+  __shared__ int4 sm_desc[kWavesPerWG];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = sread(threadIdx.x >> 6);
+  const int stride = gridDim.x * kWavesPerWG;
+  int base = blockIdx.x * kWavesPerWG;
+  int4 dn = base + w < p.r_max ? p.desc[base + w] : int4{-1, 0, 0, 0};
   RangeMap m;
   const int R = p.header[0];
   m.R = R;
   m.q = p.header[1];
   m.T = 0;  // range ends are not needed here
-  for (int base = blockIdx.x * kWavesPerWG; base < R; base += gridDim.x * kWavesPerWG) {
-    // each wave merges its own range's segment if it has few pieces ...
+  for (; base < R; base += stride) {
     const int r = base + w;
-    if (r < R) {
-      const int4 d = p.desc[r];
-      if (d.x >= 0) {
-        const Split sp = split_of(d, m);
-        if (sp.np <= kSoloPieces) merge_by_wave<DT, D, GC>(p, sp, lane);
-      }
+    const int4 d = r < R ? dn : int4{-1, 0, 0, 0};
+    if (r + stride < min(R, p.r_max)) dn = p.desc[r + stride];
+    // each wave merges its own range's segment if it has few pieces ...
+    if (d.x >= 0) {
+      const Split sp = split_of(d, m);
+      if (sp.np <= kSoloPieces) merge_by_wave<DT, D, GC>(p, sp, lane);
     }
     // ... and the four waves together take those with many
-    for (int v = 0; v < kWavesPerWG && base + v < R; ++v) {
-      const int4 d = p.desc[base + v];
-      if (d.x < 0) continue;
-      const Split sp = split_of(d, m);
+    if (lane == 0) sm_desc[w] = d;
+    __syncthreads();
+#pragma unroll 1
+    for (int u = 0; u < kWavesPerWG; ++u) {
+      const int4 du = sm_desc[u];
+      if (du.x < 0) continue;
+      const Split sp = split_of(du, m);
       if (sp.np > kSoloPieces) merge_by_workgroup<DT, D, GC>(p, sp, lane, w, sm);
     }
+    __syncthreads();
   }
 }
 
@@ -916,6 +954,7 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   const int64_t r = max_ranges((int64_t)per_launch * max_blocks_per_seq * (num_heads / gc),
                                a.tile_cap);
   if (r > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  a.r_max = (int)r;
   const WorkspaceLayout wl = workspace_layout(r, gc, head_size);
   a.header = (int*)((char*)workspace + wl.header);
   a.desc = (int4*)((char*)workspace + wl.desc);
