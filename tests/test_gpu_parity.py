@@ -232,8 +232,8 @@ def test_padding_slots_are_skipped(gpu_lib):
 
 
 def test_workspace_reused_across_calls(gpu_lib):
-    """One zero-filled workspace serves consecutive calls of different shapes:
-    each call leaves the range counter at zero for the next."""
+    """One workspace serves consecutive calls of different shapes: every call
+    writes the header, descriptors and partials it reads."""
     w1 = dataclasses.replace(W["opt13b"], num_seqs=8)
     w2 = wl.custom([5, 700, 33, 1200], 32, 8, 128, "bf16", max_len=2048)
     ws = torch.zeros(max(pkv.workspace_bytes(8, 40, 40, 128, 128),
@@ -249,3 +249,53 @@ def test_workspace_reused_across_calls(gpu_lib):
         torch.cuda.synchronize()
         ref = oracle_decode_subset(b, kc0, vc0, list(range(w.num_seqs)))
         assert_close(out, ref, w.dtype, f"reuse {w.key} seed {seed}")
+
+
+@pytest.mark.parametrize("key", ["opt13b", "gqa"])
+def test_graph_replay_matches_eager(gpu_lib, key):
+    """One step (reshape_and_cache, then decode) captured in a HIP graph and
+    replayed: every replay, with eager steps in between, gives the eager
+    step's output bit for bit, and that output matches the oracle."""
+    if key == "gqa":
+        w = wl.custom([5, 700, 33, 1200, 2048, 16], 32, 8, 128, "bf16", max_len=2048)
+    else:
+        w = dataclasses.replace(W["opt13b"], num_seqs=8)
+    b = wl.make_batch(w, 7, DEV)
+    lens = b["context_lens"]
+    kc0, vc0 = clone_pools(b)
+    bt, cl = dev_i32(b["block_tables"]), dev_i32(lens)
+    pos = lens.astype(np.int64) - 1
+    slots = torch.from_numpy(b["block_tables"][np.arange(len(lens)), pos // 16].astype(np.int64)
+                             * 16 + pos % 16).to(DEV)
+    # the appended token is the one already cached there: the pool is unchanged
+    key_new = b["key_cache"][slots // 16, :, slots % 16, :].contiguous()
+    val_new = b["value_cache"][slots // 16, :, slots % 16, :].contiguous()
+    ws = torch.zeros(pkv.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
+                                         b["block_tables"].shape[1]), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(b["query"])
+
+    def step():
+        pkv.reshape_and_cache(key_new, val_new, slots, b["key_cache"], b["value_cache"])
+        pkv.paged_attention_decode(out, b["query"], b["key_cache"], b["value_cache"], bt, cl,
+                                   float(w.scale), w.num_kv_heads, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_close(eager, oracle_decode_subset(b, kc0, vc0, list(range(w.num_seqs))), w.dtype,
+                 f"graph {key} eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager step"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"eager step after replay {i} differs"
