@@ -12,10 +12,14 @@ key/value bytes the attention must read (sum of context lengths x 2 x
 kv_heads x head_size x element bytes) divided by the step time.
 `roofline` covers the dominant kernel call, paged_attention_decode, timed
 with events on the launch stream; `cpu_baseline` times the float64 CPU
-oracle on a bounded sample of the same batch (single thread).
+oracle on a bounded sample of the same batch (single thread);
+`translation` times the same decode call on the same batch laid out with
+every sequence's blocks physically consecutive (identity block tables),
+against the random placement.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b]
                     [--also long_gqa,llama13b_conv,sampling_cow] [--no-cpu-baseline]
+                    [--no-translation]
 """
 
 import argparse
@@ -44,6 +48,8 @@ def parse():
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--also", default="long_gqa,llama13b_conv,sampling_cow")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-translation", action="store_true",
+                    help="skip the random vs contiguous placement comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--partition-size", type=int, default=None,
                     help="cap on tokens per piece (default: the workload's, 0 = none)")
@@ -193,6 +199,69 @@ def measure(w, seed, steps, warmup, ps):
     return r, st
 
 
+def contiguous_layout(st):
+    """The same batch with every sequence's blocks made physically
+    consecutive, in sequence order (identity block tables): the pool is
+    permuted and the tables renumbered, so the attention result is the same.
+    None if blocks are shared between sequences."""
+    torch, b = st.torch, st.b
+    bt, lens = b["block_tables"], st.lens
+    order = []
+    for s in range(len(lens)):
+        order.extend(int(x) for x in bt[s, :-(-int(lens[s]) // 16)])
+    if len(set(order)) != len(order):
+        return None
+    nb = b["key_cache"].shape[0]
+    used = set(order)
+    old_of_new = np.asarray(order + [x for x in range(nb) if x not in used], np.int64)
+    new_of_old = np.empty(nb, np.int64)
+    new_of_old[old_of_new] = np.arange(nb)
+    tables = np.where(bt >= 0, new_of_old[np.maximum(bt, 0)], -1).astype(np.int32)
+    idx = torch.from_numpy(old_of_new).to("cuda:0")
+    return (b["key_cache"].index_select(0, idx), b["value_cache"].index_select(0, idx),
+            torch.from_numpy(tables).to("cuda:0"))
+
+
+def translation_overhead(st, steps):
+    """Decode-call time with the batch's random block placement against the
+    same batch laid out contiguously (same kernel, same values, identity
+    tables), the two timed alternately."""
+    lay = contiguous_layout(st)
+    if lay is None:
+        return None
+    torch, b, w = st.torch, st.b, st.w
+    kc2, vc2, bt2 = lay
+    out2 = torch.empty_like(st.out)
+
+    def call(kc, vc, bt, out):
+        st.pkv.paged_attention_decode(out, b["query"], kc, vc, bt, st.cl, float(w.scale),
+                                      w.num_kv_heads, partition_size=st.ps, workspace=st.ws)
+
+    args = [(b["key_cache"], b["value_cache"], st.bt, st.out), (kc2, vc2, bt2, out2)]
+    for _ in range(3):
+        for a in args:
+            call(*a)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] for _ in args]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for j, a in enumerate(args):
+            ev[j][i][0].record()
+            call(*a)
+            ev[j][i][1].record()
+    torch.cuda.synchronize()
+    us = [1000.0 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev[j]])) for j in range(2)]
+    r = {"workload": w.key,
+         "random_placement_call_us": round(us[0], 2),
+         "contiguous_placement_call_us": round(us[1], 2),
+         "translation_overhead_pct": round(100.0 * (us[0] / us[1] - 1.0), 2),
+         "outputs_bitwise_equal": bool(torch.equal(st.out, out2)),
+         "layout": "each sequence's blocks physically consecutive in sequence order "
+                   "(identity block tables); same kernel, values and tables' content"}
+    del kc2, vc2
+    return r
+
+
 def traffic_for_current_kernel(workload):
     """HBM bytes per decode call from committed PMC counters, if the kernel
     source is unchanged since they were taken (else None)."""
@@ -282,6 +351,7 @@ def main():
     print(f"# measuring {w.key}", file=sys.stderr, flush=True)
     main_r, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size)
     cpu = None if a.no_cpu_baseline else cpu_baseline(st, a.cpu_seconds)
+    trans = None if a.no_translation else translation_overhead(st, a.steps)
     del st
     torch.cuda.empty_cache()
 
@@ -331,6 +401,7 @@ def main():
             "avg_call_ms": round(dec_ms, 5),
         },
         "cpu_baseline": cpu,
+        "translation": trans,
         "workloads": {w.key: main_r, **others},
     }
     print(json.dumps(line), flush=True)
