@@ -1,8 +1,12 @@
-"""Build libpagedkv.so (the C-ABI library) from the HIP sources, for gfx950.
+"""Build the two C-ABI libraries.
 
-Every source is compiled by hipcc into an object under csrc/_build/, then
-linked into paged_kv_cache_311_amd/libpagedkv.so.  Packed-FP32 VALU
-instructions are disabled for device code.  Usable as a script:
+* libpagedkv.so -- the GPU path, from the HIP sources, for gfx950: every
+  source is compiled by hipcc into an object under csrc/_build/, then
+  linked.  Packed-FP32 VALU instructions are disabled for device code.
+* libpkvhost.so -- the host block manager and decode-loop simulator, plain
+  C++ built with g++ (no GPU code).
+
+Usable as a script:
     python -m paged_kv_cache_311_amd.build_lib
 """
 
@@ -18,6 +22,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(CSRC, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ["paged_attention.hip", "cache_ops.hip"]
+HOST_LIB_PATH = os.path.join(HERE, "libpkvhost.so")
+HOST_SOURCES = ["block_manager.cpp"]
+CXX = os.environ.get("CXX", "g++")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -55,8 +62,20 @@ def _run(cmd):
     return err
 
 
+def build_host(verbose=False):
+    """Compile the host library (always rebuilds)."""
+    tmp = HOST_LIB_PATH + ".tmp"
+    warn = _run([CXX, "-O2", "-std=c++17", "-Wall", "-Wextra", "-fPIC", "-shared",
+                 *[os.path.join(CSRC, f) for f in HOST_SOURCES], "-o", tmp])
+    if verbose and warn.strip():
+        print(warn, file=sys.stderr)
+    os.replace(tmp, HOST_LIB_PATH)
+    return HOST_LIB_PATH
+
+
 def build(verbose=False):
-    """Compile every HIP source and link the shared library (always rebuilds)."""
+    """Compile every HIP source and link the GPU library, then the host
+    library (always rebuilds both)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
 
     stamp = f'-DPKV_BUILD_ID="{source_digest()}"'
@@ -73,6 +92,7 @@ def build(verbose=False):
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    build_host(verbose)
     return LIB_PATH
 
 

@@ -1,0 +1,93 @@
+"""The host block manager driving the GPU path through a beam-search-like
+decode loop (marked gpu).
+
+Prompts are cached with reshape_and_cache, beams fork from them (shared
+blocks, reference counts), and every step takes one new token for each live
+beam from the manager: its copy-on-write pairs go to copy_blocks, its slots
+to reshape_and_cache, its block tables and lengths to paged_attention_decode.
+Beams are killed and forked along the way, so blocks are released and
+reused.  After every step the pools must equal the oracle's replay of the
+same updates bit for bit, and the attention output must match the oracle's
+within the tolerances of the parity tests ("Your GPU was mostly empty..."
+[TEQ], "Paging's second gift: copy-on-write"; "PagedAttention KV cache
+memory management" [AITJ], "A request lifecycle: allocation, growth,
+sharing and release").
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_311_amd as pkv
+from paged_kv_cache_311_amd import host
+from paged_kv_cache_311_amd import workloads as wl
+from tests.gpu_helpers import DEV, assert_close, say
+
+pytestmark = pytest.mark.gpu
+
+BS = 16
+
+
+@pytest.mark.parametrize("num_heads,num_kv_heads,dtype", [(8, 2, "f16"), (4, 4, "bf16")])
+def test_beam_decode_loop_driven_by_host_manager(gpu_lib, num_heads, num_kv_heads, dtype):
+    rng = np.random.default_rng(311)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(311)
+    td = wl.torch_dtype(dtype)
+    NB, D, W = 96, 128, 8
+    randn = lambda *shape: torch.randn(shape, generator=gen, device=DEV).to(td)
+    kc = torch.full((NB, num_kv_heads, BS, D), float("nan"), dtype=td, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    kc_h, vc_h = wl.to_host(kc), wl.to_host(vc)
+    bm = host.BlockManager(NB, BS)
+
+    def write(seq_slots, key, val):
+        nonlocal kc_h, vc_h
+        pkv.reshape_and_cache(key, val, torch.from_numpy(seq_slots).to(DEV), kc, vc)
+        kc_h, vc_h = oracle.reshape_and_cache(wl.to_host(key), wl.to_host(val), seq_slots,
+                                              kc_h, vc_h)
+
+    for s, P in ((0, 37), (1, 50)):                      # prompts
+        bm.add_sequence(s, P)
+        t = np.arange(P)
+        write(bm.block_table(s)[t // BS].astype(np.int64) * BS + t % BS,
+              randn(P, num_kv_heads, D), randn(P, num_kv_heads, D))
+    live, next_id = [0, 1], 2
+    for parent, n in ((0, 3), (1, 2)):                   # beams share the prompts
+        for _ in range(n):
+            bm.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+    scale = 1.0 / math.sqrt(D)
+    copies = 0
+    for step in range(24):
+        if step % 6 == 5:                                # a beam dies, another splits
+            bm.free_sequence(live.pop(int(rng.integers(len(live)))))
+            bm.fork(live[int(rng.integers(len(live)))], next_id)
+            live.append(next_id)
+            next_id += 1
+        slots, pairs = bm.append_slots(live)
+        if len(pairs):
+            copies += len(pairs)
+            pkv.copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV))
+            kc_h, vc_h = oracle.copy_blocks(kc_h, vc_h, pairs)
+        write(slots, randn(len(live), num_kv_heads, D), randn(len(live), num_kv_heads, D))
+        tables, lens = bm.block_tables(live, W)
+        q = randn(len(live), num_heads, D)
+        out = torch.empty_like(q)
+        pkv.paged_attention_decode(out, q, kc, vc, torch.from_numpy(tables).to(DEV),
+                                   torch.from_numpy(lens).to(DEV), scale, num_kv_heads)
+        torch.cuda.synchronize()
+        assert wl.to_host(kc).view(np.uint16).tobytes() == kc_h.view(np.uint16).tobytes()
+        assert wl.to_host(vc).view(np.uint16).tobytes() == vc_h.view(np.uint16).tobytes()
+        ref = oracle.decode_attention(wl.to_host(q), kc_h, vc_h, tables, lens, scale,
+                                      num_kv_heads, dtype)
+        assert_close(out, ref, dtype, f"step {step}")
+    say(f"    {copies} copy-on-write pairs, {bm.num_free} blocks free at the end")
+    assert copies > 0
+    for s in live:
+        bm.free_sequence(s)
+    assert bm.num_free == NB
