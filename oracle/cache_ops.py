@@ -82,3 +82,16 @@ def copy_blocks(key_cache, value_cache, src_dst_pairs):
         vc[d] = v_src[s]
     return (kc.view(np.asarray(key_cache).dtype),
             vc.view(np.asarray(value_cache).dtype))
+
+
+def reshape_and_cache_fp8(key, value, slot_mapping, key_cache, value_cache, k_scale,
+                          v_scale, dtype, block_size=16):
+    """reshape_and_cache into e4m3 pools (uint8 codes): each new key
+    element is stored as the code of key / k_scale (values: / v_scale),
+    quantized as in oracle.fp8.quantize, then scattered like the bits of
+    any other format."""
+    from .fp8 import quantize
+    kq = quantize(key, dtype, k_scale)
+    vq = quantize(value, dtype, v_scale)
+    return reshape_and_cache(kq, vq, slot_mapping, key_cache, value_cache, block_size)
+

@@ -81,16 +81,20 @@ def attention_one_head(q, keys, values, scale):
 
 
 def decode_attention(query, key_cache, value_cache, block_tables, context_lens,
-                     scale, num_kv_heads, dtype, block_size=16, seqs=None):
+                     scale, num_kv_heads, dtype, block_size=16, seqs=None,
+                     kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Decode-step attention of every (sequence, query head), float64.
 
     query        [S, Hq, D]            storage format of `dtype`
-    key_cache    [NB, Hkv, bs, D]      storage format of `dtype`
-    value_cache  [NB, Hkv, bs, D]
+    key_cache    [NB, Hkv, bs, D]      storage format of `kv_dtype`
+    value_cache  [NB, Hkv, bs, D]      (default: `dtype`)
     block_tables [S, W] integer        physical block of each logical block
     context_lens [S] integer
     scale        float32 value (widened exactly)
     seqs         optional list of sequence indices to compute (others stay 0)
+    k_scale, v_scale  float32 per-pool scales: a cached key element's value
+                 is its decoded storage value times k_scale (values: v_scale);
+                 1 for pools that hold the values themselves
 
     Returns [S, Hq, D] float64.
     """
@@ -98,16 +102,19 @@ def decode_attention(query, key_cache, value_cache, block_tables, context_lens,
     if Hq % num_kv_heads:
         raise ValueError("query heads must be a multiple of kv heads")
     group = Hq // num_kv_heads
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     scale64 = float(np.float32(scale))
+    k_scale64 = float(np.float32(k_scale))
+    v_scale64 = float(np.float32(v_scale))
     out = np.zeros((S, Hq, D), dtype=np.float64)
     for s in (range(S) if seqs is None else seqs):
         L = int(context_lens[s])
         q_s = to_f64(query[s], dtype)
         for g in range(num_kv_heads):
-            keys = gather_sequence_kv(key_cache, block_tables[s], L, g, dtype,
-                                      block_size)
+            keys = gather_sequence_kv(key_cache, block_tables[s], L, g, kv_dtype,
+                                      block_size) * k_scale64
             values = gather_sequence_kv(value_cache, block_tables[s], L, g,
-                                        dtype, block_size)
+                                        kv_dtype, block_size) * v_scale64
             for h in range(g * group, (g + 1) * group):
                 out[s, h] = attention_one_head(q_s[h], keys, values, scale64)
     return out

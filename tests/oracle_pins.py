@@ -425,9 +425,99 @@ def pin_formats(o):
     assert np.array_equal(o.to_f64(f, "f32"), f.astype(np.float64))
 
 
+def _torch_e4m3(x32):
+    """torch's float8_e4m3fn codes of float32 values (a library routine
+    independent of the oracle; it rounds to nearest even and gives NaN
+    beyond the largest finite value, so callers stay below 448)."""
+    return torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_codec(o):
+    """OCP E4M3: every code decodes as torch's float8_e4m3fn does; hand
+    values of the definition; encoding rounds as torch wherever torch stays
+    finite (random values, every code's value, every midpoint between
+    neighbouring codes: the ties); the round trip of every code; saturation
+    at +-448 and NaN (the reading for values torch would turn into NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    d = o.e4m3_decode(codes)
+    t = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(t)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(d), nan)
+    assert np.array_equal(d[~nan], t[~nan])
+    assert np.array_equal(np.signbit(d[~nan]), np.signbit(t[~nan]))
+    for c, v in ((0x38, 1.0), (0x40, 2.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9),
+                 (0x08, 2.0 ** -6), (0x0F, 1.875 * 2.0 ** -6), (0x80, -0.0), (0xB8, -1.0)):
+        assert d[c] == v and np.signbit(d[c]) == np.signbit(v), hex(c)
+    rng = np.random.default_rng(8)
+    pos = d[(~nan) & (codes < 0x80)]
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)      # exact in float32
+    x = np.concatenate([rng.standard_normal(20000) * sd for sd in (0.003, 1.0, 60.0)] +
+                       [mids, -mids, pos, -pos]).astype(np.float32)
+    x = x[np.abs(x) < 448]
+    assert np.array_equal(o.e4m3_encode(x), _torch_e4m3(x))
+    assert np.array_equal(o.e4m3_encode(d[~nan].astype(np.float32)), codes[~nan])
+    sat = o.e4m3_encode(np.float32([448.0, 460.0, 1e6, -1e30, np.inf, -np.inf]))
+    assert sat.tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE]
+    assert o.e4m3_encode(np.float32([np.nan])).tolist() == [0x7F]
+
+
+def pin_reshape_fp8(o):
+    """New tokens land in their slots as the codes of value / scale (the
+    quotient in float32, encoded by torch), untouched slots keep their
+    codes, negative slots are skipped."""
+    rng = np.random.default_rng(9)
+    NB, Hkv, D = 6, 2, 8
+    kc = rng.integers(0, 256, (NB, Hkv, BS, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (NB, Hkv, BS, D), dtype=np.uint8)
+    key = (rng.standard_normal((5, Hkv, D)) * 3).astype(np.float16)
+    val = (rng.standard_normal((5, Hkv, D)) * 3).astype(np.float16)
+    slots = np.array([17, -1, 0, 95, 40], np.int64)
+    ks, vs = np.float32(0.0625), np.float32(0.03)
+    nk, nv = o.reshape_and_cache_fp8(key, val, slots, kc, vc, ks, vs, "f16")
+    ek, ev = kc.copy(), vc.copy()
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, off = divmod(int(slot), BS)
+        ek[b, :, off, :] = _torch_e4m3(key[i].astype(np.float32) / ks)
+        ev[b, :, off, :] = _torch_e4m3(val[i].astype(np.float32) / vs)
+    assert nk.dtype == np.uint8 and np.array_equal(nk, ek) and np.array_equal(nv, ev)
+
+
+def pin_decode_fp8(o):
+    """Attention over e4m3 pools with per-pool scales equals attention over
+    float32 pools holding decode(code) * scale, decoded by torch (scales are
+    powers of two, so those products are exact)."""
+    rng = np.random.default_rng(10)
+    lens, Hq, Hkv, D = [1, 17, 40], 4, 2, 8
+    NB = 12
+    kc = rng.integers(0, 0x7E, (NB, Hkv, BS, D), dtype=np.uint8)
+    vc = rng.integers(0, 0x7E, (NB, Hkv, BS, D), dtype=np.uint8)
+    kc ^= (rng.integers(0, 2, kc.shape) * 0x80).astype(np.uint8)   # both signs
+    vc ^= (rng.integers(0, 2, vc.shape) * 0x80).astype(np.uint8)
+    tables = np.full((3, 4), -1, np.int64)
+    perm = rng.permutation(NB)
+    n = 0
+    for s, L in enumerate(lens):
+        nbk = -(-L // BS)
+        tables[s, :nbk] = perm[n:n + nbk]
+        n += nbk
+    q = rng.standard_normal((3, Hq, D)).astype(np.float16)
+    ks, vs = np.float32(0.125), np.float32(4.0)
+    got = o.decode_attention(q, kc, vc, tables, np.array(lens), 0.5, Hkv, "f16",
+                             kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    dec = lambda c: torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    want = o.decode_attention(q, dec(kc) * ks, dec(vc) * vs, tables, np.array(lens), 0.5, Hkv,
+                              "f16", kv_dtype="f32")
+    assert np.array_equal(got, want)
+    assert np.isfinite(got).all() and np.abs(got).max() > 0
+
+
 ALL_PINS = [
     pin_brute_force, pin_torch_sdpa, pin_permutation_invariance,
     pin_gqa_reduction, pin_sharing_invariance, pin_partition_merge,
     pin_special_cases, pin_kv_bytes, pin_waste_bound,
     pin_reshape_and_cache, pin_copy_blocks, pin_formats,
+    pin_e4m3_codec, pin_reshape_fp8, pin_decode_fp8,
 ]

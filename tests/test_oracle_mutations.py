@@ -73,6 +73,24 @@ MUTANTS = [
     ("waste_off_by_one", "kv_accounting.py",
      "* block_size - context_len\n", "* block_size - context_len - 1\n"),
     ("bf16_shift", "formats.py", "<< 16", "<< 15"),
+    ("e4m3_bias_8", "fp8.py", "2.0 ** (e - 7.0)", "2.0 ** (e - 8.0)"),
+    ("e4m3_subnormal_scale", "fp8.py", "(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7"),
+    ("e4m3_no_nan_code", "fp8.py", "mag = np.where((e == 15) & (m == 7), np.nan, mag)",
+     "mag = mag"),
+    ("e4m3_truncates", "fp8.py", "f8 = np.rint((2.0 * mant - 1.0) * 8.0)",
+     "f8 = np.floor((2.0 * mant - 1.0) * 8.0)"),
+    ("e4m3_saturates_to_nan", "fp8.py", "code = np.where(a >= MAX, 126.0, code)",
+     "code = np.where(a >= MAX, 127.0, code)"),
+    ("e4m3_subnormal_grid", "fp8.py", "q_sub = np.rint(a * 512.0)", "q_sub = np.rint(a * 256.0)"),
+    ("e4m3_quantize_multiplies", "fp8.py", "q = v / np.float32(scale)",
+     "q = v * np.float32(scale)"),
+    ("fp8_key_scale_dropped", "paged_attention.py",
+     "L, g, kv_dtype,\n                                      block_size) * k_scale64",
+     "L, g, kv_dtype,\n                                      block_size)"),
+    ("fp8_value_scale_dropped", "paged_attention.py",
+     "kv_dtype, block_size) * v_scale64", "kv_dtype, block_size)"),
+    ("reshape_fp8_key_scale_for_value", "cache_ops.py",
+     "vq = quantize(value, dtype, v_scale)", "vq = quantize(value, dtype, k_scale)"),
 ]
 
 
