@@ -18,7 +18,8 @@ every sequence's blocks physically consecutive (identity block tables),
 against the random placement.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b]
-                    [--also long_gqa,llama13b_conv,sampling_cow] [--no-cpu-baseline]
+                    [--also long_gqa,llama13b_conv,sampling_cow,opt13b_fp8,long_gqa_fp8]
+                    [--no-cpu-baseline]
                     [--no-translation]
 """
 
@@ -46,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b")
-    ap.add_argument("--also", default="long_gqa,llama13b_conv,sampling_cow")
+    ap.add_argument("--also",
+                    default="long_gqa,llama13b_conv,sampling_cow,opt13b_fp8,long_gqa_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-translation", action="store_true",
                     help="skip the random vs contiguous placement comparison")
@@ -81,13 +83,14 @@ def copy_calibration(mib, steps):
 
 
 def kv_bytes(w, lens):
-    eb = 4 if w.dtype == "f32" else 2
-    return int(np.asarray(lens, np.int64).sum()) * 2 * w.num_kv_heads * w.head_size * eb
+    return (int(np.asarray(lens, np.int64).sum()) * 2 * w.num_kv_heads * w.head_size
+            * w.kv_elem_bytes)
 
 
 def decode_algorithmic_bytes(w, lens):
-    """Bytes the decode must move: K/V of every context token, q in, out,
-    the block-table entries it follows and the lengths."""
+    """Bytes the decode must move: K/V of every context token (in the pool's
+    format: 1 byte per element for E4M3 pools), q in, out, the block-table
+    entries it follows and the lengths."""
     eb = 4 if w.dtype == "f32" else 2
     lens = np.asarray(lens, np.int64)
     qo = 2 * w.num_seqs * w.num_heads * w.head_size * eb
@@ -134,18 +137,30 @@ class Step:
         self.new_tokens = len(slots)
 
     def updates(self):
-        b = self.b
+        b, w = self.b, self.w
         if self.pairs is not None:
             self.pkv.copy_blocks(b["key_cache"], b["value_cache"], self.pairs)
-        self.pkv.reshape_and_cache(self.key, self.value, self.slots, b["key_cache"],
-                                   b["value_cache"])
+        if w.fp8:
+            self.pkv.reshape_and_cache_fp8(self.key, self.value, self.slots, b["key_cache"],
+                                           b["value_cache"], w.k_scale, w.v_scale)
+        else:
+            self.pkv.reshape_and_cache(self.key, self.value, self.slots, b["key_cache"],
+                                       b["value_cache"])
+
+    def decode_into(self, out, kc, vc, bt):
+        b, w = self.b, self.w
+        if w.fp8:
+            self.pkv.paged_attention_decode_fp8(out, b["query"], kc, vc, bt, self.cl,
+                                                float(w.scale), w.k_scale, w.v_scale,
+                                                w.num_kv_heads, partition_size=self.ps,
+                                                workspace=self.ws)
+        else:
+            self.pkv.paged_attention_decode(out, b["query"], kc, vc, bt, self.cl,
+                                            float(w.scale), w.num_kv_heads,
+                                            partition_size=self.ps, workspace=self.ws)
 
     def decode(self):
-        b, w = self.b, self.w
-        self.pkv.paged_attention_decode(self.out, b["query"], b["key_cache"],
-                                        b["value_cache"], self.bt, self.cl, float(w.scale),
-                                        w.num_kv_heads, partition_size=self.ps,
-                                        workspace=self.ws)
+        self.decode_into(self.out, self.b["key_cache"], self.b["value_cache"], self.bt)
 
     def run(self, steps, warmup):
         torch = self.torch
@@ -182,7 +197,7 @@ def measure(w, seed, steps, warmup, ps):
     r = {
         "workload": w.key, "seed": seed, "seqs": w.num_seqs,
         "heads": w.num_heads, "kv_heads": w.num_kv_heads, "head_size": w.head_size,
-        "dtype": w.dtype, "partition_size": st.ps,
+        "dtype": w.dtype, "kv_dtype": w.kv_dtype or w.dtype, "partition_size": st.ps,
         "kv_tokens": int(st.lens.astype(np.int64).sum()), "kv_bytes_per_step": kvb,
         "new_tokens_per_step": st.new_tokens,
         "cow_pairs_per_step": 0 if st.pairs is None else int(st.pairs.shape[0]),
@@ -234,8 +249,7 @@ def translation_overhead(st, steps):
     out2 = torch.empty_like(st.out)
 
     def call(kc, vc, bt, out):
-        st.pkv.paged_attention_decode(out, b["query"], kc, vc, bt, st.cl, float(w.scale),
-                                      w.num_kv_heads, partition_size=st.ps, workspace=st.ws)
+        st.decode_into(out, kc, vc, bt)
 
     args = [(b["key_cache"], b["value_cache"], st.bt, st.out), (kc2, vc2, bt2, out2)]
     for _ in range(3):
@@ -296,20 +310,20 @@ def cpu_baseline(st, budget_s):
         n = -(-int(lens[s]) // 16)
         tables[s, :n] = [remap[int(x)] for x in bt[s, :n]]
     q = wl.to_host(b["query"])[:n_max]
+    fp8 = (dict(kv_dtype="e4m3", k_scale=w.k_scale, v_scale=w.v_scale) if w.fp8 else {})
     done, tokens, t_used = 0, 0, 0.0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while t_used < budget_s:       # whole passes over the sample until the budget
             for s in range(n_max):
                 oracle.decode_attention(q, kc, vc, tables, lens[:n_max], w.scale,
-                                        w.num_kv_heads, w.dtype, seqs=[s])
+                                        w.num_kv_heads, w.dtype, seqs=[s], **fp8)
                 done += 1
                 tokens += int(lens[s])
                 t_used = time.perf_counter() - t0
                 if t_used >= budget_s:
                     break
-    eb = 4 if w.dtype == "f32" else 2
-    kvb = tokens * 2 * w.num_kv_heads * w.head_size * eb
+    kvb = tokens * 2 * w.num_kv_heads * w.head_size * w.kv_elem_bytes
     return {
         "value": kvb / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": (f"float64 numpy oracle, one thread, the first {n_max} of {w.num_seqs} "

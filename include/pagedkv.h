@@ -7,7 +7,9 @@
  *                           query head), reading keys and values through
  *                           each sequence's block table;
  *   reshape_and_cache       scatter new tokens' keys/values to their slots;
- *   copy_blocks             block-level copy-on-write of shared blocks.
+ *   copy_blocks             block-level copy-on-write of shared blocks;
+ * and the first two again for pools of 8-bit float (E4M3) codes with one
+ * scale per pool (paged_attention_decode_fp8, reshape_and_cache_fp8).
  *
  * Sources (titles of the pages this library follows):
  *   [TEQ]  "Your GPU was mostly empty: how PagedAttention turned KV-cache
@@ -57,7 +59,10 @@
 extern "C" {
 #endif
 
-enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+/* Element formats.  PKV_FP8_E4M3 is a KV-pool format only (the OCP 8-bit
+ * float E4M3: bias 7, 3 mantissa bits, largest finite 448, S.1111.111 =
+ * NaN): pools in it go with the _fp8 entry points and copy_blocks. */
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 };
 
 enum pkv_status {
   PKV_OK = 0,
@@ -68,7 +73,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 2 */
+int pkv_abi_version(void);  /* 3 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -194,6 +199,47 @@ int reshape_and_cache(const void* key, const void* value,
 int copy_blocks(void* key_cache, void* value_cache, const int64_t* src_dst_pairs,
                 int num_pairs, int num_kv_heads, int head_size, int block_size,
                 int64_t num_blocks, int dtype, void* stream);
+
+/*
+ * fp8 KV pools.  A pool may hold E4M3 codes (one byte per element, same
+ * [num_blocks][num_kv_heads][16][head_size] layout) with one float32 scale
+ * per pool: the key element a code stands for is e4m3(code) * k_scale, the
+ * value element e4m3(code) * v_scale.  Half the bytes of a 16-bit pool per
+ * token, so twice the tokens per byte of HBM ([AITJ] "PagedAttention vs
+ * KV-cache quantization vs prefix caching": quantization changes how
+ * densely cached tensors are stored, paging where they are stored).
+ * copy_blocks moves such pools with dtype = PKV_FP8_E4M3.
+ *
+ * reshape_and_cache_fp8: as reshape_and_cache, but each element x of
+ * key[i] (of `dtype`, 16- or 32-bit) is stored as the code nearest to the
+ * float32 quotient x / k_scale (values: / v_scale), ties to the even
+ * mantissa; quotients of magnitude >= 448 (inf included) saturate to
+ * +-448, NaN becomes 0x7F.  Scales must be finite and > 0.
+ */
+int reshape_and_cache_fp8(const void* key, const void* value,
+                          const int64_t* slot_mapping, void* key_cache,
+                          void* value_cache, float k_scale, float v_scale,
+                          int num_tokens, int num_kv_heads, int head_size,
+                          int block_size, int64_t num_blocks, int dtype,
+                          void* stream);
+
+/*
+ * paged_attention_decode_fp8: paged_attention_decode over E4M3 pools, the
+ * keys and values being the codes' values times k_scale and v_scale.
+ * query and out are `dtype` (PKV_F16 or PKV_BF16); every other argument,
+ * the workspace (paged_attention_workspace_bytes with the same sizes) and
+ * the error behaviour are those of paged_attention_decode.  Codes widen
+ * exactly to `dtype` for the QK products (float32 accumulation); the
+ * scales are applied in float32.
+ */
+int paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, float k_scale,
+                               float v_scale, int num_kv_heads, int num_seqs,
+                               int num_heads, int head_size, int block_size,
+                               int max_blocks_per_seq, int64_t num_blocks,
+                               int partition_size, void* workspace,
+                               size_t workspace_bytes, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

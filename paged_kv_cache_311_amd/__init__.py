@@ -1,8 +1,10 @@
 """Paged KV-cache decode path for MI355X (gfx950): HIP kernels behind a C ABI.
 
 The three operations -- paged_attention_decode, reshape_and_cache and
-copy_blocks -- run entirely in the HIP kernels of libpagedkv.so (declared
-in include/pagedkv.h).  This module only marshals torch tensors (device
+copy_blocks -- and the fp8 variants of the first two (pools of E4M3 codes
+with one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8)
+run entirely in the HIP kernels of libpagedkv.so (declared in
+include/pagedkv.h).  This module only marshals torch tensors (device
 memory and the current stream) into the C calls and raises on a nonzero
 status.  There is no fallback: if the library is missing or was not built,
 every call raises.
@@ -22,7 +24,7 @@ from . import workloads  # noqa: F401  (seeded input generators)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
 _lib = None
@@ -52,6 +54,13 @@ def _declare(lib):
                                       c_i64, c_int, vp]
     lib.copy_blocks.restype = c_int
     lib.copy_blocks.argtypes = [vp, vp, vp, c_int, c_int, c_int, c_int, c_i64, c_int, vp]
+    lib.paged_attention_decode_fp8.restype = c_int
+    lib.paged_attention_decode_fp8.argtypes = [
+        vp, vp, vp, vp, vp, vp, c_f, c_f, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
+        c_i64, c_int, vp, c_sz, c_int, vp]
+    lib.reshape_and_cache_fp8.restype = c_int
+    lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_f, c_f, c_int, c_int, c_int,
+                                          c_int, c_i64, c_int, vp]
     return lib
 
 
@@ -104,6 +113,12 @@ def _dtype_code(t):
     return codes[t.dtype]
 
 
+def is_fp8_pool(t):
+    """A pool of E4M3 codes: torch.float8_e4m3fn, or uint8 holding the codes."""
+    import torch
+    return t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
 def _stream_of(t):
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -137,21 +152,18 @@ def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per
         partition_size))
 
 
-def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
-                           context_lens, scale, num_kv_heads, partition_size=0,
-                           workspace=None, validate=False):
-    """One decode step of paged attention, written into `out` [S, Hq, D].
-
-    key_cache / value_cache: [num_blocks, num_kv_heads, 16, head_size];
-    block_tables int32 [S, W]; context_lens int32 [S]; query/out [S, Hq, D].
-    `workspace` (uint8 device tensor) is allocated here if needed and None.
-    """
+def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+            num_kv_heads, partition_size, workspace, validate, fp8, k_scale, v_scale):
     import torch
     lib = load_library()
     _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens)
     code = _dtype_code(query)
-    for t in (out, key_cache, value_cache):
-        _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
+    _need(out.dtype == query.dtype, "query and out must share a dtype")
+    for t in (key_cache, value_cache):
+        if fp8:
+            _need(is_fp8_pool(t), "fp8 pools must be float8_e4m3fn or uint8 codes")
+        else:
+            _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
     S, Hq, D = query.shape
@@ -169,11 +181,38 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
         workspace = torch.zeros(need, dtype=torch.uint8, device=query.device)
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.paged_attention_decode(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), float(scale), int(num_kv_heads), S, Hq, D, bs, W, NB,
-        int(partition_size), ws_ptr, ws_len, code, _stream_of(query)))
+    common = (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+              _ptr(context_lens), float(scale))
+    tail = (int(num_kv_heads), S, Hq, D, bs, W, NB, int(partition_size), ws_ptr, ws_len, code,
+            _stream_of(query))
+    if fp8:
+        _check(lib.paged_attention_decode_fp8(*common, float(k_scale), float(v_scale), *tail))
+    else:
+        _check(lib.paged_attention_decode(*common, *tail))
     return out
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
+                           context_lens, scale, num_kv_heads, partition_size=0,
+                           workspace=None, validate=False):
+    """One decode step of paged attention, written into `out` [S, Hq, D].
+
+    key_cache / value_cache: [num_blocks, num_kv_heads, 16, head_size];
+    block_tables int32 [S, W]; context_lens int32 [S]; query/out [S, Hq, D].
+    `workspace` (uint8 device tensor) is allocated here if needed and None.
+    """
+    return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                   num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0)
+
+
+def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,
+                               context_lens, scale, k_scale, v_scale, num_kv_heads,
+                               partition_size=0, workspace=None, validate=False):
+    """paged_attention_decode over pools of E4M3 codes (float8_e4m3fn or
+    uint8 tensors): keys are code values times k_scale, values times
+    v_scale.  query/out float16 or bfloat16."""
+    return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                   num_kv_heads, partition_size, workspace, validate, True, k_scale, v_scale)
 
 
 def reshape_and_cache(key, value, slot_mapping, key_cache, value_cache, validate=False):
@@ -201,12 +240,41 @@ def reshape_and_cache(key, value, slot_mapping, key_cache, value_cache, validate
         T, Hkv, D, bs, NB, code, _stream_of(key)))
 
 
+def reshape_and_cache_fp8(key, value, slot_mapping, key_cache, value_cache, k_scale, v_scale,
+                          validate=False):
+    """Scatter key/value [T, Hkv, D] (float32/16, bfloat16) into E4M3 pools
+    as the codes of key / k_scale and value / v_scale (nearest, ties to
+    even, saturating at +-448)."""
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(key, value, slot_mapping, key_cache, value_cache)
+    code = _dtype_code(key)
+    _need(value.dtype == key.dtype, "keys and values must share a dtype")
+    _need(is_fp8_pool(key_cache) and is_fp8_pool(value_cache),
+          "fp8 pools must be float8_e4m3fn or uint8 codes")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    T, Hkv, D = key.shape
+    NB, Hkv2, bs, D2 = key_cache.shape
+    _need(tuple(value.shape) == (T, Hkv, D) and tuple(slot_mapping.shape) == (T,),
+          "key/value [T, Hkv, D], slot_mapping [T]")
+    _need(Hkv2 == Hkv and D2 == D and tuple(value_cache.shape) == tuple(key_cache.shape),
+          "pool shape does not match the new tokens")
+    if validate:
+        s = slot_mapping.cpu().numpy()
+        live = s[s >= 0]
+        _need(len(np.unique(live)) == len(live), "duplicate slot")
+        _need(not len(live) or live.max() < NB * bs, "slot outside the pool")
+    _check(lib.reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache),
+        float(k_scale), float(v_scale), T, Hkv, D, bs, NB, code, _stream_of(key)))
+
+
 def copy_blocks(key_cache, value_cache, src_dst_pairs, validate=False):
     """Copy whole blocks src -> dst in both pools (src_dst_pairs int64 [N, 2])."""
     import torch
     lib = load_library()
     _all_cuda_contiguous(key_cache, value_cache, src_dst_pairs)
-    code = _dtype_code(key_cache)
+    code = PKV_FP8_E4M3 if is_fp8_pool(key_cache) else _dtype_code(key_cache)
     _need(value_cache.dtype == key_cache.dtype and
           tuple(value_cache.shape) == tuple(key_cache.shape), "pools must match")
     _need(src_dst_pairs.dtype == torch.int64 and src_dst_pairs.dim() == 2 and

@@ -11,7 +11,11 @@
 // empty..." [TEQ], "Paging's second gift: copy-on-write").
 //
 // Both are pure data movement (bit-exact, dtype-agnostic): every thread
-// moves 16-byte chunks with dwordx4 loads and stores.
+// moves 16-byte chunks with dwordx4 loads and stores.  reshape_and_cache_fp8
+// writes into pools of 8-bit float (E4M3) codes: each new element becomes
+// the code of its float32 quotient by the pool's scale ("PagedAttention KV
+// cache memory management" [AITJ], "PagedAttention vs KV-cache quantization
+// vs prefix caching").
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,6 +47,46 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
   const int64_t dst = ((blk * num_kv_heads + g) * kBlockSize + off) * row_bytes + c * 16;
   store16(kcache + dst, load16(key + src));
   store16(vcache + dst, load16(value + src));
+}
+
+// One thread per (token, kv head, 16 elements of the row): 16 input
+// elements (32 or 64 bytes) become one 16-byte chunk of E4M3 codes.
+template <int DT>
+__global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
+    const char* __restrict__ key, const char* __restrict__ value,
+    const int64_t* __restrict__ slot_mapping, char* __restrict__ kcache,
+    char* __restrict__ vcache, float k_scale, float v_scale, int64_t total_chunks,
+    int num_kv_heads, int head_size, int64_t num_slots) {
+  constexpr int kIn = Elt<DT>::kPer16B;  // input elements per 16-B load
+  const int64_t idx = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+  if (idx >= total_chunks) return;
+  const int nch = head_size >> 4;
+  const int c = (int)(idx % nch);
+  const int64_t th = idx / nch;  // token * num_kv_heads + head
+  const int g = (int)(th % num_kv_heads);
+  const int64_t i = th / num_kv_heads;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;  // padding / out of the pool
+  const int64_t blk = slot / kBlockSize;
+  const int off = (int)(slot % kBlockSize);
+  const int64_t src = (th * head_size + c * 16) * Elt<DT>::kBytes;
+  const int64_t dst = ((blk * num_kv_heads + g) * kBlockSize + off) * head_size + c * 16;
+  auto quantize = [&](const char* in, float scale) {
+    u32x4 codes = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int part = 0; part < 16 / kIn; ++part) {
+      const u32x4 x = load16(in + part * 16);
+#pragma unroll
+      for (int e = 0; e < kIn; ++e) {
+        const int k = part * kIn + e;  // element of the 16
+        const uint32_t q = e4m3_code(elem_to_float<DT>(x, e) / scale);
+        codes[k >> 2] |= q << (8 * (k & 3));
+      }
+    }
+    return codes;
+  };
+  store16(kcache + dst, quantize(key + src, k_scale));
+  store16(vcache + dst, quantize(value + src, v_scale));
 }
 
 // grid.x = pair, grid.y = slice of the block; each thread copies kUnroll
@@ -81,7 +125,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
 }
 
 static int elem_bytes(int dtype) {
-  return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2 : 0;
+  return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2
+                                                                        : dtype == PKV_FP8_E4M3 ? 1 : 0;
 }
 
 }  // namespace pkv
@@ -96,7 +141,7 @@ extern "C" int reshape_and_cache(const void* key, const void* value,
   if (!key_cache || !value_cache) return PKV_ERR_INVALID_ARG;
   if (num_tokens > 0 && (!key || !value || !slot_mapping)) return PKV_ERR_INVALID_ARG;
   const int eb = elem_bytes(dtype);
-  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  if (eb == 0 || dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // fp8: the _fp8 call
   if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   if (head_size != 64 && head_size != 128) return PKV_ERR_UNSUPPORTED;
   if (((uintptr_t)key | (uintptr_t)value | (uintptr_t)key_cache | (uintptr_t)value_cache) &
@@ -139,11 +184,57 @@ extern "C" int copy_blocks(void* key_cache, void* value_cache, const int64_t* sr
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+extern "C" int reshape_and_cache_fp8(const void* key, const void* value,
+                                     const int64_t* slot_mapping, void* key_cache,
+                                     void* value_cache, float k_scale, float v_scale,
+                                     int num_tokens, int num_kv_heads, int head_size,
+                                     int block_size, int64_t num_blocks, int dtype,
+                                     void* stream) {
+  using namespace pkv;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (!key_cache || !value_cache) return PKV_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!key || !value || !slot_mapping)) return PKV_ERR_INVALID_ARG;
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
+    return PKV_ERR_INVALID_ARG;  // finite and positive (NaN fails both tests)
+  if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PKV_ERR_UNSUPPORTED;
+  if (((uintptr_t)key | (uintptr_t)value | (uintptr_t)key_cache | (uintptr_t)value_cache) &
+      15u)
+    return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_size / 16);
+  const int64_t grid = (total + kCopyThreads - 1) / kCopyThreads;
+  if (grid > (int64_t)(UINT32_MAX / kCopyThreads)) return PKV_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const dim3 g3((unsigned)grid), b3(kCopyThreads);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t slots = num_blocks * kBlockSize;
+  switch (dtype) {
+    case PKV_F32:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<PKV_F32>, g3, b3, 0, st, (const char*)key,
+                         (const char*)value, slot_mapping, (char*)key_cache, (char*)value_cache,
+                         k_scale, v_scale, total, num_kv_heads, head_size, slots);
+      break;
+    case PKV_F16:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<PKV_F16>, g3, b3, 0, st, (const char*)key,
+                         (const char*)value, slot_mapping, (char*)key_cache, (char*)value_cache,
+                         k_scale, v_scale, total, num_kv_heads, head_size, slots);
+      break;
+    default:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<PKV_BF16>, g3, b3, 0, st, (const char*)key,
+                         (const char*)value, slot_mapping, (char*)key_cache, (char*)value_cache,
+                         k_scale, v_scale, total, num_kv_heads, head_size, slots);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 #ifndef PKV_BUILD_ID
 #define PKV_BUILD_ID "unstamped"
 #endif
 
-extern "C" int pkv_abi_version(void) { return 2; }
+extern "C" int pkv_abi_version(void) { return 3; }
 
 extern "C" const char* pkv_build_id(void) { return PKV_BUILD_ID; }
 

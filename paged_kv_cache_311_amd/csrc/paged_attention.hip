@@ -66,26 +66,36 @@ constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
 constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
 
-template <int DT, int D, int GC>
+// DT: query / output element; KT: pool element (DT itself, or E4M3 codes
+// with 16-bit queries).
+template <int DT, int KT, int D, int GC>
 struct DecodeCfg {
-  static constexpr int kEsz = Elt<DT>::kBytes;
-  static constexpr int kEpc = Elt<DT>::kPer16B;      // elements per 16-B chunk
-  static constexpr int kRowB = D * kEsz;             // bytes per token row
-  static constexpr int kNch = kRowB / 16;            // 16-B chunks per row
+  static constexpr bool kFp8 = KT == PKV_FP8_E4M3;
+  static_assert(KT == DT || (kFp8 && (DT == PKV_F16 || DT == PKV_BF16)), "pool format");
+  static constexpr int kEsz = Elt<KT>::kBytes;       // pool element bytes
+  static constexpr int kEszQ = Elt<DT>::kBytes;      // query / output element bytes
+  static constexpr int kEpc = Elt<KT>::kPer16B;      // pool elements per 16-B chunk
+  static constexpr int kEpcQ = Elt<DT>::kPer16B;     // output elements per 16-B chunk
+  static constexpr int kRowB = D * kEsz;             // pool bytes per token row
+  static constexpr int kRowQ = D * kEszQ;            // query / output bytes per row
+  static constexpr int kNch = kRowB / 16;            // 16-B chunks per pool row
   static constexpr int kTileB = kBlockSize * kRowB;  // bytes per (block, kv head)
   static constexpr int kNld = kTileB / 1024;         // 16-B loads per lane per tile
   static constexpr int kTpl = kWave / kNch;          // tokens per 1-KiB value load
+  // MFMA k-steps per chain: one per key chunk, two for E4M3 chunks (16
+  // codes widen to two 8-element operands); as many q registers
+  static constexpr int kNq = kFp8 ? 2 * kNld : kNld;
   static constexpr int kGcq = GC < 4 ? GC : 4;       // heads per MFMA chain
   static constexpr int kNqg = (GC + 3) / 4;          // MFMA chains per tile
   static_assert(kNch * 16 == kRowB, "row must be a whole number of 16-B chunks");
   static_assert(kNld * 4 == kNch, "key tile: 4 lane groups x kNld chunks per row");
-  static_assert(kNch >= 8 && kNch <= 32, "lane-group reduction assumes 8..32 chunks");
+  static_assert(kNch >= 4 && kNch <= 32, "lane-group reduction assumes 4..32 chunks");
   static_assert(GC == 1 || GC == 2 || GC == 4 || GC == 8, "heads per workgroup");
   // Waves per SIMD the register allocator must leave room for: 3 (168
   // VGPRs) where the kernel fits without spilling (one head per group with
   // 16-bit K/V or 64-wide rows, two heads with 64-wide rows), 2 (256 VGPRs)
   // for up to four heads per group, otherwise whatever it needs.
-  static constexpr bool kNarrow = kEsz == 2 || D == 64;
+  static constexpr bool kNarrow = kEsz <= 2 || D == 64;
   static constexpr int kMinWaves =
       kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1);
 };
@@ -97,7 +107,8 @@ struct DecodeParams {
   const char* vcache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float scale_log2;
+  float scale_log2;    // softmax scale (times the key scale of an E4M3 pool) x log2 e
+  float v_scale;       // value scale of an E4M3 pool (1 otherwise)
   int num_seqs, num_heads, num_kv_heads, max_blocks;
   int64_t num_blocks;
   int tile_cap;        // max tiles per range (0: no cap)
@@ -218,12 +229,43 @@ __device__ RangeMap plan_ranges(int T, int nwaves, int cap) {
   return m;
 }
 
-template <int DT, int NLD>
-__device__ __forceinline__ floatx4 qk_mfma(const u32x4 (&q)[NLD], const Tile& t) {
+// Eight E4M3 codes (two words) widened exactly to one 16-bit MFMA operand.
+template <int DT>
+__device__ __forceinline__ u32x4 widen_e4m3x8(int w0, int w1) {
+  typedef float float2_ __attribute__((ext_vector_type(2)));
+  const float2_ f[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(w0, false),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(w0, true),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(w1, false),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(w1, true)};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == PKV_F16) {
+      r[i] = float_to_bits<PKV_F16>(f[i].x) | (float_to_bits<PKV_F16>(f[i].y) << 16);
+    } else {  // the codes' values have 4 significant bits: the upper half is exact
+      r[i] = (bits_of(f[i].x) >> 16) | (bits_of(f[i].y) & 0xffff0000u);
+    }
+  }
+  return r;
+}
+
+template <int DT, int KT, int NQ>
+__device__ __forceinline__ floatx4 qk_mfma(const u32x4 (&q)[NQ], const Tile& t) {
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < NLD; ++m) {
-    if constexpr (DT == PKV_F16) {
+  for (int m = 0; m < NQ; ++m) {
+    if constexpr (KT == PKV_FP8_E4M3) {
+      // k-step m takes half m % 2 of key chunk m / 2 (the query is read in
+      // the same order, so the dot products are unchanged)
+      const u32x4 kc = t.k[m / 2];
+      const u32x4 kb = widen_e4m3x8<DT>((int)kc[2 * (m % 2)], (int)kc[2 * (m % 2) + 1]);
+      if constexpr (DT == PKV_F16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, q[m]),
+                                                     __builtin_bit_cast(half8, kb), acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, q[m]), __builtin_bit_cast(bf16x8, kb), acc, 0, 0, 0);
+    } else if constexpr (DT == PKV_F16) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           __builtin_bit_cast(half8, q[m]), __builtin_bit_cast(half8, t.k[m]), acc, 0, 0, 0);
     } else if constexpr (DT == PKV_BF16) {
@@ -505,10 +547,10 @@ __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const
   return wd;
 }
 
-template <int DT, int D, int GC>
-__global__ __launch_bounds__(kThreads, (DecodeCfg<DT, D, GC>::kMinWaves)) void
+template <int DT, int KT, int D, int GC>
+__global__ __launch_bounds__(kThreads, (DecodeCfg<DT, KT, D, GC>::kMinWaves)) void
 paged_decode_kernel(const DecodeParams p) {
-  using C = DecodeCfg<DT, D, GC>;
+  using C = DecodeCfg<DT, KT, D, GC>;
   constexpr int NLD = C::kNld;
   constexpr int EPC = C::kEpc;
 
@@ -562,14 +604,18 @@ paged_decode_kernel(const DecodeParams p) {
   const int64_t block_stride = (int64_t)p.num_kv_heads * C::kTileB;
 
   // query rows as MFMA A operands: row r of chain c is head c*4 + r % kGcq
-  using QRegs = u32x4[C::kNqg][NLD];
+  using QRegs = u32x4[C::kNqg][C::kNq];
   auto load_q = [&](QRegs& q, int s, int hg) {
 #pragma unroll
     for (int c = 0; c < C::kNqg; ++c) {
       const int head = hg * GC + c * 4 + (row % C::kGcq);
-      const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowB;
+      const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowQ;
+      // k-step m reads the query elements of key chunk jg + 4m (E4M3: half
+      // m % 2 of chunk jg + 4 (m / 2), 16 codes per chunk)
 #pragma unroll
-      for (int m = 0; m < NLD; ++m) q[c][m] = load16(qrow + (jg + 4 * m) * 16);
+      for (int m = 0; m < C::kNq; ++m)
+        q[c][m] = load16(qrow + (C::kFp8 ? (jg + 4 * (m / 2)) * 32 + (m % 2) * 16
+                                         : (jg + 4 * m) * 16));
     }
   };
   auto load_tile = [&](Tile& t, int id, int hg) {
@@ -641,7 +687,7 @@ paged_decode_kernel(const DecodeParams p) {
       float sc[GC];
 #pragma unroll
       for (int c = 0; c < C::kNqg; ++c) {
-        const floatx4 rr = qk_mfma<DT, NLD>(qa[c], tc);
+        const floatx4 rr = qk_mfma<DT, KT, C::kNq>(qa[c], tc);
 #pragma unroll
         for (int j = 0; j < C::kGcq; ++j) sc[c * 4 + j] = rr[j] * p.scale_log2;
       }
@@ -678,7 +724,7 @@ paged_decode_kernel(const DecodeParams p) {
         if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          const float f = elem_to_float<DT>(vv, e);
+          const float f = elem_to_float<KT>(vv, e);
 #pragma unroll
           for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], f, acc[g][e]);
         }
@@ -698,25 +744,27 @@ paged_decode_kernel(const DecodeParams p) {
         if (lane < C::kNch) {
 #pragma unroll
           for (int g = 0; g < GC; ++g) {
-            const float inv = 1.f / l_run[g];
+            const float inv = (C::kFp8 ? p.v_scale : 1.f) / l_run[g];
             float o[EPC];
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o[e] = acc[g][e] * inv;
             char* dst = (char*)p.out +
-                        (((int64_t)s * p.num_heads + h0 + g) * D + lane * EPC) * C::kEsz;
-            store_chunk<DT>(dst, o);
+                        (((int64_t)s * p.num_heads + h0 + g) * D + lane * EPC) * C::kEszQ;
+#pragma unroll
+            for (int e = 0; e < EPC; e += C::kEpcQ) store_chunk<DT>(dst + e * C::kEszQ, o + e);
           }
         }
       } else {  // a piece of a split segment: float32 partials
         const int64_t slot = pc_slot;
+        const float vs = C::kFp8 ? p.v_scale : 1.f;  // partials hold the values' scale
         if (lane < C::kNch) {
 #pragma unroll
           for (int g = 0; g < GC; ++g) {
             float* dst = p.part_acc + (slot * GC + g) * D + lane * EPC;
 #pragma unroll
             for (int e = 0; e < EPC; e += 4)
-              store16(dst + e, u32x4{bits_of(acc[g][e]), bits_of(acc[g][e + 1]),
-                                     bits_of(acc[g][e + 2]), bits_of(acc[g][e + 3])});
+              store16(dst + e, u32x4{bits_of(acc[g][e] * vs), bits_of(acc[g][e + 1] * vs),
+                                     bits_of(acc[g][e + 2] * vs), bits_of(acc[g][e + 3] * vs)});
           }
         }
         if (lane == 0) {
@@ -823,30 +871,31 @@ static int resident_workgroups(const void* kernel) {
   return n;
 }
 
-template <int DT, int D, int GC>
+template <int DT, int KT, int D, int GC>
 static hipError_t launch_decode(const DecodeParams& a, hipStream_t st) {
-  const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, D, GC>);
+  const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC>);
   const int nwg = resident_workgroups(k);
   if (nwg <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((paged_decode_kernel<DT, D, GC>), dim3(nwg), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((paged_decode_kernel<DT, KT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
+                     a);
   hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
                      a);
   return hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int KT, int D>
 static hipError_t dispatch_gc(const DecodeParams& a, int gc, hipStream_t st) {
   switch (gc) {
-    case 1: return launch_decode<DT, D, 1>(a, st);
-    case 2: return launch_decode<DT, D, 2>(a, st);
-    case 4: return launch_decode<DT, D, 4>(a, st);
-    default: return launch_decode<DT, D, 8>(a, st);
+    case 1: return launch_decode<DT, KT, D, 1>(a, st);
+    case 2: return launch_decode<DT, KT, D, 2>(a, st);
+    case 4: return launch_decode<DT, KT, D, 4>(a, st);
+    default: return launch_decode<DT, KT, D, 8>(a, st);
   }
 }
 
-template <int DT>
+template <int DT, int KT>
 static hipError_t dispatch_d(const DecodeParams& a, int d, int gc, hipStream_t st) {
-  return d == 64 ? dispatch_gc<DT, 64>(a, gc, st) : dispatch_gc<DT, 128>(a, gc, st);
+  return d == 64 ? dispatch_gc<DT, KT, 64>(a, gc, st) : dispatch_gc<DT, KT, 128>(a, gc, st);
 }
 
 static int heads_per_wg(int num_heads, int num_kv_heads) {
@@ -903,14 +952,18 @@ extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
   return workspace_layout(r, gc, head_size).total;
 }
 
-extern "C" int paged_attention_decode(void* out, const void* query, const void* key_cache,
-                                      const void* value_cache, const int32_t* block_tables,
-                                      const int32_t* context_lens, float scale,
-                                      int num_kv_heads, int num_seqs, int num_heads,
-                                      int head_size, int block_size, int max_blocks_per_seq,
-                                      int64_t num_blocks, int partition_size, void* workspace,
-                                      size_t workspace_bytes, int dtype, void* stream) {
-  using namespace pkv;
+namespace pkv {
+
+// Both decode entry points: validation, workspace layout and one launch
+// (decode + merge) per kLdsSeqs sequences.  kv_dtype is dtype itself or
+// PKV_FP8_E4M3 (with 16-bit queries).
+static int decode_impl(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, float scale, float k_scale, float v_scale,
+                       int num_kv_heads, int num_seqs, int num_heads, int head_size,
+                       int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                       int partition_size, void* workspace, size_t workspace_bytes, int dtype,
+                       int kv_dtype, void* stream) {
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -918,6 +971,10 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
     return PKV_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype != dtype && !(kv_dtype == PKV_FP8_E4M3 && dtype != PKV_F32))
+    return PKV_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale > 3.0e38f || v_scale > 3.0e38f)
+    return PKV_ERR_INVALID_ARG;  // finite and positive (NaN fails both tests)
   if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   if (head_size != 64 && head_size != 128) return PKV_ERR_UNSUPPORTED;
   if (!partition_ok(partition_size)) return PKV_ERR_INVALID_ARG;
@@ -944,7 +1001,9 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   a.vcache = (const char*)value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.scale_log2 = scale * 1.4426950408889634f;  // exp(x) = 2^(x log2 e)
+  // exp(x) = 2^(x log2 e); an E4M3 pool's key scale multiplies every logit
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -974,12 +1033,48 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
     b.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
     b.context_lens = context_lens + s0;
     hipError_t e;
-    switch (dtype) {
-      case PKV_F32: e = dispatch_d<PKV_F32>(b, head_size, gc, st); break;
-      case PKV_F16: e = dispatch_d<PKV_F16>(b, head_size, gc, st); break;
-      default: e = dispatch_d<PKV_BF16>(b, head_size, gc, st); break;
+    if (kv_dtype == PKV_FP8_E4M3) {
+      e = dtype == PKV_F16 ? dispatch_d<PKV_F16, PKV_FP8_E4M3>(b, head_size, gc, st)
+                           : dispatch_d<PKV_BF16, PKV_FP8_E4M3>(b, head_size, gc, st);
+    } else {
+      switch (dtype) {
+        case PKV_F32: e = dispatch_d<PKV_F32, PKV_F32>(b, head_size, gc, st); break;
+        case PKV_F16: e = dispatch_d<PKV_F16, PKV_F16>(b, head_size, gc, st); break;
+        default: e = dispatch_d<PKV_BF16, PKV_BF16>(b, head_size, gc, st); break;
+      }
     }
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, float scale,
+                                      int num_kv_heads, int num_seqs, int num_heads,
+                                      int head_size, int block_size, int max_blocks_per_seq,
+                                      int64_t num_blocks, int partition_size, void* workspace,
+                                      size_t workspace_bytes, int dtype, void* stream) {
+  return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                          1.f, 1.f, num_kv_heads, num_seqs, num_heads, head_size, block_size,
+                          max_blocks_per_seq, num_blocks, partition_size, workspace,
+                          workspace_bytes, dtype, dtype, stream);
+}
+
+extern "C" int paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale,
+                                          float k_scale, float v_scale, int num_kv_heads,
+                                          int num_seqs, int num_heads, int head_size,
+                                          int block_size, int max_blocks_per_seq,
+                                          int64_t num_blocks, int partition_size,
+                                          void* workspace, size_t workspace_bytes, int dtype,
+                                          void* stream) {
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                          k_scale, v_scale, num_kv_heads, num_seqs, num_heads, head_size,
+                          block_size, max_blocks_per_seq, num_blocks, partition_size, workspace,
+                          workspace_bytes, dtype, PKV_FP8_E4M3, stream);
 }

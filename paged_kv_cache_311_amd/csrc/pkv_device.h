@@ -31,6 +31,10 @@ template <> struct Elt<PKV_BF16> {
   static constexpr int kBytes = 2;
   static constexpr int kPer16B = 8;
 };
+template <> struct Elt<PKV_FP8_E4M3> {
+  static constexpr int kBytes = 1;
+  static constexpr int kPer16B = 16;
+};
 
 // Bit casts through by-value scalars.  clang's __builtin_bit_cast applied
 // directly to an element of an ext_vector_type lvalue (v[i]) reads the
@@ -59,6 +63,46 @@ __device__ __forceinline__ float elem_to_float<PKV_BF16>(const u32x4& v, int e) 
   // a bfloat16 is the upper half of a binary32: placing it there is exact
   uint32_t f = (e & 1) ? (w & 0xffff0000u) : (w << 16);
   return __builtin_bit_cast(float, f);
+}
+// E4M3 codes widen exactly with the hardware conversion (OCP format on
+// gfx950: bias 7, S.1111.111 = NaN); the byte index must be a constant.
+template <>
+__device__ __forceinline__ float elem_to_float<PKV_FP8_E4M3>(const u32x4& v, int e) {
+  const int w = (int)v[e >> 2];
+  switch (e & 3) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  }
+}
+
+// E4M3 code of a float: nearest code, ties to the even mantissa; |x| >=
+// 448 (inf included) saturates to +-448; NaN gives 0x7F.  Written from the
+// format: below 2^-6 the codes are the multiples of 2^-9 (8 reaching the
+// smallest normal), above it (1 + f/8) 2^(E) with E + 7 in the exponent
+// field.  frexp and the scalings are exact, rint rounds to nearest even.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  if (x != x) return 0x7Fu;
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    int e;
+    const float m = frexpf(a, &e);  // a = m 2^e, m in [0.5, 1)
+    float f8 = rintf((2.f * m - 1.f) * 8.f);
+    int E = e - 1;
+    if (f8 == 8.f) {
+      f8 = 0.f;
+      ++E;
+    }
+    code = (uint32_t)((E + 7) * 8 + (int)f8);
+  }
+  return code | sign;
 }
 
 // Round float to the storage type (nearest-even) and return its bits.
@@ -99,6 +143,7 @@ constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i in each 8-lane half
 constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i in each row
 constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16
+constexpr int kDppRowRor4 = 0x124;       // lane i <- lane (i+4) mod 16
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -124,9 +169,10 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 
 // Sum of x over the lanes whose index differs from this lane's only in
-// bits >= log2(STRIDE) (STRIDE in {8,16,32}): lanes that share lane % STRIDE.
+// bits >= log2(STRIDE) (STRIDE in {4,8,16,32}): lanes that share lane % STRIDE.
 template <int STRIDE>
 __device__ __forceinline__ float sum_over_lane_groups(float x) {
+  if constexpr (STRIDE <= 4) x += dpp_f<kDppRowRor4>(x);
   if constexpr (STRIDE <= 8) x += dpp_f<kDppRowRor8>(x);
   if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16, kWave);
   x += __shfl_xor(x, 32, kWave);

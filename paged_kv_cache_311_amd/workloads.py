@@ -24,6 +24,15 @@ sampling over a shared prompt, long contexts):
   long_gqa       32 query heads over 8 kv heads of 128, bf16, 16 seqs of
                  32,768 tokens, pool 1.25x the need; contexts are split
                  into pieces merged through float32 (max, sum) states.
+  opt13b_fp8,    the same shapes and lengths with pools of OCP E4M3 codes
+  long_gqa_fp8   and one scale per pool (keys 1/64, values 3/128); queries,
+                 outputs and new tokens stay fp16 / bf16.
+
+An E4M3 pool is drawn as codes: N(0,1) values divided by the pool's scale,
+clamped to the format's range and converted by torch's float8_e4m3fn cast
+(a library conversion used only to draw codes with that spread; both the
+oracle and the GPU path read the codes as given).  Its free slots hold the
+NaN code 0x7F.
 
 Every slot that holds no token -- unused blocks and the tail of each
 sequence's last block -- is filled with NaN, so any stray read shows up in
@@ -38,12 +47,16 @@ from dataclasses import dataclass
 import numpy as np
 
 BLOCK_SIZE = 16
+FP8_K_SCALE = 1.0 / 64     # N(0,1) / scale stays below the E4M3 maximum 448
+FP8_V_SCALE = 3.0 / 128
+E4M3_NAN = 0x7F
 
 
 @dataclass(frozen=True)
 class Workload:
     key: str
-    index: int              # 1-based position in the workload list
+    index: int              # seeds the workload; an fp8 variant shares its base's,
+                            # so lengths, placement and values match
     num_seqs: int
     num_heads: int
     num_kv_heads: int
@@ -56,6 +69,17 @@ class Workload:
     partition_size: int = 0   # cap on tokens per piece of a split context (0: none)
     prompts: int = 0
     samples: int = 0
+    kv_dtype: str = ""      # "" (pools in `dtype`) | "e4m3" (pools of E4M3 codes)
+    k_scale: float = 1.0    # per-pool scales of an E4M3 pool
+    v_scale: float = 1.0
+
+    @property
+    def fp8(self):
+        return self.kv_dtype == "e4m3"
+
+    @property
+    def kv_elem_bytes(self):
+        return 1 if self.fp8 else (4 if self.dtype == "f32" else 2)
 
     @property
     def table_width(self):
@@ -89,6 +113,12 @@ WORKLOADS = {
                  prompts=32, samples=8),
         Workload("long_gqa", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
                  ("factor", 1.25), "decode", 32768),
+        Workload("opt13b_fp8", 2, 64, 40, 40, 128, "f16", ("uniform", 1, 2048),
+                 ("factor", 1.25), "decode", 2048, kv_dtype="e4m3",
+                 k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE),
+        Workload("long_gqa_fp8", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
+                 ("factor", 1.25), "decode", 32768, kv_dtype="e4m3",
+                 k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE),
     )
 }
 
@@ -315,14 +345,24 @@ def make_batch(w, seed=None, device="cpu", chunk_blocks=2048):
     live = md["live_slots"]
     used = np.flatnonzero(live.any(axis=1))
     caches = []
-    for _ in range(2):
-        cache = torch.full((nb, Hkv, BLOCK_SIZE, D), float("nan"), dtype=td,
-                           device=device)
+    for pool_scale in (w.k_scale, w.v_scale):
+        shape = (nb, Hkv, BLOCK_SIZE, D)
+        if w.fp8:
+            cache = torch.full(shape, E4M3_NAN, dtype=torch.uint8, device=device)
+        else:
+            cache = torch.full(shape, float("nan"), dtype=td, device=device)
         for c0 in range(0, len(used), chunk_blocks):
             ids = used[c0:c0 + chunk_blocks]
-            vals = _randn((len(ids), Hkv, BLOCK_SIZE, D), gen, device, w.dtype)
-            dead = torch.from_numpy(~live[ids]).to(device)
-            vals.masked_fill_(dead[:, None, :, None], float("nan"))
+            dead = torch.from_numpy(~live[ids]).to(device)[:, None, :, None]
+            if w.fp8:
+                vals = torch.randn((len(ids), Hkv, BLOCK_SIZE, D), generator=gen,
+                                   device=device, dtype=torch.float32)
+                vals = (vals / pool_scale).clamp_(-448.0, 448.0)
+                vals = vals.to(torch.float8_e4m3fn).view(torch.uint8)
+                vals.masked_fill_(dead, E4M3_NAN)
+            else:
+                vals = _randn((len(ids), Hkv, BLOCK_SIZE, D), gen, device, w.dtype)
+                vals.masked_fill_(dead, float("nan"))
             cache[torch.from_numpy(ids).to(device)] = vals
         caches.append(cache)
     batch = dict(md)
@@ -353,10 +393,11 @@ def kv_token_count(md):
 
 
 def custom(lens, num_heads, num_kv_heads, head_size, dtype, max_len=None,
-           pool_factor=1.25, partition_size=512):
+           pool_factor=1.25, partition_size=512, kv_dtype="", k_scale=1.0, v_scale=1.0):
     """A decode workload with explicit context lengths (edge-case tests)."""
     lens = tuple(int(x) for x in lens)
     max_len = max(max(lens), 1) if max_len is None else max_len
     return Workload("custom", 0, len(lens), num_heads, num_kv_heads, head_size,
                     dtype, ("list", lens), ("factor", pool_factor), "decode",
-                    max_len, partition_size)
+                    max_len, partition_size, kv_dtype=kv_dtype, k_scale=k_scale,
+                    v_scale=v_scale)

@@ -37,9 +37,13 @@ def run_decode(b, partition_size=None, out=None):
     w = b["workload"]
     ps = w.partition_size if partition_size is None else partition_size
     out = torch.empty_like(b["query"]) if out is None else out
-    pkv.paged_attention_decode(out, b["query"], b["key_cache"], b["value_cache"],
-                               dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
-                               float(w.scale), w.num_kv_heads, partition_size=ps)
+    args = (out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
+            dev_i32(b["context_lens"]), float(w.scale))
+    if w.fp8:
+        pkv.paged_attention_decode_fp8(*args, w.k_scale, w.v_scale, w.num_kv_heads,
+                                       partition_size=ps)
+    else:
+        pkv.paged_attention_decode(*args, w.num_kv_heads, partition_size=ps)
     torch.cuda.synchronize()
     return out
 
@@ -50,8 +54,13 @@ def run_pool_updates(b):
         pkv.copy_blocks(b["key_cache"], b["value_cache"], dev_i64(b["cow_pairs"]),
                         validate=True)
     if "slot_mapping" in b:
-        pkv.reshape_and_cache(b["key"], b["value"], dev_i64(b["slot_mapping"]),
-                              b["key_cache"], b["value_cache"], validate=True)
+        w = b["workload"]
+        args = (b["key"], b["value"], dev_i64(b["slot_mapping"]), b["key_cache"],
+                b["value_cache"])
+        if w.fp8:
+            pkv.reshape_and_cache_fp8(*args, w.k_scale, w.v_scale, validate=True)
+        else:
+            pkv.reshape_and_cache(*args, validate=True)
     torch.cuda.synchronize()
 
 
@@ -94,7 +103,12 @@ def oracle_pool(b, kc_before, vc_before, ids):
                              np.int64)
             key = wl.to_host(b["key"])[keep]
             val = wl.to_host(b["value"])[keep]
-            kc, vc = oracle.reshape_and_cache(key, val, sub, kc, vc)
+            w = b["workload"]
+            if w.fp8:
+                kc, vc = oracle.reshape_and_cache_fp8(key, val, sub, kc, vc, w.k_scale,
+                                                      w.v_scale, w.dtype)
+            else:
+                kc, vc = oracle.reshape_and_cache(key, val, sub, kc, vc)
     return kc, vc, remap
 
 
@@ -112,6 +126,10 @@ def oracle_decode_subset(b, kc_before, vc_before, seqs):
         n = -(-int(lens[i]) // BS)
         tables[i, :n] = [remap[int(x)] for x in bt[s, :n]]
     q = wl.to_host(b["query"])[seqs]
+    if w.fp8:
+        return oracle.decode_attention(q, kc, vc, tables, lens, w.scale, w.num_kv_heads,
+                                       w.dtype, kv_dtype="e4m3", k_scale=w.k_scale,
+                                       v_scale=w.v_scale)
     return oracle.decode_attention(q, kc, vc, tables, lens, w.scale, w.num_kv_heads,
                                    w.dtype)
 
@@ -151,6 +169,50 @@ def assert_close(out_rows, ref, dtype, what=""):
 
 def bits(t):
     t = t.contiguous()
+    if t.element_size() == 1:
+        return t.view(torch.uint8)
     if t.element_size() == 2:
         return t.view(torch.int16)
     return t.view(torch.int32)
+
+
+def clone_pools(b):
+    return b["key_cache"].clone(), b["value_cache"].clone()
+
+
+def full_step_and_check(b, seqs=None, check_pool=True):
+    """Run pool updates + decode on the GPU; compare with the oracle."""
+    w = b["workload"]
+    kc0, vc0 = clone_pools(b)
+    run_pool_updates(b)
+    if check_pool and ("slot_mapping" in b or "cow_pairs" in b):
+        touched = set()
+        if "cow_pairs" in b:
+            touched.update(int(d) for d in b["cow_pairs"][:, 1])
+            touched.update(int(s) for s in b["cow_pairs"][:, 0])
+        if "slot_mapping" in b:
+            touched.update(int(s) // wl.BLOCK_SIZE for s in b["slot_mapping"] if s >= 0)
+        ids = np.asarray(sorted(touched), np.int64)
+        ek, ev, _ = oracle_pool(b, kc0, vc0, ids)
+        gk = gather_blocks(b["key_cache"], ids)
+        gv = gather_blocks(b["value_cache"], ids)
+        assert gk.tobytes() == ek.tobytes() and gv.tobytes() == ev.tobytes()
+        rest = torch.ones(b["key_cache"].shape[0], dtype=torch.bool, device=DEV)
+        rest[torch.from_numpy(ids).to(DEV)] = False
+        assert torch.equal(bits(b["key_cache"][rest]), bits(kc0[rest]))
+        assert torch.equal(bits(b["value_cache"][rest]), bits(vc0[rest]))
+        say(f"    pool updates bit-exact on {len(ids)} touched blocks, rest unchanged")
+    out = run_decode(b)
+    S = w.num_seqs
+    seqs = list(range(S)) if seqs is None else seqs
+    ref = oracle_decode_subset(b, kc0, vc0, seqs)
+    assert_close(out[seqs], ref, w.dtype, f"{w.key} seqs={len(seqs)}")
+    assert torch.isfinite(out.float()).all()
+    return out
+
+
+def sample_seqs(lens, k=3, seed=7):
+    rng = np.random.default_rng(seed)
+    pick = {int(np.argmin(lens)), int(np.argmax(lens))}
+    pick.update(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
+    return sorted(pick)

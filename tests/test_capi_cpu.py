@@ -36,6 +36,7 @@ def declared_functions(header=HEADER):
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("paged_attention_decode", "reshape_and_cache", "copy_blocks",
+              "paged_attention_decode_fp8", "reshape_and_cache_fp8",
               "paged_attention_workspace_bytes", "pkv_status_string", "pkv_abi_version"):
         assert n in names
 
@@ -65,7 +66,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -157,6 +158,49 @@ def test_cache_ops_argument_validation(lib):
     assert c(FAKE, FAKE, FAKE, 3, 2, 64, 16, 0, 1, 0) == INVALID
     assert c(FAKE, FAKE, FAKE, 3, 2, 256, 16, 8, 1, 0) == UNSUPPORTED
     assert c(FAKE, FAKE, FAKE, 0, 2, 128, 16, 8, 2, 0) == OK
+    assert c(FAKE, FAKE, FAKE, 0, 2, 128, 16, 8, 3, 0) == OK       # E4M3 pools copy too
+    assert c(FAKE, FAKE, FAKE, 1, 2, 128, 16, 8, 4, 0) == UNSUPPORTED
+    # the unscaled call does not write E4M3 pools
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 3, 0) == UNSUPPORTED
+
+
+def decode_fp8(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, ks=0.5,
+             vs=2.0, hkv=4, S=2, Hq=8, D=128, bs=16, W=4, NB=64, ps=0, ws=0, wsb=0,
+             dtype=1, stream=0)
+    a.update(kw)
+    return lib.paged_attention_decode_fp8(
+        a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["ks"], a["vs"],
+        a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ps"], a["ws"],
+        a["wsb"], a["dtype"], a["stream"])
+
+
+def test_fp8_argument_validation(lib):
+    nan, inf = float("nan"), float("inf")
+    assert decode_fp8(lib) == WORKSPACE                   # valid up to the workspace
+    assert decode_fp8(lib, S=0) == OK
+    assert decode_fp8(lib, dtype=0) == UNSUPPORTED        # queries are 16-bit
+    assert decode_fp8(lib, dtype=3) == UNSUPPORTED
+    assert decode_fp8(lib, dtype=2) == WORKSPACE          # bfloat16 queries
+    for bad in (0.0, -1.0, nan, inf):
+        assert decode_fp8(lib, ks=bad) == INVALID
+        assert decode_fp8(lib, vs=bad) == INVALID
+    assert decode_fp8(lib, D=96) == UNSUPPORTED
+    assert decode_fp8(lib, kc=FAKE + 8) == INVALID
+    r = lib.reshape_and_cache_fp8
+    args = lambda ks=0.5, vs=2.0, T=4, D=128, bs=16, dtype=1, kc=FAKE: r(
+        FAKE, FAKE, FAKE, kc, FAKE, ks, vs, T, 2, D, bs, 8, dtype, 0)
+    assert args(T=0) == OK
+    for dt in (0, 1, 2):
+        assert args(T=0, dtype=dt) == OK                  # float32/16 and bfloat16 inputs
+    assert args(dtype=3) == UNSUPPORTED
+    for bad in (0.0, -2.0, nan, inf):
+        assert args(ks=bad) == INVALID
+        assert args(vs=bad) == INVALID
+    assert args(D=96) == UNSUPPORTED
+    assert args(bs=8) == UNSUPPORTED
+    assert args(kc=FAKE + 4) == INVALID
+    assert args(T=-1) == INVALID
 
 
 def test_library_build_id_matches_sources(lib):

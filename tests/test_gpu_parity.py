@@ -14,9 +14,9 @@ import torch
 
 import paged_kv_cache_311_amd as pkv
 from paged_kv_cache_311_amd import workloads as wl
-from tests.gpu_helpers import (DEV, TOL, assert_close, bits, blocks_read_by,
-                               dev_i32, gather_blocks, oracle_decode_subset,
-                               oracle_pool, run_decode, run_pool_updates, say)
+from tests.gpu_helpers import (DEV, TOL, assert_close, bits, blocks_read_by, clone_pools,
+                               dev_i32, full_step_and_check, gather_blocks,
+                               oracle_decode_subset, oracle_pool, run_decode, sample_seqs)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,41 +31,6 @@ REDUCED = {
 }
 
 
-def clone_pools(b):
-    return b["key_cache"].clone(), b["value_cache"].clone()
-
-
-def full_step_and_check(b, seqs=None, check_pool=True):
-    """Run pool updates + decode on the GPU; compare with the oracle."""
-    w = b["workload"]
-    kc0, vc0 = clone_pools(b)
-    run_pool_updates(b)
-    if check_pool and ("slot_mapping" in b or "cow_pairs" in b):
-        touched = set()
-        if "cow_pairs" in b:
-            touched.update(int(d) for d in b["cow_pairs"][:, 1])
-            touched.update(int(s) for s in b["cow_pairs"][:, 0])
-        if "slot_mapping" in b:
-            touched.update(int(s) // wl.BLOCK_SIZE for s in b["slot_mapping"] if s >= 0)
-        ids = np.asarray(sorted(touched), np.int64)
-        ek, ev, _ = oracle_pool(b, kc0, vc0, ids)
-        gk = gather_blocks(b["key_cache"], ids)
-        gv = gather_blocks(b["value_cache"], ids)
-        assert gk.tobytes() == ek.tobytes() and gv.tobytes() == ev.tobytes()
-        rest = torch.ones(b["key_cache"].shape[0], dtype=torch.bool, device=DEV)
-        rest[torch.from_numpy(ids).to(DEV)] = False
-        assert torch.equal(bits(b["key_cache"][rest]), bits(kc0[rest]))
-        assert torch.equal(bits(b["value_cache"][rest]), bits(vc0[rest]))
-        say(f"    pool updates bit-exact on {len(ids)} touched blocks, rest unchanged")
-    out = run_decode(b)
-    S = w.num_seqs
-    seqs = list(range(S)) if seqs is None else seqs
-    ref = oracle_decode_subset(b, kc0, vc0, seqs)
-    assert_close(out[seqs], ref, w.dtype, f"{w.key} seqs={len(seqs)}")
-    assert torch.isfinite(out.float()).all()
-    return out
-
-
 @pytest.mark.parametrize("seed", W["tiny"].seeds())
 def test_tiny_every_output(gpu_lib, seed):
     b = wl.make_batch(W["tiny"], seed, DEV)
@@ -78,13 +43,6 @@ def test_reduced_workload_every_output(gpu_lib, key, si):
     w = dataclasses.replace(W[key], **REDUCED[key])
     b = wl.make_batch(w, w.seeds()[si], DEV)
     full_step_and_check(b)
-
-
-def sample_seqs(lens, k=3, seed=7):
-    rng = np.random.default_rng(seed)
-    pick = {int(np.argmin(lens)), int(np.argmax(lens))}
-    pick.update(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
-    return sorted(pick)
 
 
 @pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa"])

@@ -118,3 +118,32 @@ def test_bf16_to_host_bits():
     h = wl.to_host(t)
     assert h.dtype == np.uint16
     assert h.tolist() == [0x3F80, 0xC000, 0x7F80]
+
+
+@pytest.mark.parametrize("base", ["opt13b", "long_gqa"])
+def test_fp8_variant_shares_metadata(base):
+    """An E4M3 workload draws the same lengths and placement as its base."""
+    w, w8 = wl.WORKLOADS[base], wl.WORKLOADS[base + "_fp8"]
+    assert w8.fp8 and not w.fp8 and w8.kv_elem_bytes == 1 and w.kv_elem_bytes == 2
+    a, b = wl.draw_metadata(w, w.default_seed), wl.draw_metadata(w8, w8.default_seed)
+    assert (a["context_lens"] == b["context_lens"]).all()
+    assert (a["block_tables"] == b["block_tables"]).all()
+
+
+def test_fp8_pool_codes():
+    """E4M3 pools hold codes: the NaN code in free slots, finite codes with
+    the pool's scale in live ones."""
+    w = wl.custom([5, 33, 16], 4, 2, 64, "f16", kv_dtype="e4m3", k_scale=1 / 64,
+                  v_scale=3 / 128)
+    b = wl.make_batch(w, 3)
+    live = b["live_slots"]
+    for cache, scale in ((b["key_cache"], w.k_scale), (b["value_cache"], w.v_scale)):
+        assert cache.dtype == torch.uint8
+        codes = cache.numpy()
+        dead = ~live[:, None, :, None].repeat(w.num_kv_heads, 1).repeat(w.head_size, 3)
+        assert (codes[dead] == wl.E4M3_NAN).all()
+        vals = oracle.e4m3_decode(codes[~dead])
+        assert np.isfinite(vals).all()
+        # N(0,1) in the pool's units: the spread comes back after scaling
+        assert 0.8 < np.std(vals * scale) < 1.2
+    assert b["query"].dtype == torch.float16
