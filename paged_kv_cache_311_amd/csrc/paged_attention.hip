@@ -62,9 +62,13 @@ constexpr int kThreads = kWavesPerWG * kWave;
 constexpr int kMaxWGs = 1024;                   // at most 4 waves per SIMD
 constexpr int kMaxWaves = kMaxWGs * kWavesPerWG;
 constexpr int kWavesPerSimd = 2;                // resident waves the grid is sized for
+constexpr int kWavesPerSimdFp8 = 3;             // ... with E4M3 pools
 constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
 constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitAllLoads = 0x0F70;
 
 // DT: query / output element; KT: pool element (DT itself, or E4M3 codes
 // with 16-bit queries).
@@ -98,6 +102,14 @@ struct DecodeCfg {
   static constexpr bool kNarrow = kEsz <= 2 || D == 64;
   static constexpr int kMinWaves =
       kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1);
+  static constexpr int kGridWaves = kFp8 ? kWavesPerSimdFp8 : kWavesPerSimd;
+  // E4M3 tiles: the next tile's loads stay in flight while the current
+  // tile is computed.  16-bit tiles: the wave waits for them as well before
+  // computing; their stream is at the HBM ceiling already and more loads
+  // in flight only add contention (measured on one MI355X: overlapping is
+  // 15% faster on the 32K-token grouped workload with E4M3 pools, 3.7%
+  // slower with bfloat16 pools).
+  static constexpr bool kOverlapNext = kFp8;
 };
 
 struct DecodeParams {
@@ -229,22 +241,22 @@ __device__ RangeMap plan_ranges(int T, int nwaves, int cap) {
   return m;
 }
 
-// Eight E4M3 codes (two words) widened exactly to one 16-bit MFMA operand.
+// Eight E4M3 codes (two words) widened exactly to one 16-bit MFMA operand
+// by the packed conversions to float16 / bfloat16 (scale 1: every E4M3
+// value is representable in both formats).
 template <int DT>
 __device__ __forceinline__ u32x4 widen_e4m3x8(int w0, int w1) {
-  typedef float float2_ __attribute__((ext_vector_type(2)));
-  const float2_ f[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(w0, false),
-                        __builtin_amdgcn_cvt_pk_f32_fp8(w0, true),
-                        __builtin_amdgcn_cvt_pk_f32_fp8(w1, false),
-                        __builtin_amdgcn_cvt_pk_f32_fp8(w1, true)};
   u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (DT == PKV_F16) {
-      r[i] = float_to_bits<PKV_F16>(f[i].x) | (float_to_bits<PKV_F16>(f[i].y) << 16);
-    } else {  // the codes' values have 4 significant bits: the upper half is exact
-      r[i] = (bits_of(f[i].x) >> 16) | (bits_of(f[i].y) & 0xffff0000u);
-    }
+  if constexpr (DT == PKV_F16) {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true));
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true));
   }
   return r;
 }
@@ -639,12 +651,23 @@ paged_decode_kernel(const DecodeParams p) {
   // last tile is computed)
   QRegs qa;
 
-  // the current piece
+  // the current piece (set at every piece's first tile; defined here too,
+  // since undefined loop-carried values get lowered to reads of arbitrary
+  // registers, which may be waiting on a load)
   float m_run[GC], l_run[GC], acc[GC][EPC];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
+  }
   bool pc_seg_start = false;
   int pc_slot = 0;
 
-  auto step = [&](const Tile& tc, Tile& tn) __attribute__((always_inline)) -> bool {
+  bool done = false;  // the wave's last tile is computed
+  auto step = [&](const Tile& tc, Tile& tn) __attribute__((always_inline)) {
+    if (done) return;
     // 1. look ahead: prepare the next window (of this range or the next)
     if (!have_nw && !no_more && cw.cnt - ci <= kPrepAhead) {
       const int r2 = cw.ends_range ? cw.r + nwaves : cw.r;
@@ -669,7 +692,12 @@ paged_decode_kernel(const DecodeParams p) {
     const int j = in_cw ? ci + 1 : 0;
     const int info_n = __builtin_amdgcn_readlane(pick(in_cw, cw.info, nw.info), j);
     const int s_n = __builtin_amdgcn_readlane(pick(in_cw, cw.s, nw.s), j);
-    if (more) load_tile(tn, __builtin_amdgcn_readlane(pick(in_cw, cw.id, nw.id), j), info_n & 0xffff);
+    // Issued on every step, also after the wave's last tile (then of lane 0
+    // of a stale window: every window lane holds a block id clamped into
+    // the pool).  A load issued on some paths only would make the wait for
+    // this tile's data also wait for the next tile's.
+    load_tile(tn, __builtin_amdgcn_readlane(pick(in_cw, cw.id, nw.id), j), info_n & 0xffff);
+    if constexpr (!C::kOverlapNext) __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
 
     // 3. compute the current tile
     if (info & kPieceFirst) {
@@ -722,11 +750,12 @@ paged_decode_kernel(const DecodeParams p) {
         for (int g = 0; g < GC; ++g) pv[g] = pw[tok * GC + g];
         u32x4 vv = tc.v[ld];
         if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
+        float fv[EPC];
+        widen_chunk<KT>(vv, fv);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          const float f = elem_to_float<KT>(vv, e);
 #pragma unroll
-          for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], f, acc[g][e]);
+          for (int g = 0; g < GC; ++g) acc[g][e] = fmaf(pv[g], fv[e], acc[g][e]);
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -783,12 +812,11 @@ paged_decode_kernel(const DecodeParams p) {
 
     // 5. advance
     if (++ci == cw.cnt) {
-      if (!have_nw) return false;
+      done = !have_nw;
       cw = nw;
       have_nw = false;
       ci = 0;
     }
-    return true;
   };
 
   // two register tiles, alternating: the next tile is in flight while the
@@ -799,9 +827,14 @@ paged_decode_kernel(const DecodeParams p) {
     load_tile(ta, __builtin_amdgcn_readlane(cw.id, 0), info & 0xffff);
     load_q(qa, __builtin_amdgcn_readlane(cw.s, 0), info & 0xffff);
   }
+  // One exit, at the end of the body: leaving between the two steps leaves
+  // the second step's loop-carried values undefined on that path, and
+  // those get materialized from arbitrary registers -- which can hold a
+  // load in flight, so every step would wait for it.
   for (;;) {
-    if (!step(ta, tb)) break;
-    if (!step(tb, ta)) break;
+    step(ta, tb);
+    step(tb, ta);
+    if (done) break;
   }
 }
 
@@ -850,7 +883,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const Deco
 // ------------------------------------------------------------------ host --
 // Resident workgroups of a kernel on the current device (memoized: the
 // answer depends only on the device and the kernel's resources).
-static int resident_workgroups(const void* kernel) {
+static int resident_workgroups(const void* kernel, int waves_per_simd) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   static std::mutex mu;
@@ -864,7 +897,7 @@ static int resident_workgroups(const void* kernel) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
     return 0;
   // a workgroup puts one wave on each SIMD of its CU
-  if (per_cu > kWavesPerSimd) per_cu = kWavesPerSimd;
+  if (per_cu > waves_per_simd) per_cu = waves_per_simd;
   int n = cus * (per_cu > 0 ? per_cu : 1);
   n = n > kMaxWGs ? kMaxWGs : n;
   memo.push_back({{dev, kernel}, n});
@@ -874,7 +907,7 @@ static int resident_workgroups(const void* kernel) {
 template <int DT, int KT, int D, int GC>
 static hipError_t launch_decode(const DecodeParams& a, hipStream_t st) {
   const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC>);
-  const int nwg = resident_workgroups(k);
+  const int nwg = resident_workgroups(k, DecodeCfg<DT, KT, D, GC>::kGridWaves);
   if (nwg <= 0) return hipErrorInvalidDevice;
   hipLaunchKernelGGL((paged_decode_kernel<DT, KT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
                      a);

@@ -77,6 +77,28 @@ __device__ __forceinline__ float elem_to_float<PKV_FP8_E4M3>(const u32x4& v, int
   }
 }
 
+// Every element of a 16-byte chunk widened to float; E4M3 codes two at a
+// time with the packed hardware conversion (exact).
+template <int KT>
+__device__ __forceinline__ void widen_chunk(const u32x4& v, float (&f)[Elt<KT>::kPer16B]) {
+  if constexpr (KT == PKV_FP8_E4M3) {
+    typedef float float2_ __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int word = (int)v[w];
+      const float2_ lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const float2_ hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      f[4 * w] = lo.x;
+      f[4 * w + 1] = lo.y;
+      f[4 * w + 2] = hi.x;
+      f[4 * w + 3] = hi.y;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < Elt<KT>::kPer16B; ++e) f[e] = elem_to_float<KT>(v, e);
+  }
+}
+
 // E4M3 code of a float: nearest code, ties to the even mantissa; |x| >=
 // 448 (inf included) saturates to +-448; NaN gives 0x7F.  Written from the
 // format: below 2^-6 the codes are the multiples of 2^-9 (8 reaching the
