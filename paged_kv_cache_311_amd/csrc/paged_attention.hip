@@ -692,11 +692,12 @@ paged_decode_kernel(const DecodeParams p) {
     const int j = in_cw ? ci + 1 : 0;
     const int info_n = __builtin_amdgcn_readlane(pick(in_cw, cw.info, nw.info), j);
     const int s_n = __builtin_amdgcn_readlane(pick(in_cw, cw.s, nw.s), j);
-    // Issued on every step, also after the wave's last tile (then of lane 0
-    // of a stale window: every window lane holds a block id clamped into
-    // the pool).  A load issued on some paths only would make the wait for
-    // this tile's data also wait for the next tile's.
-    load_tile(tn, __builtin_amdgcn_readlane(pick(in_cw, cw.id, nw.id), j), info_n & 0xffff);
+    // Issued on every step; after the wave's last tile it reloads that tile
+    // (just read, so served by L2).  A load issued on some paths only would
+    // make the wait for this tile's data also wait for the next tile's.
+    const int id_n = __builtin_amdgcn_readlane(pick(in_cw, cw.id, nw.id), j);
+    const int id_c = __builtin_amdgcn_readlane(cw.id, ci);
+    load_tile(tn, more ? id_n : id_c, more ? (info_n & 0xffff) : hg);
     if constexpr (!C::kOverlapNext) __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
 
     // 3. compute the current tile
