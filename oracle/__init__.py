@@ -32,6 +32,7 @@ from .paged_attention import (  # noqa: F401
     attention_one_head,
 )
 from .cache_ops import reshape_and_cache, copy_blocks, reshape_and_cache_fp8  # noqa: F401
+from .prefill import prefill_attention  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, quantize as e4m3_quantize  # noqa: F401
 from .kv_accounting import (  # noqa: F401
     kv_bytes_per_token,

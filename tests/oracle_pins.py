@@ -514,10 +514,135 @@ def pin_decode_fp8(o):
     assert np.isfinite(got).all() and np.abs(got).max() > 0
 
 
+# ----------------------------------------------------------------- prefill --
+def prefill_case(seed, lens, news, Hq, Hkv, D, dtype, extra_blocks=3):
+    """scatter_case plus packed queries: sequence s has news[s] new rows,
+    its last news[s] tokens."""
+    c = scatter_case(seed, lens, Hq, Hkv, D, dtype, extra_blocks=extra_blocks)
+    rng = np.random.default_rng(seed + 1000)
+    qsl = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    c["query"] = encode(rng.standard_normal((int(qsl[-1]), Hq, D)), dtype)
+    c["query_start_loc"] = qsl
+    return c
+
+
+def run_prefill(o, c, scale):
+    return o.prefill_attention(c["query"], c["key_cache"], c["value_cache"],
+                               c["block_tables"], c["context_lens"], c["query_start_loc"],
+                               scale, c["Hkv"], c["dtype"])
+
+
+def torch_causal(c, scale):
+    """torch float64 attention on the contiguous copies with the mask written
+    out: row i of a sequence with L tokens and n new rows sees t <= L - n + i
+    (is_causal=True when n = L)."""
+    Hq, Hkv = c["Hq"], c["Hkv"]
+    G = Hq // Hkv
+    q = widen(c["query"], c["dtype"])
+    qsl = c["query_start_loc"]
+    out = np.zeros(tuple(q.shape))
+    for s in range(len(c["context_lens"])):
+        a, b = int(qsl[s]), int(qsl[s + 1])
+        n, L = b - a, int(c["context_lens"][s])
+        if n == 0:
+            continue
+        K = widen(c["seqs_k"][s], c["dtype"]).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        V = widen(c["seqs_v"][s], c["dtype"]).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        qh = q[a:b].permute(1, 0, 2)                                  # [Hq, n, D]
+        if n == L:
+            r = torch.nn.functional.scaled_dot_product_attention(
+                qh, K, V, is_causal=True, scale=float(np.float32(scale)))
+        else:
+            mask = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]
+            r = torch.nn.functional.scaled_dot_product_attention(
+                qh, K, V, attn_mask=mask, scale=float(np.float32(scale)))
+        out[a:b] = r.permute(1, 0, 2).numpy()
+    return out
+
+
+PREFILL_CASES = [
+    # (seed, lens, new rows, Hq, Hkv, D, dtype)
+    (21, [17, 40, 5], [17, 40, 5], 4, 2, 8, "f16"),     # whole prompts
+    (22, [33, 70, 16], [9, 1, 16], 4, 4, 8, "bf16"),    # chunks after a prefix
+    (23, [50, 3], [20, 0], 8, 2, 16, "f32"),
+    (24, [64, 31], [32, 31], 2, 1, 64, "f16"),
+]
+
+
+def pin_prefill_torch(o):
+    for seed, lens, news, Hq, Hkv, D, dt in PREFILL_CASES:
+        c = prefill_case(seed, lens, news, Hq, Hkv, D, dt)
+        scale = np.float32(1.0 / math.sqrt(D))
+        got = run_prefill(o, c, scale)
+        ref = torch_causal(c, scale)
+        assert got.shape == ref.shape
+        err = np.abs(got - ref).max()
+        assert err <= 1e-12, (seed, err)
+
+
+def pin_prefill_loops(o):
+    """Pure-Python loops with the visibility rule written out, tiny sizes."""
+    c = prefill_case(25, [19, 6], [5, 6], 4, 2, 4, "f32")
+    scale = np.float32(0.7)
+    got = run_prefill(o, c, scale)
+    q = widen(c["query"], "f32").numpy()
+    qsl = c["query_start_loc"]
+    for s, L in enumerate(c["context_lens"]):
+        K = widen(c["seqs_k"][s], "f32").numpy()
+        V = widen(c["seqs_v"][s], "f32").numpy()
+        n = int(qsl[s + 1] - qsl[s])
+        for i in range(n):
+            for h in range(4):
+                g = h // 2
+                logits = [float(scale) * sum(q[qsl[s] + i, h, d] * K[t, g, d] for d in range(4))
+                          for t in range(int(L)) if t <= int(L) - n + i]
+                m = max(logits)
+                w = [math.exp(x - m) for x in logits]
+                for d in range(4):
+                    want = sum(w[t] * V[t, g, d] for t in range(len(w))) / sum(w)
+                    assert abs(got[qsl[s] + i, h, d] - want) <= 1e-12
+
+
+def pin_prefill_rows_are_decodes(o):
+    """Row i of a chunk equals a decode step of the same query at length
+    L - n + i + 1 (same pool, same table): the two oracles agree exactly."""
+    c = prefill_case(26, [45, 20], [13, 20], 4, 2, 8, "f16", extra_blocks=5)
+    scale = np.float32(0.4)
+    got = run_prefill(o, c, scale)
+    qsl = c["query_start_loc"]
+    for s, L in enumerate(c["context_lens"]):
+        n = int(qsl[s + 1] - qsl[s])
+        for i in range(n):
+            lens = np.zeros(len(c["context_lens"]), np.int32)
+            lens[s] = int(L) - n + i + 1
+            q = np.zeros((len(lens),) + c["query"].shape[1:], c["query"].dtype)
+            q[s] = c["query"][qsl[s] + i]
+            d = o.decode_attention(q, c["key_cache"], c["value_cache"], c["block_tables"],
+                                   lens, scale, c["Hkv"], c["dtype"], seqs=[s])
+            assert np.array_equal(d[s], got[qsl[s] + i]), (s, i)
+
+
+def pin_prefill_permutation_invariance(o):
+    c = prefill_case(27, [50, 16, 77], [10, 16, 3], 4, 2, 16, "bf16", extra_blocks=9)
+    scale = np.float32(0.25)
+    ref = run_prefill(o, c, scale)
+    pi = np.random.default_rng(28).permutation(c["key_cache"].shape[0])
+    kc = np.empty_like(c["key_cache"])
+    vc = np.empty_like(c["value_cache"])
+    kc[pi] = c["key_cache"]
+    vc[pi] = c["value_cache"]
+    bt = c["block_tables"].copy()
+    bt[bt >= 0] = pi[bt[bt >= 0]]
+    got = run_prefill(o, dict(c, key_cache=kc, value_cache=vc, block_tables=bt), scale)
+    assert np.array_equal(got, ref)
+
+
 ALL_PINS = [
     pin_brute_force, pin_torch_sdpa, pin_permutation_invariance,
     pin_gqa_reduction, pin_sharing_invariance, pin_partition_merge,
     pin_special_cases, pin_kv_bytes, pin_waste_bound,
     pin_reshape_and_cache, pin_copy_blocks, pin_formats,
     pin_e4m3_codec, pin_reshape_fp8, pin_decode_fp8,
+    pin_prefill_torch, pin_prefill_loops, pin_prefill_rows_are_decodes,
+    pin_prefill_permutation_invariance,
 ]

@@ -91,6 +91,20 @@ MUTANTS = [
      "kv_dtype, block_size) * v_scale64", "kv_dtype, block_size)"),
     ("reshape_fp8_key_scale_for_value", "cache_ops.py",
      "vq = quantize(value, dtype, v_scale)", "vq = quantize(value, dtype, k_scale)"),
+    ("prefill_ignores_prefix", "prefill.py",
+     "visible = L - n + i + 1", "visible = i + 1"),
+    ("prefill_excludes_self", "prefill.py",
+     "visible = L - n + i + 1", "visible = L - n + i"),
+    ("prefill_sees_future", "prefill.py",
+     "visible = L - n + i + 1", "visible = L"),
+    ("prefill_rows_of_first_sequence", "prefill.py",
+     "out[qsl[s] + i, h] = attention_one_head", "out[i, h] = attention_one_head"),
+    ("prefill_gqa_interleaved", "prefill.py",
+     "for h in range(g * group, (g + 1) * group):\n                    out[qsl[s] + i, h]",
+     "for h in range(g, Hq, num_kv_heads):\n                    out[qsl[s] + i, h]"),
+    ("prefill_values_are_keys", "prefill.py",
+     "keys[:visible],\n                                                            values[:visible]",
+     "keys[:visible],\n                                                            keys[:visible]"),
 ]
 
 
