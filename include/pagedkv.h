@@ -8,8 +8,11 @@
  *                           each sequence's block table;
  *   reshape_and_cache       scatter new tokens' keys/values to their slots;
  *   copy_blocks             block-level copy-on-write of shared blocks;
- * and the first two again for pools of 8-bit float (E4M3) codes with one
- * scale per pool (paged_attention_decode_fp8, reshape_and_cache_fp8).
+ * the first two again for pools of 8-bit float (E4M3) codes with one
+ * scale per pool (paged_attention_decode_fp8, reshape_and_cache_fp8); and
+ *   paged_attention_prefill causal attention of a chunk of new tokens per
+ *                           sequence (a whole prompt, or the next part of
+ *                           one) over the cached tokens, on the same pools.
  *
  * Sources (titles of the pages this library follows):
  *   [TEQ]  "Your GPU was mostly empty: how PagedAttention turned KV-cache
@@ -73,7 +76,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 3 */
+int pkv_abi_version(void);  /* 4 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -240,6 +243,55 @@ int paged_attention_decode_fp8(void* out, const void* query, const void* key_cac
                                int max_blocks_per_seq, int64_t num_blocks,
                                int partition_size, void* workspace,
                                size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * paged_attention_prefill
+ *
+ * The new tokens of each sequence attend causally to its cached tokens:
+ * the prompt (or the next chunk of it) has been written into the blocks
+ * the runtime assigned ([AITJ] "A request lifecycle: allocation, growth,
+ * sharing and release"), and each new token sees every token up to its
+ * own position, the decoder's masked self-attention ([VAS] section 3.2.3,
+ * eq. (1)); keys and values are read through the block table as in
+ * decoding ([IV] "Architecture, step by step", step 3).
+ *
+ * Sequence s owns the n_s = query_start_loc[s+1] - query_start_loc[s]
+ * rows query_start_loc[s] .. +n_s-1 of `query` and `out`.  With
+ * L = context_lens[s] (clamped to [0, 16*max_blocks_per_seq]), those rows
+ * are the sequence's last n_s tokens, whose keys and values are already in
+ * the pools: row i sits at position L - n_s + i and, for every query head
+ * h with kv head g = h / (num_heads / num_kv_heads),
+ *     out[row][h] = sum_t softmax_t(scale * q[row][h] . k_t) v_t,
+ *     t = 0 .. L - n_s + i.
+ * n_s = L is a whole prompt; n_s < L a chunk after a cached prefix.
+ *
+ *   out, query       [total rows][num_heads][head_size], `dtype`
+ *                    (PKV_F16 or PKV_BF16); query 16-byte aligned, out
+ *                    8-byte aligned
+ *   key_cache, value_cache, block_tables, num_blocks, scale: as for
+ *                    paged_attention_decode (pools in `dtype`)
+ *   query_start_loc  int32 [num_seqs + 1], non-decreasing from 0
+ *   max_query_len    at least every n_s (sizes the grid; rows of a
+ *                    sequence beyond it are not written); n_s <= L
+ *
+ * Work: one workgroup per 128 rows of one (sequence, kv head), rows being
+ * (new token, query head of the group) pairs; keys are walked 32 at a
+ * time through LDS and both products run on MFMA with float32
+ * accumulation.  The probabilities enter the second product rounded to
+ * `dtype`.  No workspace.  Errors: INVALID_ARG for null pointers, sizes
+ * out of range, Hq % Hkv != 0 or misalignment; UNSUPPORTED for other
+ * dtypes, block_size != 16 or head_size not 64/128.  Device-side contents
+ * (tables, lengths, query_start_loc) are not validated; every read stays
+ * inside the buffers whatever they hold, provided query_start_loc
+ * describes rows of `query`.
+ */
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start_loc,
+                            float scale, int num_kv_heads, int num_seqs, int num_heads,
+                            int head_size, int block_size, int max_blocks_per_seq,
+                            int64_t num_blocks, int max_query_len, int dtype,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ from .paged_attention import attention_one_head, gather_sequence_kv
 
 
 def prefill_attention(query, key_cache, value_cache, block_tables, context_lens,
-                      query_start_loc, scale, num_kv_heads, dtype, block_size=16):
+                      query_start_loc, scale, num_kv_heads, dtype, block_size=16, seqs=None):
     """Causal attention of every new token of every sequence, float64.
 
     query            [T, Hq, D]        storage format of `dtype`
@@ -47,6 +47,7 @@ def prefill_attention(query, key_cache, value_cache, block_tables, context_lens,
     context_lens     [S] integer       L_s, cached prefix plus new tokens
     query_start_loc  [S + 1] integer   rows of each sequence in `query`
     scale            float32 value (widened exactly)
+    seqs             optional list of sequences to compute (other rows stay 0)
 
     Returns [T, Hq, D] float64.
     """
@@ -60,7 +61,7 @@ def prefill_attention(query, key_cache, value_cache, block_tables, context_lens,
     group = Hq // num_kv_heads
     scale64 = float(np.float32(scale))
     out = np.zeros((T, Hq, D), dtype=np.float64)
-    for s in range(S):
+    for s in (range(S) if seqs is None else seqs):
         L = int(context_lens[s])
         n = int(qsl[s + 1] - qsl[s])
         if n > L:

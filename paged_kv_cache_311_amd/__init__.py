@@ -1,9 +1,10 @@
 """Paged KV-cache decode path for MI355X (gfx950): HIP kernels behind a C ABI.
 
 The three operations -- paged_attention_decode, reshape_and_cache and
-copy_blocks -- and the fp8 variants of the first two (pools of E4M3 codes
-with one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8)
-run entirely in the HIP kernels of libpagedkv.so (declared in
+copy_blocks -- the fp8 variants of the first two (pools of E4M3 codes with
+one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8) and
+paged_attention_prefill (causal attention of a chunk of new tokens) run
+entirely in the HIP kernels of libpagedkv.so (declared in
 include/pagedkv.h).  This module only marshals torch tensors (device
 memory and the current stream) into the C calls and raises on a nonzero
 status.  There is no fallback: if the library is missing or was not built,
@@ -61,6 +62,9 @@ def _declare(lib):
     lib.reshape_and_cache_fp8.restype = c_int
     lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_f, c_f, c_int, c_int, c_int,
                                           c_int, c_i64, c_int, vp]
+    lib.paged_attention_prefill.restype = c_int
+    lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int,
+                                            c_int, c_int, c_int, c_i64, c_int, c_int, vp]
     return lib
 
 
@@ -213,6 +217,50 @@ def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,
     v_scale.  query/out float16 or bfloat16."""
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, True, k_scale, v_scale)
+
+
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
+                            query_start_loc, scale, num_kv_heads, max_query_len,
+                            validate=False):
+    """Causal attention of each sequence's new tokens over its cached ones.
+
+    query/out [T, Hq, D] (float16 or bfloat16): sequence s owns rows
+    query_start_loc[s] .. query_start_loc[s+1]-1, its last n_s tokens
+    (already written to the pools); row i sees tokens 0 .. L_s - n_s + i.
+    query_start_loc int32 [S+1]; max_query_len >= every n_s.
+    """
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens,
+                         query_start_loc)
+    code = _dtype_code(query)
+    for t in (out, key_cache, value_cache):
+        _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
+    for t in (block_tables, context_lens, query_start_loc):
+        _need(t.dtype == torch.int32, "block_tables, context_lens, query_start_loc: int32")
+    T, Hq, D = query.shape
+    NB, Hkv, bs, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    _need(tuple(out.shape) == (T, Hq, D), "out must match query")
+    _need(tuple(value_cache.shape) == tuple(key_cache.shape), "pools must match")
+    _need(D2 == D and Hkv == num_kv_heads, "pool shape does not match query")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables [S, W]")
+    _need(tuple(query_start_loc.shape) == (S + 1,), "query_start_loc [S + 1]")
+    W = block_tables.shape[1]
+    if validate:
+        _validate_tables(block_tables, context_lens, NB)
+        qsl = query_start_loc.cpu().numpy().astype(np.int64)
+        lens = context_lens.cpu().numpy().astype(np.int64)
+        n = np.diff(qsl)
+        _need(qsl[0] == 0 and qsl[-1] == T and (n >= 0).all(),
+              "query_start_loc must rise from 0 to the number of rows")
+        _need((n <= lens).all(), "more new tokens than the context holds")
+        _need(not len(n) or n.max() <= max_query_len, "max_query_len below a sequence's rows")
+    _check(lib.paged_attention_prefill(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start_loc), float(scale), int(num_kv_heads), S, Hq, D,
+        bs, W, NB, int(max_query_len), code, _stream_of(query)))
+    return out
 
 
 def reshape_and_cache(key, value, slot_mapping, key_cache, value_cache, validate=False):

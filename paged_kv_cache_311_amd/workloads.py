@@ -27,6 +27,13 @@ sampling over a shared prompt, long contexts):
   opt13b_fp8,    the same shapes and lengths with pools of OCP E4M3 codes
   long_gqa_fp8   and one scale per pool (keys 1/64, values 3/128); queries,
                  outputs and new tokens stay fp16 / bf16.
+  prefill_chunk  chunked prefill: 16 seqs, 40 heads of 128, fp16, a cached
+                 prefix of U{0..1536} tokens and a new chunk of 512 tokens
+                 each (written by reshape_and_cache, then attended).
+  prefill_gqa    whole prompts: 8 seqs of 2048 new tokens, 32 query heads
+                 over 8 kv heads of 128, bf16.
+  prefill_tiny   4 seqs, 4 query / 2 kv heads of 64, fp16, prefixes
+                 U{0..40}, chunks U{1..24}, a 64-block pool.
 
 An E4M3 pool is drawn as codes: N(0,1) values divided by the pool's scale,
 clamped to the format's range and converted by torch's float8_e4m3fn cast
@@ -64,7 +71,7 @@ class Workload:
     dtype: str              # "f32" | "f16" | "bf16"
     lengths: tuple          # see draw_context_lens
     pool: tuple             # ("blocks", n) | ("factor", f)
-    step: str               # "decode" | "append" | "cow"
+    step: str               # "decode" | "append" | "cow" | "prefill"
     max_len: int            # longest possible context (sets the table width)
     partition_size: int = 0   # cap on tokens per piece of a split context (0: none)
     prompts: int = 0
@@ -72,6 +79,11 @@ class Workload:
     kv_dtype: str = ""      # "" (pools in `dtype`) | "e4m3" (pools of E4M3 codes)
     k_scale: float = 1.0    # per-pool scales of an E4M3 pool
     v_scale: float = 1.0
+
+    @property
+    def max_query_len(self):
+        """Most new tokens of one sequence in a prefill step."""
+        return int(self.lengths[4]) if self.step == "prefill" else 1
 
     @property
     def fp8(self):
@@ -119,6 +131,12 @@ WORKLOADS = {
         Workload("long_gqa_fp8", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
                  ("factor", 1.25), "decode", 32768, kv_dtype="e4m3",
                  k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE),
+        Workload("prefill_chunk", 8, 16, 40, 40, 128, "f16", ("prefill", 0, 1536, 512, 512),
+                 ("factor", 1.25), "prefill", 2048),
+        Workload("prefill_gqa", 9, 8, 32, 8, 128, "bf16", ("prefill", 0, 0, 2048, 2048),
+                 ("factor", 1.25), "prefill", 2048),
+        Workload("prefill_tiny", 10, 4, 4, 2, 64, "f16", ("prefill", 0, 40, 1, 24),
+                 ("blocks", 64), "prefill", 64),
     )
 }
 
@@ -239,10 +257,41 @@ def draw_metadata(w, seed):
       token_seq     int64 [T]      (append / cow) sequence of each new token
       cow_pairs     int64 [N, 2]   (cow) blocks to copy before the writes
       shared_blocks int            (cow) blocks referenced by > 1 sequence
+      query_start_loc int32 [S+1]  (prefill) rows of each sequence's chunk
     """
     rng = np.random.default_rng(seed)
     bs = BLOCK_SIZE
     md = {}
+    if w.step == "prefill":
+        # a cached prefix of P tokens and a chunk of n new ones per sequence:
+        # the chunk's slots are assigned (blocks taken for all P + n tokens)
+        # but hold no token until the step writes them
+        if w.lengths[0] == "prefill":
+            plo, phi, nlo, nhi = w.lengths[1:]
+            P = rng.integers(plo, phi + 1, size=w.num_seqs)
+            n = rng.integers(nlo, nhi + 1, size=w.num_seqs)
+        else:  # ("prefill_list", prefixes, chunks), for edge-case tests
+            P = np.asarray(w.lengths[1], dtype=np.int64)
+            n = np.asarray(w.lengths[2], dtype=np.int64)
+        lens = (P + n).astype(np.int64)
+        need = int(sum(-(-int(L) // bs) for L in lens))
+        nb = _pool_blocks(w, need)
+        mgr = BlockManager(nb, rng)
+        tables, slots, token_seq = [], [], []
+        for s_, L in enumerate(lens):
+            t = mgr.allocate_for(int(L))
+            tables.append(t)
+            for pos in range(int(P[s_]), int(L)):
+                slots.append(t[pos // bs] * bs + pos % bs)
+                token_seq.append(s_)
+        md["context_lens"] = lens.astype(np.int32)
+        md["block_tables"] = _table_array(tables, w.table_width)
+        md["num_blocks"] = nb
+        md["live_slots"] = _live_slot_mask(nb, tables, P)
+        md["slot_mapping"] = np.asarray(slots, dtype=np.int64)
+        md["token_seq"] = np.asarray(token_seq, dtype=np.int64)
+        md["query_start_loc"] = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        return md
     if w.step in ("decode", "append"):
         lens = draw_context_lens(w, rng)
         need = int(sum(-(-int(L) // bs) for L in lens))
@@ -366,9 +415,10 @@ def make_batch(w, seed=None, device="cpu", chunk_blocks=2048):
             cache[torch.from_numpy(ids).to(device)] = vals
         caches.append(cache)
     batch = dict(md)
+    nq = int(md["query_start_loc"][-1]) if w.step == "prefill" else S
     batch.update(
         workload=w, seed=seed, scale=w.scale,
-        query=_randn((S, Hq, D), gen, device, w.dtype),
+        query=_randn((nq, Hq, D), gen, device, w.dtype),
         key_cache=caches[0], value_cache=caches[1],
     )
     if "slot_mapping" in md:
@@ -390,6 +440,17 @@ def to_host(t):
 def kv_token_count(md):
     """Tokens attended in one decode step (sum of context lengths)."""
     return int(np.asarray(md["context_lens"], dtype=np.int64).sum())
+
+
+def custom_prefill(prefixes, chunks, num_heads, num_kv_heads, head_size, dtype,
+                   pool_factor=1.25):
+    """A prefill workload with explicit prefix and chunk lengths."""
+    prefixes = tuple(int(x) for x in prefixes)
+    chunks = tuple(int(x) for x in chunks)
+    max_len = max(max(p + c for p, c in zip(prefixes, chunks)), 1)
+    return Workload("custom_prefill", 0, len(chunks), num_heads, num_kv_heads, head_size,
+                    dtype, ("prefill_list", prefixes, chunks, 0, max(chunks)),
+                    ("factor", pool_factor), "prefill", max_len)
 
 
 def custom(lens, num_heads, num_kv_heads, head_size, dtype, max_len=None,

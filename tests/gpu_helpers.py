@@ -216,3 +216,36 @@ def sample_seqs(lens, k=3, seed=7):
     pick = {int(np.argmin(lens)), int(np.argmax(lens))}
     pick.update(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
     return sorted(pick)
+
+
+def run_prefill(b, out=None):
+    w = b["workload"]
+    out = torch.empty_like(b["query"]) if out is None else out
+    pkv.paged_attention_prefill(out, b["query"], b["key_cache"], b["value_cache"],
+                                dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
+                                dev_i32(b["query_start_loc"]), float(w.scale), w.num_kv_heads,
+                                w.max_query_len, validate=True)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prefill_subset(b, kc_before, vc_before, seqs):
+    """Oracle rows of the chosen sequences (their chunks, packed in order),
+    after replaying the step's cache writes on host copies of the pools."""
+    w = b["workload"]
+    ids = blocks_read_by(b, seqs)
+    if len(ids) == 0:
+        ids = np.zeros(1, np.int64)
+    kc, vc, remap = oracle_pool(b, kc_before, vc_before, ids)
+    bt, qsl = b["block_tables"], b["query_start_loc"]
+    lens = b["context_lens"][seqs]
+    tables = np.full((len(seqs), bt.shape[1]), -1, np.int32)
+    for i, s in enumerate(seqs):
+        n = -(-int(lens[i]) // BS)
+        tables[i, :n] = [remap[int(x)] for x in bt[s, :n]]
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs]).astype(np.int64)
+    sub_qsl = np.concatenate([[0], np.cumsum([qsl[s + 1] - qsl[s] for s in seqs])])
+    q = wl.to_host(b["query"])[rows]
+    ref = oracle.prefill_attention(q, kc, vc, tables, lens, sub_qsl, w.scale, w.num_kv_heads,
+                                   w.dtype)
+    return rows, ref

@@ -36,7 +36,7 @@ def declared_functions(header=HEADER):
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("paged_attention_decode", "reshape_and_cache", "copy_blocks",
-              "paged_attention_decode_fp8", "reshape_and_cache_fp8",
+              "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
               "paged_attention_workspace_bytes", "pkv_status_string", "pkv_abi_version"):
         assert n in names
 
@@ -66,7 +66,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -237,3 +237,29 @@ def test_binding_rejects_host_tensors(lib):
         pkv.paged_attention_decode(q.clone(), q, kc, kc.clone(),
                                    torch.zeros(2, 1, dtype=torch.int32),
                                    torch.ones(2, dtype=torch.int32), 0.125, 4)
+
+
+def prefill(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, qsl=FAKE, scale=0.1,
+             hkv=4, S=2, Hq=8, D=128, bs=16, W=4, NB=64, mq=16, dtype=1, stream=0)
+    a.update(kw)
+    return lib.paged_attention_prefill(
+        a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["qsl"], a["scale"],
+        a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["mq"], a["dtype"],
+        a["stream"])
+
+
+def test_prefill_argument_validation(lib):
+    assert prefill(lib, qsl=0) == INVALID
+    assert prefill(lib, out=0) == INVALID
+    assert prefill(lib, Hq=6) == INVALID
+    assert prefill(lib, mq=-1) == INVALID
+    assert prefill(lib, NB=0) == INVALID
+    assert prefill(lib, dtype=0) == UNSUPPORTED          # float32: no MFMA path
+    assert prefill(lib, dtype=3) == UNSUPPORTED
+    assert prefill(lib, bs=32) == UNSUPPORTED
+    assert prefill(lib, D=96) == UNSUPPORTED
+    assert prefill(lib, query=FAKE + 8) == INVALID        # 16-byte loads
+    assert prefill(lib, out=FAKE + 4) == INVALID          # 8-byte stores
+    assert prefill(lib, S=0) == OK                        # nothing to do: no launch
+    assert prefill(lib, mq=0) == OK

@@ -1,0 +1,149 @@
+"""Parity of paged prefill attention with the CPU oracle on an MI355X
+(marked gpu).
+
+A prefill step writes each sequence's chunk of new tokens into its slots
+(reshape_and_cache, compared bit for bit) and then runs
+paged_attention_prefill: every new token attends to the cached tokens up to
+its own position ("PagedAttention KV cache memory management" [AITJ], "A
+request lifecycle: allocation, growth, sharing and release"; Vaswani et al.
+section 3.2.3).  Outputs are compared with the float64 oracle within the
+tolerances of the decode tests (5e-3 for float16/bfloat16 inputs, plus half
+an output ulp for bfloat16).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_311_amd as pkv
+from paged_kv_cache_311_amd import workloads as wl
+from tests.gpu_helpers import (DEV, assert_close, bits, clone_pools, dev_i32, gather_blocks,
+                               oracle_pool, oracle_prefill_subset, run_decode, run_pool_updates,
+                               run_prefill, say)
+
+pytestmark = pytest.mark.gpu
+
+W = wl.WORKLOADS
+
+
+def prefill_step_and_check(b, seqs=None):
+    w = b["workload"]
+    kc0, vc0 = clone_pools(b)
+    run_pool_updates(b)
+    touched = np.asarray(sorted({int(s) // wl.BLOCK_SIZE for s in b["slot_mapping"]}), np.int64)
+    if len(touched):
+        ek, ev, _ = oracle_pool(b, kc0, vc0, touched)
+        assert gather_blocks(b["key_cache"], touched).tobytes() == ek.tobytes()
+        assert gather_blocks(b["value_cache"], touched).tobytes() == ev.tobytes()
+    out = run_prefill(b)
+    seqs = list(range(w.num_seqs)) if seqs is None else seqs
+    rows, ref = oracle_prefill_subset(b, kc0, vc0, seqs)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, w.dtype,
+                 f"prefill {w.key} seqs={len(seqs)} rows={len(rows)}")
+    return out
+
+
+@pytest.mark.parametrize("seed", W["prefill_tiny"].seeds())
+def test_prefill_tiny_every_output(gpu_lib, seed):
+    b = wl.make_batch(W["prefill_tiny"], seed, DEV)
+    prefill_step_and_check(b)
+
+
+@pytest.mark.parametrize("key,kw", [
+    ("prefill_chunk", dict(num_seqs=3, lengths=("prefill", 0, 700, 100, 300))),
+    ("prefill_gqa", dict(num_seqs=2, lengths=("prefill", 0, 0, 300, 300))),
+    ("prefill_gqa", dict(num_seqs=2, lengths=("prefill", 200, 600, 1, 200))),
+])
+def test_prefill_reduced_every_output(gpu_lib, key, kw):
+    w = dataclasses.replace(W[key], **kw)
+    b = wl.make_batch(w, w.default_seed + 7, DEV)
+    prefill_step_and_check(b)
+
+
+@pytest.mark.parametrize("key", ["prefill_chunk", "prefill_gqa"])
+def test_prefill_full_size_sampled(gpu_lib, key):
+    """Full workload in the benchmark's launch configuration; the oracle on
+    the sequences with the longest and shortest contexts."""
+    w = W[key]
+    b = wl.make_batch(w, w.default_seed, DEV)
+    lens = b["context_lens"]
+    prefill_step_and_check(b, seqs=sorted({int(np.argmin(lens)), int(np.argmax(lens))}))
+
+
+GROUPS = [(4, 4), (8, 4), (8, 2), (8, 1), (16, 2), (6, 2), (12, 2), (10, 2), (32, 4)]
+
+
+@pytest.mark.parametrize("hq,hkv", GROUPS)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_head_grouping_and_types(gpu_lib, dtype, d, hq, hkv):
+    rng = np.random.default_rng(hq * 100 + hkv * 10 + d)
+    prefixes = rng.integers(0, 90, size=3)
+    chunks = rng.integers(1, 70, size=3)
+    w = wl.custom_prefill(prefixes, chunks, hq, hkv, d, dtype)
+    b = wl.make_batch(w, int(rng.integers(1 << 30)), DEV)
+    prefill_step_and_check(b)
+
+
+def test_prefill_edge_cases(gpu_lib):
+    """Whole prompts of 1, 15, 16, 17 tokens; chunks of one token (a decode
+    step); chunks ending exactly on block and 32-token boundaries; more
+    rows than one 128-row tile with a ragged tail; an empty chunk."""
+    prefixes = [0, 0, 0, 0, 40, 31, 16, 0, 100, 7]
+    chunks = [1, 15, 16, 17, 1, 1, 16, 200, 0, 57]
+    w = wl.custom_prefill(prefixes, chunks, 8, 2, 128, "f16")
+    b = wl.make_batch(w, 3, DEV)
+    out = prefill_step_and_check(b)
+    # one new token of a 1-token prompt sees only itself: out = its value
+    v0 = b["value_cache"][int(b["block_tables"][0, 0]), :, 0, :]       # [Hkv, D]
+    assert torch.equal(bits(out[0].view(2, 4, 128)[:, 0]), bits(v0))
+
+
+def test_prefill_one_token_chunks_match_decode(gpu_lib):
+    """A chunk of one token is a decode step: the prefill kernel and the
+    decode kernel agree within the float32 accumulation tolerance."""
+    prefixes = [0, 20, 63, 500, 1999]
+    w = wl.custom_prefill(prefixes, [1] * len(prefixes), 32, 8, 128, "bf16")
+    b = wl.make_batch(w, 11, DEV)
+    run_pool_updates(b)
+    out_p = run_prefill(b)
+    wd = wl.custom([p + 1 for p in prefixes], 32, 8, 128, "bf16", max_len=w.max_len,
+                   partition_size=0)
+    bd = dict(b, workload=wd)
+    out_d = run_decode(bd)
+    diff = (out_p.float() - out_d.float()).abs().max().item()
+    say(f"    prefill vs decode, one-token chunks: max diff {diff:.2e}")
+    assert diff <= 1e-2
+
+
+def test_prefill_placement_permutation_is_bitwise_invariant(gpu_lib):
+    w = dataclasses.replace(W["prefill_chunk"], num_seqs=4,
+                            lengths=("prefill", 0, 300, 50, 150))
+    b = wl.make_batch(w, 77, DEV)
+    run_pool_updates(b)
+    out = run_prefill(b).clone()
+    pi = np.random.default_rng(5).permutation(b["num_blocks"])
+    pit = torch.from_numpy(pi).to(DEV)
+    kc = torch.empty_like(b["key_cache"])
+    vc = torch.empty_like(b["value_cache"])
+    kc[pit] = b["key_cache"]
+    vc[pit] = b["value_cache"]
+    bt = b["block_tables"].copy()
+    bt[bt >= 0] = pi[bt[bt >= 0]]
+    out2 = run_prefill(dict(b, key_cache=kc, value_cache=vc, block_tables=bt))
+    assert torch.equal(bits(out), bits(out2))
+
+
+def test_prefill_rejects_bad_arguments(gpu_lib):
+    w = wl.custom_prefill([3], [5], 4, 2, 64, "f16")
+    b = wl.make_batch(w, 1, DEV)
+    out = torch.empty_like(b["query"])
+    args = (out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
+            dev_i32(b["context_lens"]), dev_i32(b["query_start_loc"]), float(w.scale), 2)
+    with pytest.raises(ValueError):
+        pkv.paged_attention_prefill(*args, 4, validate=True)      # max_query_len < 5
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_prefill(out.float(), b["query"].float(), b["key_cache"].float(),
+                                    b["value_cache"].float(), *args[4:], 5)   # float32

@@ -36,7 +36,7 @@ def test_metadata_invariants(key):
     # at most 15 empty slots per sequence; under 4% of the pool on every
     # workload of realistic lengths (the 4-sequence tiny case is too short)
     assert max(oracle.empty_slots(int(L)) for L in lens) <= BS - 1
-    if key != "tiny":
+    if key not in ("tiny", "prefill_tiny"):
         assert oracle.waste_fraction(lens) < 0.04
     if w.pool[0] == "factor":
         need = len(set(used))
@@ -147,3 +147,29 @@ def test_fp8_pool_codes():
         # N(0,1) in the pool's units: the spread comes back after scaling
         assert 0.8 < np.std(vals * scale) < 1.2
     assert b["query"].dtype == torch.float16
+
+
+@pytest.mark.parametrize("key", ["prefill_chunk", "prefill_gqa", "prefill_tiny"])
+def test_prefill_metadata(key):
+    """A prefill step's chunk: n new rows per sequence at positions L - n ..
+    L - 1, whose slots are in the sequence's blocks and empty before the
+    step; the prefix slots are live."""
+    w = wl.WORKLOADS[key]
+    md = wl.draw_metadata(w, w.default_seed)
+    qsl = md["query_start_loc"]
+    n = np.diff(qsl)
+    lens = md["context_lens"].astype(np.int64)
+    assert qsl[0] == 0 and (n >= 1).all() and (n <= lens).all() and n.max() <= w.max_query_len
+    assert len(md["slot_mapping"]) == qsl[-1]
+    live = md["live_slots"]
+    bt = md["block_tables"]
+    for s in range(w.num_seqs):
+        L, k = int(lens[s]), int(n[s])
+        slots = md["slot_mapping"][qsl[s]:qsl[s + 1]]
+        want = [bt[s, t // BS] * BS + t % BS for t in range(L - k, L)]
+        assert slots.tolist() == want
+        assert not live.reshape(-1)[slots].any()
+        prefix = [bt[s, t // BS] * BS + t % BS for t in range(L - k)]
+        assert live.reshape(-1)[prefix].all()
+    b = wl.make_batch(wl.WORKLOADS["prefill_tiny"], 5)
+    assert b["query"].shape[0] == b["query_start_loc"][-1] == b["key"].shape[0]
