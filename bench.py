@@ -15,7 +15,9 @@ with events on the launch stream; `cpu_baseline` times the float64 CPU
 oracle on a bounded sample of the same batch (single thread);
 `translation` times the same decode call on the same batch laid out with
 every sequence's blocks physically consecutive (identity block tables),
-against the random placement.
+against the random placement.  `prefill` times the prefill path (the
+chunk's reshape_and_cache, then paged_attention_prefill) on its own
+workloads, in TFLOP/s of causal attention against the MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b]
                     [--also long_gqa,llama13b_conv,sampling_cow,opt13b_fp8,long_gqa_fp8]
@@ -36,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, AMD's published figure
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_311_amd", "csrc", "paged_attention.hip")
@@ -50,6 +53,8 @@ def parse():
     ap.add_argument("--also",
                     default="long_gqa,llama13b_conv,sampling_cow,opt13b_fp8,long_gqa_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", default="prefill_chunk,prefill_gqa",
+                    help="prefill workloads to time ('' for none)")
     ap.add_argument("--no-translation", action="store_true",
                     help="skip the random vs contiguous placement comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -186,6 +191,72 @@ class Step:
         step_ms = t_start.elapsed_time(t_end) / steps
         dec = np.asarray([a.elapsed_time(c) for a, c in ev])
         return step_ms, dec, wall
+
+
+def prefill_flops(w, md):
+    """Causal attention flops of a prefill step: per new token and query
+    head, 2·D for each visible key in QK and 2·D in PV."""
+    qsl = np.asarray(md["query_start_loc"], np.int64)
+    lens = np.asarray(md["context_lens"], np.int64)
+    visible = 0
+    for s in range(len(lens)):
+        n, L = int(qsl[s + 1] - qsl[s]), int(lens[s])
+        visible += n * (L - n) + n * (n + 1) // 2
+    return 4 * w.head_size * w.num_heads * visible
+
+
+class PrefillStep:
+    """A prefill batch resident on the GPU: the chunk's cache writes, then
+    the attention (no allocation inside)."""
+
+    def __init__(self, w, seed):
+        import torch
+        import paged_kv_cache_311_amd as pkv
+        from paged_kv_cache_311_amd import workloads as wl
+        self.pkv, self.torch, self.w = pkv, torch, w
+        dev = "cuda:0"
+        b = wl.make_batch(w, seed, dev)
+        self.b = b
+        self.bt = torch.from_numpy(b["block_tables"]).to(dev)
+        self.cl = torch.from_numpy(b["context_lens"]).to(dev)
+        self.qsl = torch.from_numpy(b["query_start_loc"]).to(dev)
+        self.slots = torch.from_numpy(b["slot_mapping"]).to(dev)
+        self.out = torch.empty_like(b["query"])
+
+    def updates(self):
+        b = self.b
+        self.pkv.reshape_and_cache(b["key"], b["value"], self.slots, b["key_cache"],
+                                   b["value_cache"])
+
+    def decode(self):
+        b, w = self.b, self.w
+        self.pkv.paged_attention_prefill(self.out, b["query"], b["key_cache"], b["value_cache"],
+                                         self.bt, self.cl, self.qsl, float(w.scale),
+                                         w.num_kv_heads, w.max_query_len)
+
+    run = Step.run
+
+
+def measure_prefill(w, seed, steps, warmup):
+    st = PrefillStep(w, seed)
+    step_ms, call_ms, wall = st.run(steps, warmup)
+    fl = prefill_flops(w, st.b)
+    call_avg = float(call_ms.mean())
+    qsl = st.b["query_start_loc"]
+    return {
+        "workload": w.key, "seed": seed, "seqs": w.num_seqs, "heads": w.num_heads,
+        "kv_heads": w.num_kv_heads, "head_size": w.head_size, "dtype": w.dtype,
+        "new_tokens": int(qsl[-1]), "context_tokens": int(st.b["context_lens"].sum()),
+        "flops_per_step": fl, "ms_per_step": step_ms,
+        "prefill_call_ms_avg": call_avg, "prefill_call_ms_min": float(call_ms.min()),
+        "step_TFLOPs": fl / (step_ms * 1e-3) / 1e12,
+        "prefill_TFLOPs": fl / (call_avg * 1e-3) / 1e12,
+        "new_tokens_per_s": int(qsl[-1]) / (step_ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": round(fl / (call_avg * 1e-3) / 1e12, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fl / (call_avg * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)},
+        "host_wall_s": wall,
+    }
 
 
 def measure(w, seed, steps, warmup, ps):
@@ -378,6 +449,13 @@ def main():
         del st
         torch.cuda.empty_cache()
 
+    prefill = {}
+    for key in [k for k in a.prefill.split(",") if k]:
+        print(f"# measuring {key}", file=sys.stderr, flush=True)
+        pw = wl.WORKLOADS[key]
+        prefill[key] = measure_prefill(pw, pw.default_seed, a.steps, a.warmup)
+        torch.cuda.empty_cache()
+
     dec_ms = main_r["decode_call_ms_avg"]
     achieved = main_r["decode_GBps"]
     line = {
@@ -417,6 +495,7 @@ def main():
         "cpu_baseline": cpu,
         "translation": trans,
         "workloads": {w.key: main_r, **others},
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

@@ -24,9 +24,11 @@
 //               of 16 rows.  It walks the keys 32 at a time (two pool
 //               blocks), from token 0 to the last position its rows see.
 //   per step  = the 256 threads load the two blocks' K and V tiles
-//               (16-B chunks, through the table) into registers, then into
-//               one of two LDS buffers; the step after computes from that
-//               buffer while the next step's loads are in flight.
+//               (16-B chunks, a row's chunks on consecutive lanes) into
+//               registers, then into one of two LDS buffers (V transposed);
+//               the step after computes from that buffer while the next
+//               step's loads are in flight.  The table entries a step needs
+//               are read one step earlier than its tiles.
 //
 // Per step and wave (transposed products, so no operand needs a shuffle):
 //   S^T = K Q^T  MFMA 16x16x32: A = key rows from LDS as stored, B = the
@@ -36,16 +38,18 @@
 //                4 lanes (l, l^16, l^32, l^48); masked by select.
 //   O^T += V^T P^T  MFMA 16x16x32: B = the probabilities exactly as the
 //                QK left them (8 keys per lane: 4 of each block, the k
-//                order of both operands permuted alike), A = values read
-//                transposed from LDS (2-byte reads).  Lane l holds output
-//                dims 16j + 4(l/16) .. +3 of row l % 16, so the rescale by
-//                the row's running max and the final 1/sum are lane-local.
+//                order of both operands permuted alike), A = values from a
+//                transposed copy in LDS ([dim][token], written once per
+//                step by the loading threads), two 8-byte reads per lane.
+//                Lane l holds output dims 16j + 4(l/16) .. +3 of row
+//                l % 16, so the rescale by the row's running max and the
+//                final 1/sum are lane-local.
+//   Masking selects only on the steps that reach past a wave's earliest
+//   row; the rescale is skipped when no row's max moved.
 //
 // Precision: products accumulate in float32; the probabilities enter the
-// second product rounded to the input type (as the values are), and the
-// row sums are taken over the rounded probabilities, so the output is an
-// exact weighted mean of the values under weights perturbed by at most one
-// rounding each.
+// second product rounded to the input type (as the values are); the row
+// sums are float32.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -62,17 +66,49 @@ constexpr int kRB = 2;                      // 16-row blocks per wave
 constexpr int kRows = kWaves * kRB * 16;    // rows per workgroup
 constexpr int kKeys = 2 * kBlockSize;       // tokens per step (two pool blocks)
 
-// LDS: two buffers of K [32 tokens][D] and V [32 tokens][D], rows padded so
-// that the 16-lane groups of a 16-B key read and of a transposed 2-B value
-// read fall on distinct banks.
+// LDS: two buffers of K [32 tokens][D] and of V transposed [D][32 tokens],
+// rows padded so that the 16 lanes of a 16-B key read, and of an 8-B
+// value read, fall on distinct banks.
 template <int D>
 struct Lds {
-  static constexpr int kKS = D * 2 + 16;    // key row stride (bytes), 16-B aligned
-  static constexpr int kVS = D * 2 + 8;     // value row stride (bytes), 8-B aligned
+  static constexpr int kKS = D * 2 + 16;      // key row stride (bytes), 16-B aligned
+  static constexpr int kVS = kKeys * 2 + 8;   // transposed value row stride (bytes)
   static constexpr int kKBuf = kKeys * kKS;
-  static constexpr int kVBuf = kKeys * kVS;
+  static constexpr int kVBuf = D * kVS;
   static constexpr int kBytes = 2 * kKBuf + 2 * kVBuf;
 };
+
+// The value of lane l ^ 16 and of lane l ^ 32, combined with max / sum
+// across the four lanes l, l^16, l^32, l^48 (one row's lanes), through the
+// row-swapping permutes.
+__device__ __forceinline__ float max4rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)b[0]), __builtin_bit_cast(float, (int)b[1]));
+}
+__device__ __forceinline__ float sum4rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
+// Two floats rounded (nearest-even) to the 16-bit type, packed lo | hi << 16.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == PKV_F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, b2{(__bf16)lo, (__bf16)hi});
+  }
+}
 
 struct Params {
   void* out;
@@ -98,18 +134,6 @@ __device__ __forceinline__ floatx4 mfma32(const u32x4& a, const u32x4& b, const 
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Round a float to the 16-bit type and give its bits, and back (exact).
-template <int DT>
-__device__ __forceinline__ uint32_t to16(float x) {
-  return float_to_bits<DT>(x);
-}
-template <int DT>
-__device__ __forceinline__ float from16(uint32_t h) {
-  if constexpr (DT == PKV_F16)
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-  else
-    return float_of(h << 16);
-}
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params p) {
@@ -170,11 +194,22 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   }
 
   // cooperative tile loads: chunk c = tid + 256u is 16 B of token c / CPR
+  // of the step (a row's chunks on consecutive lanes).  The block ids a
+  // step needs are read from the table one step before its tiles are
+  // loaded, so the two reads never follow one another.
   const int64_t blk_bytes = (int64_t)p.num_kv_heads * kBlockSize * D * 2;
   const int64_t head_bytes = (int64_t)g * kBlockSize * D * 2;
   const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
   u32x4 kst[NCH], vst[NCH];
-  auto gload = [&](int step) {
+  int32_t ids[NCH], ids_next[NCH];
+  auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int t = step * kKeys + (tid + u * kThreads) / CPR;
+      dst[u] = table[t < Lc ? t / kBlockSize : 0];  // always a table entry
+    }
+  };
+  auto gload = [&](int step, const int32_t (&id)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
@@ -183,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       kst[u] = u32x4{0u, 0u, 0u, 0u};  // tokens past the context: zero
       vst[u] = u32x4{0u, 0u, 0u, 0u};
       if (t < Lc) {
-        int64_t b = table[t / kBlockSize];
+        int64_t b = id[u];
         b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
         const int64_t off = b * blk_bytes + head_bytes + (int64_t)(t % kBlockSize) * D * 2 +
                             (c - tk * CPR) * 16;
@@ -199,34 +234,43 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
       const int tk = c / CPR;
-      const int dc = c - tk * CPR;
-      store16(kb + tk * LD::kKS + dc * 16, kst[u]);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const uint32_t v0 = vst[u][0], v1 = vst[u][1], v2 = vst[u][2], v3 = vst[u][3];
-      *reinterpret_cast<u32x2*>(vb + tk * LD::kVS + dc * 16) = u32x2{v0, v1};
-      *reinterpret_cast<u32x2*>(vb + tk * LD::kVS + dc * 16 + 8) = u32x2{v2, v3};
+      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kst[u]);
+      const int d0 = (c - tk * CPR) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = vst[u][e / 2];
+        *reinterpret_cast<uint16_t*>(vb + (d0 + e) * LD::kVS + tk * 2) =
+            (uint16_t)((e & 1) ? word >> 16 : word & 0xffffu);
+      }
     }
   };
 
+  // running max in log2 units, floored at -1e30 so that a row with nothing
+  // visible yet keeps alpha = 1 and p = 0 (no infinity minus infinity)
   float m_run[kRB], l_run[kRB];
   floatx4 acc[kRB][NDB];
+  const float c2 = p.scale_log2;
+  const int wave_pos0 = base + min(R0 + w * kRB * 16, rows - 1) / G;  // earliest row of the wave
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    m_run[rb] = -INFINITY;
+    m_run[rb] = -1e30f;
     l_run[rb] = 0.f;
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
   if (nsteps > 0) {
-    gload(0);
+    read_ids(0, ids);
+    gload(0, ids);
+    read_ids(1, ids);
     lstore(0);
   }
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     const bool more = step + 1 < nsteps;
-    if (more) gload(step + 1);
+    read_ids(step + 2, ids_next);
+    if (more) gload(step + 1, ids);
     const char* kb = lds + buf * LD::kKBuf;
     const char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
 
@@ -244,70 +288,69 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       }
     }
 
-    // online softmax per row; probabilities packed as the B operand of PV
+    // online softmax per row; probabilities packed as the B operand of PV.
+    // Steps that end at or before the wave's earliest row need no mask.
+    const bool masked = step * kKeys + kKeys - 1 > wave_pos0;
     u32x4 pb[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       float x[8];
-      float mt = -INFINITY;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = step * kKeys + h * 16 + 4 * grp + i;
-          const float v = sc[rb][h][i] * p.scale_log2;
-          x[h * 4 + i] = (t <= pos[rb] && t < Lc) ? v : -INFINITY;
-          mt = fmaxf(mt, x[h * 4 + i]);
+        for (int i = 0; i < 4; ++i) x[h * 4 + i] = sc[rb][h][i];
+      }
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = step * kKeys + (e >> 2) * 16 + 4 * grp + (e & 3);
+          x[e] = t <= pos[rb] ? x[e] : -INFINITY;
         }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-      const float m_new = fmaxf(m_run[rb], mt);
-      const bool none = m_new == -INFINITY;  // nothing visible to this row yet
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+      float mt = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+      const float m_new = fmaxf(m_run[rb], max4rows(mt) * c2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
       m_run[rb] = m_new;
-      uint32_t hbits[8];
+      float pe[8];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = none ? 0.f : __builtin_amdgcn_exp2f(x[e] - m_new);
-        hbits[e] = to16<DT>(pe);
-        psum += from16<DT>(hbits[e]);
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_new));
+        psum += pe[e];
       }
-      l_run[rb] = l_run[rb] * alpha + psum;
+      l_run[rb] = fmaf(l_run[rb], alpha, psum);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-      for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
+        for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pb[rb][e] = hbits[2 * e] | (hbits[2 * e + 1] << 16);
+      for (int e = 0; e < 4; ++e) pb[rb][e] = pack2<DT>(pe[2 * e], pe[2 * e + 1]);
     }
 
     // O^T += V^T P^T, one 16-dim block at a time
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
-      uint32_t vh[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vh[h * 4 + i] = *reinterpret_cast<const uint16_t*>(
-              vb + (h * 16 + 4 * grp + i) * LD::kVS + (16 * j + col) * 2);
-      }
-      const u32x4 a = {vh[0] | (vh[1] << 16), vh[2] | (vh[3] << 16), vh[4] | (vh[5] << 16),
-                       vh[6] | (vh[7] << 16)};
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const char* vrow = vb + (16 * j + col) * LD::kVS + 8 * grp;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32);
+      const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(a, pb[rb], acc[rb][j]);
     }
 
     if (more) lstore(buf ^ 1);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
     __syncthreads();
   }
 
   // normalize and store: lane l holds dims 16j + 4(l/16) .. +3 of its row
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    float l = l_run[rb];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    const float l = sum4rows(l_run[rb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (row_ok[rb]) {
       char* dst = (char*)p.out + (row_off[rb] + 4 * grp) * 2;
@@ -316,8 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const floatx4 o = acc[rb][j];
         const float o0 = o[0] * inv, o1 = o[1] * inv, o2 = o[2] * inv, o3 = o[3] * inv;
-        *reinterpret_cast<u32x2*>(dst + 16 * j * 2) =
-            u32x2{to16<DT>(o0) | (to16<DT>(o1) << 16), to16<DT>(o2) | (to16<DT>(o3) << 16)};
+        *reinterpret_cast<u32x2*>(dst + 16 * j * 2) = u32x2{pack2<DT>(o0, o1), pack2<DT>(o2, o3)};
       }
     }
   }
