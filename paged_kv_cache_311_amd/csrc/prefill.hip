@@ -200,7 +200,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   const int64_t blk_bytes = (int64_t)p.num_kv_heads * kBlockSize * D * 2;
   const int64_t head_bytes = (int64_t)g * kBlockSize * D * 2;
   const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
-  u32x4 kst[NCH], vst[NCH];
+  struct Stage {
+    u32x4 k[NCH], v[NCH];
+  };
   int32_t ids[NCH], ids_next[NCH];
   auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
 #pragma unroll
@@ -209,36 +211,40 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       dst[u] = table[t < Lc ? t / kBlockSize : 0];  // always a table entry
     }
   };
-  auto gload = [&](int step, const int32_t (&id)[NCH]) {
+  // Loads are issued for every step, also past the last one (then of the
+  // sequence's first block: every address stays in the pool), so the
+  // compiler's count of loads in flight is the same on every path; tokens
+  // past the context are zeroed when the stage is stored.
+  auto gload = [&](Stage& st, int step, const int32_t (&id)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
       const int tk = c / CPR;
       const int t = step * kKeys + tk;
-      kst[u] = u32x4{0u, 0u, 0u, 0u};  // tokens past the context: zero
-      vst[u] = u32x4{0u, 0u, 0u, 0u};
-      if (t < Lc) {
-        int64_t b = id[u];
-        b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
-        const int64_t off = b * blk_bytes + head_bytes + (int64_t)(t % kBlockSize) * D * 2 +
-                            (c - tk * CPR) * 16;
-        kst[u] = load16(p.kcache + off);
-        vst[u] = load16(p.vcache + off);
-      }
+      int64_t b = id[u];
+      b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
+      const int64_t off = b * blk_bytes + head_bytes + (int64_t)(t % kBlockSize) * D * 2 +
+                          (c - tk * CPR) * 16;
+      st.k[u] = load16(p.kcache + off);
+      st.v[u] = load16(p.vcache + off);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const Stage& st, int buf, int step) {
     char* kb = lds + buf * LD::kKBuf;
     char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
       const int tk = c / CPR;
-      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kst[u]);
+      const bool live = step * kKeys + tk < Lc;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 kv = live ? st.k[u] : z;
+      const u32x4 vv = live ? st.v[u] : z;
+      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kv);
       const int d0 = (c - tk * CPR) * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t word = vst[u][e / 2];
+        const uint32_t word = vv[e / 2];
         *reinterpret_cast<uint16_t*>(vb + (d0 + e) * LD::kVS + tk * 2) =
             (uint16_t)((e & 1) ? word >> 16 : word & 0xffffu);
       }
@@ -259,22 +265,28 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     for (int j = 0; j < NDB; ++j) acc[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (nsteps > 0) {
-    read_ids(0, ids);
-    gload(0, ids);
-    read_ids(1, ids);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
+  // Three steps in flight: while step s is computed from LDS buffer s % 2,
+  // the tiles of step s + 1 sit in one register stage (stored to the other
+  // buffer after the compute) and those of step s + 2 arrive in the other
+  // stage.  The body is written once and run with the two stages swapped.
+  Stage sa, sb;
+  auto body = [&](int step, Stage& fill, const Stage& ready) __attribute__((always_inline)) {
     const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    read_ids(step + 2, ids_next);
-    if (more) gload(step + 1, ids);
+    read_ids(step + 3, ids_next);
+    gload(fill, step + 2, ids);
     const char* kb = lds + buf * LD::kKBuf;
     const char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
 
-    // S^T for both key blocks and both row blocks
+    // S^T for both key blocks and both row blocks: all key operands are
+    // read from LDS first, so their latencies overlap
+    u32x4 ka[2][NKS];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int m = 0; m < NKS; ++m)
+        ka[h][m] = load16(kb + (h * 16 + col) * LD::kKS + (32 * m + 8 * grp) * 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     floatx4 sc[kRB][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -282,11 +294,22 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < NKS; ++m) {
-        const u32x4 a = load16(kb + (h * 16 + col) * LD::kKS + (32 * m + 8 * grp) * 2);
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = mfma32<DT>(a, q[rb][m], sc[rb][h]);
+        for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = mfma32<DT>(ka[h][m], q[rb][m], sc[rb][h]);
       }
     }
+
+    // the value operands of this step, read while the softmax runs
+    u32x4 va[NDB];
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const char* vrow = vb + (16 * j + col) * LD::kVS + 8 * grp;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32);
+      va[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // online softmax per row; probabilities packed as the B operand of PV.
     // Steps that end at or before the wave's earliest row need no mask.
@@ -332,19 +355,28 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     // O^T += V^T P^T, one 16-dim block at a time
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const char* vrow = vb + (16 * j + col) * LD::kVS + 8 * grp;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32);
-      const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(a, pb[rb], acc[rb][j]);
+      for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
     }
 
-    if (more) lstore(buf ^ 1);
+    if (step + 1 < nsteps) lstore(ready, buf ^ 1, step + 1);
 #pragma unroll
     for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
     __syncthreads();
+  };
+
+  if (nsteps > 0) {
+    read_ids(0, ids);
+    gload(sa, 0, ids);
+    read_ids(1, ids);
+    gload(sb, 1, ids);
+    read_ids(2, ids);
+    lstore(sa, 0, 0);
+  }
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    body(step, sa, sb);
+    if (step + 1 < nsteps) body(step + 1, sb, sa);
   }
 
   // normalize and store: lane l holds dims 16j + 4(l/16) .. +3 of its row
