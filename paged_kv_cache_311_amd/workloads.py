@@ -27,6 +27,12 @@ sampling over a shared prompt, long contexts):
   opt13b_fp8,    the same shapes and lengths with pools of OCP E4M3 codes
   long_gqa_fp8   and one scale per pool (keys 1/64, values 3/128); queries,
                  outputs and new tokens stay fp16 / bf16.
+  beam           beam search: 16 requests x 4 beams, 40 heads of 128, fp16,
+                 prompts U{256..1024} shared by their beams; 24 steps of
+                 appends (copy-on-write of shared partial blocks) with beams
+                 dying and survivors forking in their place, then one more
+                 append of every beam (its copy_blocks pairs and slots) and
+                 the decode.
   prefill_chunk  chunked prefill: 16 seqs, 40 heads of 128, fp16, a cached
                  prefix of U{0..1536} tokens and a new chunk of 512 tokens
                  each (written by reshape_and_cache, then attended).
@@ -71,7 +77,7 @@ class Workload:
     dtype: str              # "f32" | "f16" | "bf16"
     lengths: tuple          # see draw_context_lens
     pool: tuple             # ("blocks", n) | ("factor", f)
-    step: str               # "decode" | "append" | "cow" | "prefill"
+    step: str               # "decode" | "append" | "cow" | "beam" | "prefill"
     max_len: int            # longest possible context (sets the table width)
     partition_size: int = 0   # cap on tokens per piece of a split context (0: none)
     prompts: int = 0
@@ -131,6 +137,8 @@ WORKLOADS = {
         Workload("long_gqa_fp8", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
                  ("factor", 1.25), "decode", 32768, kv_dtype="e4m3",
                  k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE),
+        Workload("beam", 11, 64, 40, 40, 128, "f16", ("beam", 256, 1024, 24),
+                 ("factor", 1.25), "beam", 1056, prompts=16, samples=4),
         Workload("prefill_chunk", 8, 16, 40, 40, 128, "f16", ("prefill", 0, 1536, 512, 512),
                  ("factor", 1.25), "prefill", 2048),
         Workload("prefill_gqa", 9, 8, 32, 8, 128, "bf16", ("prefill", 0, 0, 2048, 2048),
@@ -358,6 +366,59 @@ def draw_metadata(w, seed):
         md["cow_pairs"] = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
         md["shared_blocks"] = int((mgr.ref > 1).sum())
         md["prompt_lens"] = P.astype(np.int64)
+        return md
+
+    if w.step == "beam":
+        # beam search: each request's beams share its prompt; every step each
+        # beam appends a token (copying a shared partial last block first),
+        # and between steps some beams die and surviving ones fork to take
+        # their place.  The state after `history` such steps is cached; the
+        # step drawn here is one more append of every beam.
+        plo, phi, history = w.lengths[1:]
+        R, B = w.prompts, w.samples
+        P = rng.integers(plo, phi + 1, size=R)
+        need = int(sum(-(-int(p) // bs) for p in P)) + R * B * (history + 2)
+        nb = _pool_blocks(w, need)
+        mgr = BlockManager(nb, rng)
+        beams = []  # (request, table, length)
+        for i in range(R):
+            prompt = mgr.allocate_for(int(P[i]))
+            beams.extend((i, mgr.fork(prompt), int(P[i])) for _ in range(B))
+            mgr.release(prompt)
+        forks = kills = 0
+        for step in range(history):
+            for k, (i, t, L) in enumerate(beams):
+                mgr.append_slot(t, L)
+                beams[k] = (i, t, L + 1)
+            for i in range(R):  # some beams die, survivors fork in their place
+                mine = [k for k, b in enumerate(beams) if b[0] == i]
+                dead = rng.choice(mine, size=int(rng.integers(0, B // 2 + 1)), replace=False)
+                alive = [k for k in mine if k not in set(dead.tolist())]
+                for k in dead:
+                    mgr.release(beams[k][1])
+                    src = beams[int(rng.choice(alive))]
+                    beams[k] = (i, mgr.fork(src[1]), src[2])
+                    forks += 1
+                    kills += 1
+        tables = [t for _, t, _ in beams]
+        lens = [L for _, _, L in beams]
+        live = _live_slot_mask(nb, tables, lens)
+        slots, pairs = [], []
+        for k, (i, t, L) in enumerate(beams):
+            slot, pair = mgr.append_slot(t, L)
+            if pair is not None:
+                pairs.append(pair)
+            slots.append(slot)
+        md["context_lens"] = np.asarray([L + 1 for L in lens], dtype=np.int32)
+        md["block_tables"] = _table_array(tables, w.table_width)
+        md["num_blocks"] = nb
+        md["live_slots"] = live
+        md["slot_mapping"] = np.asarray(slots, dtype=np.int64)
+        md["token_seq"] = np.arange(len(beams), dtype=np.int64)
+        md["cow_pairs"] = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+        md["shared_blocks"] = int((mgr.ref > 1).sum())
+        md["prompt_lens"] = P.astype(np.int64)
+        md["forks"] = forks
         return md
     raise ValueError(w.step)
 

@@ -28,6 +28,7 @@ REDUCED = {
     "llama13b_conv": dict(num_seqs=24),
     "sampling_cow": dict(num_seqs=16, prompts=2),
     "long_gqa": dict(num_seqs=2),
+    "beam": dict(num_seqs=12, prompts=3, lengths=("beam", 64, 300, 12)),
 }
 
 
@@ -45,7 +46,7 @@ def test_reduced_workload_every_output(gpu_lib, key, si):
     full_step_and_check(b)
 
 
-@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa"])
+@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa", "beam"])
 def test_full_size_sampled(gpu_lib, key):
     """Full workload, launch configuration of the benchmark, oracle on a sample."""
     w = W[key]

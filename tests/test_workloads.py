@@ -27,8 +27,8 @@ def test_metadata_invariants(key):
         assert (row[n:] == -1).all()
         used.extend(row[:n].tolist())
     counts = np.bincount(np.asarray(used), minlength=nb)
-    if w.step == "cow":
-        # only prompt blocks are shared, each by at most `samples` sequences
+    if w.step in ("cow", "beam"):
+        # blocks are shared only among one prompt's samples / beams
         assert counts.max() <= w.samples
         assert (counts > 1).sum() == md["shared_blocks"]
     else:
@@ -40,7 +40,7 @@ def test_metadata_invariants(key):
         assert oracle.waste_fraction(lens) < 0.04
     if w.pool[0] == "factor":
         need = len(set(used))
-        assert nb == int(np.ceil(w.pool[1] * need)) or w.step == "cow"
+        assert nb == int(np.ceil(w.pool[1] * need)) or w.step in ("cow", "beam")
 
 
 def test_tiny_pool_and_lengths():
@@ -173,3 +173,27 @@ def test_prefill_metadata(key):
         assert live.reshape(-1)[prefix].all()
     b = wl.make_batch(wl.WORKLOADS["prefill_tiny"], 5)
     assert b["query"].shape[0] == b["query_start_loc"][-1] == b["key"].shape[0]
+
+
+def test_beam_step_copies_shared_partial_blocks():
+    """The beam workload's step: every beam appends one token; a pair is
+    drawn exactly where a beam's last block was shared and partly filled,
+    its destination is that beam's own block now, and the new token lands
+    in it.  Beams of one request share their prompt's full blocks."""
+    w = wl.WORKLOADS["beam"]
+    md = wl.draw_metadata(w, w.default_seed)
+    bt, lens, slots = md["block_tables"], md["context_lens"], md["slot_mapping"]
+    assert len(slots) == w.num_seqs == w.prompts * w.samples
+    assert md["forks"] > 0 and len(md["cow_pairs"]) > 0
+    refs = np.bincount(bt[bt >= 0], minlength=md["num_blocks"])
+    dsts = {int(d): int(sv) for sv, d in md["cow_pairs"]}
+    for s_ in range(w.num_seqs):
+        L = int(lens[s_])
+        last = int(bt[s_, (L - 1) // BS])
+        assert slots[s_] == last * BS + (L - 1) % BS
+        if last in dsts:
+            assert refs[last] == 1 and (L - 1) % BS != 0
+            assert md["live_slots"][dsts[last], :(L - 1) % BS].all()
+    # the first prompt block of a request is shared by all its beams
+    first = bt[:, 0].reshape(w.prompts, w.samples)
+    assert (first == first[:, :1]).all()
