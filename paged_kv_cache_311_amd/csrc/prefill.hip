@@ -45,7 +45,8 @@
 //                l % 16, so the rescale by the row's running max and the
 //                final 1/sum are lane-local.
 //   Masking selects only on the steps that reach past a wave's earliest
-//   row; the rescale is skipped when no row's max moved.
+//   row.  A row's max is raised only when a step's exceeds it by 2^8 (so
+//   probabilities stay below 256) and the rescale then runs for the wave.
 //
 // Precision: products accumulate in float32; the probabilities enter the
 // second product rounded to the input type (as the values are); the row
@@ -65,6 +66,10 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kRB = 2;                      // 16-row blocks per wave
 constexpr int kRows = kWaves * kRB * 16;    // rows per workgroup
 constexpr int kKeys = 2 * kBlockSize;       // tokens per step (two pool blocks)
+// A row's running max is raised only when a step's max exceeds it by more
+// than this (log2 units); probabilities then stay below 2^kSlack and the
+// accumulator is rescaled rarely.
+constexpr float kSlack = 8.f;
 
 // LDS: two buffers of K [32 tokens][D] and of V transposed [D][32 tokens],
 // rows padded so that the 16 lanes of a 16-B key read, and of an 8-B
@@ -203,28 +208,34 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   struct Stage {
     u32x4 k[NCH], v[NCH];
   };
+  // per chunk: which of the step's two blocks, and the byte offset inside
+  // the block of this kv head's tile (both fixed for the thread)
+  int blk_u[NCH];
+  int64_t in_blk[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int c = tid + u * kThreads;
+    const int tk = c / CPR;
+    blk_u[u] = tk / kBlockSize;
+    in_blk[u] = head_bytes + (int64_t)(tk % kBlockSize) * D * 2 + (c - tk * CPR) * 16;
+  }
+  const int last_blk = Lc > 0 ? (Lc - 1) / kBlockSize : 0;
   int32_t ids[NCH], ids_next[NCH];
   auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int t = step * kKeys + (tid + u * kThreads) / CPR;
-      dst[u] = table[t < Lc ? t / kBlockSize : 0];  // always a table entry
-    }
+    for (int u = 0; u < NCH; ++u)  // always a table entry of the context
+      dst[u] = table[min(step * 2 + blk_u[u], last_blk)];
   };
   // Loads are issued for every step, also past the last one (then of the
   // sequence's first block: every address stays in the pool), so the
   // compiler's count of loads in flight is the same on every path; tokens
   // past the context are zeroed when the stage is stored.
-  auto gload = [&](Stage& st, int step, const int32_t (&id)[NCH]) {
+  const int max_blk = (int)(p.num_blocks - 1);
+  auto gload = [&](Stage& st, const int32_t (&id)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int c = tid + u * kThreads;
-      const int tk = c / CPR;
-      const int t = step * kKeys + tk;
-      int64_t b = id[u];
-      b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
-      const int64_t off = b * blk_bytes + head_bytes + (int64_t)(t % kBlockSize) * D * 2 +
-                          (c - tk * CPR) * 16;
+      const int b = min(max(id[u], 0), max_blk);  // clamped into the pool
+      const int64_t off = (int64_t)b * blk_bytes + in_blk[u];
       st.k[u] = load16(p.kcache + off);
       st.v[u] = load16(p.vcache + off);
     }
@@ -236,10 +247,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
       const int tk = c / CPR;
-      const bool live = step * kKeys + tk < Lc;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 kv = live ? st.k[u] : z;
-      const u32x4 vv = live ? st.v[u] : z;
+      u32x4 kv = st.k[u], vv = st.v[u];
+      if (step * kKeys + kKeys > Lc) {  // the context's last step (uniform)
+        if (step * kKeys + tk >= Lc) {  // tokens past the context: zeros
+          kv = u32x4{0u, 0u, 0u, 0u};
+          vv = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
       store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kv);
       const int d0 = (c - tk * CPR) * 8;
 #pragma unroll
@@ -273,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   auto body = [&](int step, Stage& fill, const Stage& ready) __attribute__((always_inline)) {
     const int buf = step & 1;
     read_ids(step + 3, ids_next);
-    gload(fill, step + 2, ids);
+    gload(fill, ids);
     const char* kb = lds + buf * LD::kKBuf;
     const char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
 
@@ -333,21 +347,24 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       float mt = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      const float m_new = fmaxf(m_run[rb], max4rows(mt) * c2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-      m_run[rb] = m_new;
+      const float m_tile = max4rows(mt) * c2;
+      const bool grow = m_tile > m_run[rb] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // some row of the wave: rescale it
+        const float m_new = grow ? m_tile : m_run[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
+      }
       float pe[8];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_new));
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_run[rb]));
         psum += pe[e];
       }
-      l_run[rb] = fmaf(l_run[rb], alpha, psum);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
-      }
+      l_run[rb] += psum;
 #pragma unroll
       for (int e = 0; e < 4; ++e) pb[rb][e] = pack2<DT>(pe[2 * e], pe[2 * e + 1]);
     }
@@ -367,9 +384,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 
   if (nsteps > 0) {
     read_ids(0, ids);
-    gload(sa, 0, ids);
+    gload(sa, ids);
     read_ids(1, ids);
-    gload(sb, 1, ids);
+    gload(sb, ids);
     read_ids(2, ids);
     lstore(sa, 0, 0);
   }
