@@ -17,6 +17,8 @@
 // a dense contraction and runs on MFMA.
 //
 // Work decomposition
+//   placement = every (sequence, kv head)'s row tiles on one XCD, in a run,
+//               so they share its keys and values in that XCD's L2.
 //   rows      = (new token, query head of the group) pairs of one
 //               (sequence, kv head), token-major: row r is token r / G,
 //               head r % G of the group (G = Hq / Hkv).
@@ -66,6 +68,13 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kRB = 2;                      // 16-row blocks per wave
 constexpr int kRows = kWaves * kRB * 16;    // rows per workgroup
 constexpr int kKeys = 2 * kBlockSize;       // tokens per step (two pool blocks)
+constexpr int kXcds = 8;                    // accelerator dies (each with its own L2)
+// Pairs interleaved per XCD bundle: about 64 row tiles' worth, at least 4
+// pairs (measured on one MI355X: 16 pairs of 4 tiles beat both a
+// one-pair-at-a-time order and a whole-XCD interleave by 13%; with 64 tiles
+// per pair, 4 pairs beat 1 by 7%).
+constexpr int kBundleTiles = 64;
+constexpr int kMinBundle = 4;
 // A row's running max is raised only when a step's max exceeds it by more
 // than this (log2 units); probabilities then stay below 2^kSlack and the
 // accumulator is rescaled rarely.
@@ -127,6 +136,7 @@ struct Params {
   int num_seqs, num_heads, num_kv_heads, max_blocks;
   int64_t num_blocks;
   int row_tiles;     // 128-row tiles per (sequence, kv head) the grid covers
+  int bundle;        // (sequence, kv head) pairs interleaved on an XCD
 };
 
 template <int DT>
@@ -150,11 +160,20 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   static_assert(NCH * kThreads == kKeys * CPR, "whole chunks per thread");
   __shared__ __attribute__((aligned(16))) char lds[LD::kBytes];
 
-  // workgroup -> (row tile, sequence, kv head); the latest (heaviest) row
-  // tiles of every (sequence, kv head) are dispatched first
-  const int per_tile = p.num_seqs * p.num_kv_heads;
-  const int rank = blockIdx.x / per_tile;
-  const int sg = blockIdx.x - rank * per_tile;
+  // workgroup -> (sequence, kv head, row tile).  Workgroups are dealt to
+  // the 8 XCDs round-robin; every (sequence, kv head) belongs to one XCD.
+  // On an XCD, its pairs are taken `bundle` at a time, and within a bundle
+  // the row tiles go out latest (heaviest) first across its pairs: the
+  // tiles that run together share their keys and values in that XCD's L2,
+  // and the longest ones start first.
+  const int xcd = blockIdx.x & (kXcds - 1);
+  const int k = blockIdx.x / kXcds;
+  const int per_bundle = p.bundle * p.row_tiles;
+  const int bdl = k / per_bundle;
+  const int in_b = k - bdl * per_bundle;
+  const int rank = in_b / p.bundle;
+  const int sg = ((bdl * p.bundle + (in_b - rank * p.bundle)) * kXcds) + xcd;
+  if (sg >= p.num_seqs * p.num_kv_heads) return;  // padding of the grid
   const int s = sg / p.num_kv_heads;
   const int g = sg - s * p.num_kv_heads;
   const int tile = p.row_tiles - 1 - rank;
@@ -449,7 +468,12 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
   if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
   const int64_t rows = (int64_t)max_query_len * (num_heads / num_kv_heads);
   const int64_t row_tiles = (rows + kRows - 1) / kRows;
-  const int64_t grid = row_tiles * num_seqs * num_kv_heads;
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  const int64_t per_xcd = (pairs + kXcds - 1) / kXcds;
+  int64_t bundle = kBundleTiles / row_tiles;
+  bundle = bundle < kMinBundle ? kMinBundle : bundle;
+  bundle = bundle > per_xcd ? per_xcd : bundle;
+  const int64_t grid = row_tiles * ((per_xcd + bundle - 1) / bundle) * bundle * kXcds;
   if (row_tiles > INT32_MAX || grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
   if ((int64_t)max_query_len * num_heads > INT32_MAX / 2) return PKV_ERR_INVALID_ARG;
   Params a;
@@ -467,6 +491,7 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.row_tiles = (int)row_tiles;
+  a.bundle = (int)bundle;
   (void)hipGetLastError();
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
