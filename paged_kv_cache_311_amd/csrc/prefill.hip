@@ -27,7 +27,7 @@
 //               blocks), from token 0 to the last position its rows see.
 //   per step  = the 256 threads load the two blocks' K and V tiles
 //               (16-B chunks, a row's chunks on consecutive lanes) into
-//               registers, then into one of two LDS buffers (V transposed);
+//               registers, then into one of two LDS buffers;
 //               the step after computes from that buffer while the next
 //               step's loads are in flight.  The table entries a step needs
 //               are read one step earlier than its tiles.
@@ -40,9 +40,9 @@
 //                4 lanes (l, l^16, l^32, l^48); masked by select.
 //   O^T += V^T P^T  MFMA 16x16x32: B = the probabilities exactly as the
 //                QK left them (8 keys per lane: 4 of each block, the k
-//                order of both operands permuted alike), A = values from a
-//                transposed copy in LDS ([dim][token], written once per
-//                step by the loading threads), two 8-byte reads per lane.
+//                order of both operands permuted alike), A = values read
+//                from LDS rows with the transposing 8-byte read, two per
+//                lane and 16-dim block.
 //                Lane l holds output dims 16j + 4(l/16) .. +3 of row
 //                l % 16, so the rescale by the row's running max and the
 //                final 1/sum are lane-local.
@@ -80,17 +80,29 @@ constexpr int kMinBundle = 4;
 // accumulator is rescaled rarely.
 constexpr float kSlack = 8.f;
 
-// LDS: two buffers of K [32 tokens][D] and of V transposed [D][32 tokens],
-// rows padded so that the 16 lanes of a 16-B key read, and of an 8-B
-// value read, fall on distinct banks.
+// LDS: two buffers of K [32 tokens][D] and V [32 tokens][D], rows padded
+// so that the 16 lanes of a 16-B key read, and the four rows of a
+// transposing value read, fall on distinct banks.
 template <int D>
 struct Lds {
   static constexpr int kKS = D * 2 + 16;      // key row stride (bytes), 16-B aligned
-  static constexpr int kVS = kKeys * 2 + 8;   // transposed value row stride (bytes)
+  static constexpr int kVS = D * 2 + 32;      // value row stride: 4 rows on distinct banks
   static constexpr int kKBuf = kKeys * kKS;
-  static constexpr int kVBuf = D * kVS;
+  static constexpr int kVBuf = kKeys * kVS;
   static constexpr int kBytes = 2 * kKBuf + 2 * kVBuf;
 };
+
+// Four 16-bit elements of one column from four rows, through the gfx950
+// transposing LDS read.  In each group of 16 lanes, lane a + 4e passes the
+// address of 4 consecutive elements of row e (columns 4a .. 4a+3); lane
+// 4a + b then receives column 4a + b of rows 0..3 (checked on the GPU).
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr16(const char* lds_addr) {
+  const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(lds_addr));
+  return uint2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+               (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
+}
 
 // The value of lane l ^ 16 and of lane l ^ 32, combined with max / sum
 // across the four lanes l, l^16, l^32, l^48 (one row's lanes), through the
@@ -274,13 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
         }
       }
       store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kv);
-      const int d0 = (c - tk * CPR) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = vv[e / 2];
-        *reinterpret_cast<uint16_t*>(vb + (d0 + e) * LD::kVS + tk * 2) =
-            (uint16_t)((e & 1) ? word >> 16 : word & 0xffffu);
-      }
+      store16(vb + tk * LD::kVS + (c - tk * CPR) * 16, vv);
     }
   };
 
@@ -332,15 +338,16 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       }
     }
 
-    // the value operands of this step, read while the softmax runs
+    // the value operands of this step, read transposed while the softmax
+    // runs: lane l gets dim 16j + l % 16 of tokens 4(l/16) + 0..3 of each
+    // block (the probabilities' k order)
     u32x4 va[NDB];
+    const char* vsrc = vb + (4 * grp + (col >> 2)) * LD::kVS + (col & 3) * 8;
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const char* vrow = vb + (16 * j + col) * LD::kVS + 8 * grp;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32);
-      va[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      const uint2 lo = read_tr16(vsrc + 32 * j);
+      const uint2 hi = read_tr16(vsrc + 16 * LD::kVS + 32 * j);
+      va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
     __builtin_amdgcn_sched_barrier(0);
 
