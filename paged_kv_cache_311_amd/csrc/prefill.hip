@@ -239,54 +239,60 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   struct Stage {
     u32x4 k[NCH], v[NCH];
   };
-  // per chunk: which of the step's two blocks, and the byte offset inside
-  // the block of this kv head's tile (both fixed for the thread)
-  int blk_u[NCH];
-  int64_t in_blk[NCH];
+  // per chunk: its token within a step and the byte offset, inside a
+  // block, of this kv head's row chunk (both fixed for the thread)
+  int tk_u[NCH];
+  uint32_t in_blk[NCH];
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const int c = tid + u * kThreads;
-    const int tk = c / CPR;
-    blk_u[u] = tk / kBlockSize;
-    in_blk[u] = head_bytes + (int64_t)(tk % kBlockSize) * D * 2 + (c - tk * CPR) * 16;
+    tk_u[u] = c / CPR;
+    in_blk[u] = (uint32_t)(head_bytes + (tk_u[u] % kBlockSize) * D * 2 + (c - tk_u[u] * CPR) * 16);
   }
-  const int last_blk = Lc > 0 ? (Lc - 1) / kBlockSize : 0;
+  // Tokens past the context are read from the sequence's first block
+  // instead (same row): from the second step on, the context holds more
+  // than 32 tokens, so that block is full of cached tokens, whose values
+  // the zero probabilities of masked tokens then multiply.  The first step
+  // is stored with explicit zeros past the context.
   int32_t ids[NCH], ids_next[NCH];
   auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
 #pragma unroll
-    for (int u = 0; u < NCH; ++u)  // always a table entry of the context
-      dst[u] = table[min(step * 2 + blk_u[u], last_blk)];
+    for (int u = 0; u < NCH; ++u) {
+      const int t = step * kKeys + tk_u[u];
+      dst[u] = table[t < Lc ? t / kBlockSize : 0];  // always a table entry of the context
+    }
   };
-  // Loads are issued for every step, also past the last one (then of the
-  // sequence's first block: every address stays in the pool), so the
-  // compiler's count of loads in flight is the same on every path; tokens
-  // past the context are zeroed when the stage is stored.
+  // Loads are issued for every step, also past the last one, so the
+  // compiler's count of loads in flight is the same on every path.
   const int max_blk = (int)(p.num_blocks - 1);
+  const uint32_t blk_bytes32 = (uint32_t)blk_bytes;  // below 2^32 (checked at launch)
   auto gload = [&](Stage& st, const int32_t (&id)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int b = min(max(id[u], 0), max_blk);  // clamped into the pool
-      const int64_t off = (int64_t)b * blk_bytes + in_blk[u];
+      const uint32_t b = (uint32_t)min(max(id[u], 0), max_blk);  // clamped into the pool
+      const uint64_t off = (uint64_t)b * blk_bytes32 + in_blk[u];
       st.k[u] = load16(p.kcache + off);
       st.v[u] = load16(p.vcache + off);
     }
   };
-  auto lstore = [&](const Stage& st, int buf, int step) {
+  auto lstore = [&](const Stage& st, int buf) {
     char* kb = lds + buf * LD::kKBuf;
     char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
       const int tk = c / CPR;
-      u32x4 kv = st.k[u], vv = st.v[u];
-      if (step * kKeys + kKeys > Lc) {  // the context's last step (uniform)
-        if (step * kKeys + tk >= Lc) {  // tokens past the context: zeros
-          kv = u32x4{0u, 0u, 0u, 0u};
-          vv = u32x4{0u, 0u, 0u, 0u};
-        }
+      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, st.k[u]);
+      store16(vb + tk * LD::kVS + (c - tk * CPR) * 16, st.v[u]);
+    }
+  };
+  auto zero_tail = [&](Stage& st) {  // first step: tokens past the context
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      if (tk_u[u] >= Lc) {
+        st.k[u] = u32x4{0u, 0u, 0u, 0u};
+        st.v[u] = u32x4{0u, 0u, 0u, 0u};
       }
-      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kv);
-      store16(vb + tk * LD::kVS + (c - tk * CPR) * 16, vv);
     }
   };
 
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
     }
 
-    if (step + 1 < nsteps) lstore(ready, buf ^ 1, step + 1);
+    if (step + 1 < nsteps) lstore(ready, buf ^ 1);
 #pragma unroll
     for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
     __syncthreads();
@@ -414,7 +420,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     read_ids(1, ids);
     gload(sb, ids);
     read_ids(2, ids);
-    lstore(sa, 0, 0);
+    zero_tail(sa);
+    lstore(sa, 0);
   }
   __syncthreads();
   for (int step = 0; step < nsteps; step += 2) {
@@ -483,6 +490,8 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
   const int64_t grid = row_tiles * ((per_xcd + bundle - 1) / bundle) * bundle * kXcds;
   if (row_tiles > INT32_MAX || grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
   if ((int64_t)max_query_len * num_heads > INT32_MAX / 2) return PKV_ERR_INVALID_ARG;
+  if ((int64_t)num_kv_heads * kBlockSize * head_size * 2 > (int64_t)UINT32_MAX)
+    return PKV_ERR_INVALID_ARG;  // bytes of one block, all kv heads
   Params a;
   a.out = out;
   a.query = (const char*)query;
