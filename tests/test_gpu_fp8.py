@@ -199,3 +199,24 @@ def test_fp8_scale_validation_raises(gpu_lib):
                                            dev_i32(b["block_tables"]),
                                            dev_i32(b["context_lens"]), float(w.scale), ks, vs,
                                            w.num_kv_heads)
+
+
+def test_fp8_workspace_reused_and_many_sequences(gpu_lib):
+    """One workspace serves E4M3 and 16-bit calls of different shapes in
+    turn; more than 2048 sequences run as several launches."""
+    w1 = fp8_variant("opt13b", num_seqs=8)
+    w2 = wl.custom(np.full(2100, 3), 4, 4, 64, "f16", max_len=16, partition_size=0, **ODD)
+    ws = torch.zeros(max(pkv.workspace_bytes(8, 40, 40, 128, 128),
+                         pkv.workspace_bytes(2100, 4, 4, 64, 1)), dtype=torch.uint8, device=DEV)
+    for w, seed in ((w1, 1), (w2, 2), (w1, 3)):
+        b = wl.make_batch(w, seed, DEV)
+        kc0, vc0 = clone_pools(b)
+        out = torch.empty_like(b["query"])
+        pkv.paged_attention_decode_fp8(out, b["query"], b["key_cache"], b["value_cache"],
+                                       dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
+                                       float(w.scale), w.k_scale, w.v_scale, w.num_kv_heads,
+                                       workspace=ws)
+        torch.cuda.synchronize()
+        seqs = list(range(w.num_seqs)) if w.num_seqs <= 64 else [0, 1, 2047, 2048, 2099]
+        ref = oracle_decode_subset(b, kc0, vc0, seqs)
+        assert_close(out[seqs], ref, w.dtype, f"e4m3 reuse {w.key} seed {seed}")

@@ -147,3 +147,59 @@ def test_prefill_rejects_bad_arguments(gpu_lib):
     with pytest.raises(pkv.PagedKVError):
         pkv.paged_attention_prefill(out.float(), b["query"].float(), b["key_cache"].float(),
                                     b["value_cache"].float(), *args[4:], 5)   # float32
+
+
+def test_prefill_graph_replay_matches_eager(gpu_lib):
+    """The prefill step (chunk write, then attention) captured in a HIP
+    graph and replayed, with eager steps in between: every replay gives the
+    eager output bit for bit."""
+    w = dataclasses.replace(W["prefill_chunk"], num_seqs=3, lengths=("prefill", 0, 200, 40, 90))
+    b = wl.make_batch(w, 9, DEV)
+    bt, cl = dev_i32(b["block_tables"]), dev_i32(b["context_lens"])
+    qsl, slots = dev_i32(b["query_start_loc"]), torch.from_numpy(b["slot_mapping"]).to(DEV)
+    out = torch.empty_like(b["query"])
+
+    def step():
+        pkv.reshape_and_cache(b["key"], b["value"], slots, b["key_cache"], b["value_cache"])
+        pkv.paged_attention_prefill(out, b["query"], b["key_cache"], b["value_cache"], bt, cl,
+                                    qsl, float(w.scale), w.num_kv_heads, w.max_query_len)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager step"
+        step()
+        torch.cuda.synchronize()
+
+
+def test_prefill_of_a_long_prompt_in_chunks_matches_whole(gpu_lib):
+    """A 600-token prompt attended in one call equals the same prompt
+    attended in three chunks (200 tokens each, each after the previous ones
+    are cached): rows agree within the float32 accumulation tolerance."""
+    w = wl.custom_prefill([0], [600], 8, 2, 128, "f16")
+    b = wl.make_batch(w, 13, DEV)
+    run_pool_updates(b)
+    whole = run_prefill(b).clone()
+    parts = []
+    for start in (0, 200, 400):
+        L = start + 200
+        b2 = dict(b, context_lens=np.asarray([L], np.int32),
+                  query_start_loc=np.asarray([0, 200], np.int32),
+                  query=b["query"][start:L].contiguous(),
+                  workload=dataclasses.replace(w, lengths=("prefill_list", (start,), (200,), 0,
+                                                           200)))
+        parts.append(run_prefill(b2).clone())
+    diff = (torch.cat(parts).float() - whole.float()).abs().max().item()
+    say(f"    chunked vs whole prompt: max diff {diff:.2e}")
+    assert diff <= 2e-3
