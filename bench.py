@@ -4,7 +4,10 @@ One step = one pass of the whole path over one seeded synthetic batch:
 copy_blocks (workloads with copy-on-write pairs), reshape_and_cache of the
 step's new tokens (one per sequence -- the token each sequence appends in
 this decode step -- or the private tokens of the sampling workload), then
-paged_attention_decode over every sequence.  Inputs are resident in HBM
+paged_attention_decode over every sequence.  Where every sequence appends
+exactly its newest token into a 16/32-bit pool, the caching and the
+attention are one call, paged_attention_decode_append (--no-fuse keeps
+them apart).  Inputs are resident in HBM
 before the timed region; K steps are timed between two synchronizations.
 
 Prints ONE JSON line.  `value` is whole-step KV throughput in GB/s: the
@@ -58,6 +61,8 @@ def parse():
     ap.add_argument("--no-translation", action="store_true",
                     help="skip the random vs contiguous placement comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="cache new tokens with reshape_and_cache instead of the decode call")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="cap on tokens per piece (default: the workload's, 0 = none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -106,7 +111,7 @@ def decode_algorithmic_bytes(w, lens):
 class Step:
     """Device-resident batch and the calls of one step (no allocation inside)."""
 
-    def __init__(self, w, seed, ps):
+    def __init__(self, w, seed, ps, fuse=True):
         import torch
         import paged_kv_cache_311_amd as pkv
         from paged_kv_cache_311_amd import workloads as wl
@@ -140,11 +145,18 @@ class Step:
         self.pairs = (torch.from_numpy(pairs).to(dev)
                       if pairs is not None and len(pairs) else None)
         self.new_tokens = len(slots)
+        # one new token per sequence, token s of sequence s, at position L-1:
+        # the decode call caches it itself (16/32-bit pools)
+        one_each = ("slot_mapping" not in b
+                    or np.array_equal(b.get("token_seq", []), np.arange(w.num_seqs)))
+        self.fused = bool(fuse and not w.fp8 and one_each and (lens >= 1).all())
 
     def updates(self):
         b, w = self.b, self.w
         if self.pairs is not None:
             self.pkv.copy_blocks(b["key_cache"], b["value_cache"], self.pairs)
+        if self.fused:
+            return
         if w.fp8:
             self.pkv.reshape_and_cache_fp8(self.key, self.value, self.slots, b["key_cache"],
                                            b["value_cache"], w.k_scale, w.v_scale)
@@ -165,7 +177,14 @@ class Step:
                                             partition_size=self.ps, workspace=self.ws)
 
     def decode(self):
-        self.decode_into(self.out, self.b["key_cache"], self.b["value_cache"], self.bt)
+        b, w = self.b, self.w
+        if self.fused:
+            self.pkv.paged_attention_decode_append(
+                self.out, b["query"], b["key_cache"], b["value_cache"], self.bt, self.cl,
+                self.key, self.value, float(w.scale), w.num_kv_heads, partition_size=self.ps,
+                workspace=self.ws)
+        else:
+            self.decode_into(self.out, b["key_cache"], b["value_cache"], self.bt)
 
     def run(self, steps, warmup):
         torch = self.torch
@@ -259,11 +278,13 @@ def measure_prefill(w, seed, steps, warmup):
     }
 
 
-def measure(w, seed, steps, warmup, ps):
-    st = Step(w, seed, ps)
+def measure(w, seed, steps, warmup, ps, fuse=True):
+    st = Step(w, seed, ps, fuse)
     step_ms, dec_ms, wall = st.run(steps, warmup)
     kvb = kv_bytes(w, st.lens)
     algo = decode_algorithmic_bytes(w, st.lens)
+    if st.fused:  # the call also writes each sequence's new key and value rows
+        algo += 2 * w.num_seqs * w.num_kv_heads * w.head_size * w.kv_elem_bytes
     dec_avg = float(dec_ms.mean())
     r = {
         "workload": w.key, "seed": seed, "seqs": w.num_seqs,
@@ -271,6 +292,7 @@ def measure(w, seed, steps, warmup, ps):
         "dtype": w.dtype, "kv_dtype": w.kv_dtype or w.dtype, "partition_size": st.ps,
         "kv_tokens": int(st.lens.astype(np.int64).sum()), "kv_bytes_per_step": kvb,
         "new_tokens_per_step": st.new_tokens,
+        "append": "fused into the decode call" if st.fused else "reshape_and_cache",
         "cow_pairs_per_step": 0 if st.pairs is None else int(st.pairs.shape[0]),
         "ms_per_step": step_ms, "kv_GBps": kvb / (step_ms * 1e-3) / 1e9,
         "decode_tokens_per_s": w.num_seqs / (step_ms * 1e-3),
@@ -434,7 +456,8 @@ def main():
 
     w = wl.WORKLOADS[a.workload]
     print(f"# measuring {w.key}", file=sys.stderr, flush=True)
-    main_r, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size)
+    main_r, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size,
+                         not a.no_fuse)
     cpu = None if a.no_cpu_baseline else cpu_baseline(st, a.cpu_seconds)
     trans = None if a.no_translation else translation_overhead(st, a.steps)
     del st
@@ -444,7 +467,8 @@ def main():
     for key in [k for k in a.also.split(",") if k and k != w.key]:
         print(f"# measuring {key}", file=sys.stderr, flush=True)
         ow = wl.WORKLOADS[key]
-        r, st = measure(ow, ow.default_seed, a.steps, a.warmup, a.partition_size)
+        r, st = measure(ow, ow.default_seed, a.steps, a.warmup, a.partition_size,
+                        not a.no_fuse)
         others[key] = r
         del st
         torch.cuda.empty_cache()

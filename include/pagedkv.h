@@ -76,7 +76,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 4 */
+int pkv_abi_version(void);  /* 5 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -225,6 +225,31 @@ int reshape_and_cache_fp8(const void* key, const void* value,
                           int num_tokens, int num_kv_heads, int head_size,
                           int block_size, int64_t num_blocks, int dtype,
                           void* stream);
+
+/*
+ * paged_attention_decode_append: one decode step that also caches the
+ * step's token -- reshape_and_cache followed by paged_attention_decode, in
+ * one launch.  For every sequence s with L = context_lens[s] >= 1, token
+ * L - 1 is the new one: its key and value rows new_key[s], new_value[s]
+ * ([num_seqs][num_kv_heads][head_size], `dtype`, 16-byte aligned) are
+ * written into its slot, block_tables[s][(L-1)/16] * 16 + (L-1) % 16
+ * ([TEQ] "The OS already solved this in the 1960s": a token's slot comes
+ * from the table), and the attention over tokens 0 .. L-1 uses them.  The
+ * result equals reshape_and_cache of those rows to those slots followed by
+ * paged_attention_decode (same arguments otherwise).  The block holding a
+ * new token must not be shared (copy it first, as for reshape_and_cache).
+ * Pools in `dtype` (not E4M3: UNSUPPORTED).  Sequences with L = 0 write
+ * nothing.
+ */
+int paged_attention_decode_append(void* out, const void* query, void* key_cache,
+                                  void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const void* new_key,
+                                  const void* new_value, float scale, int num_kv_heads,
+                                  int num_seqs, int num_heads, int head_size,
+                                  int block_size, int max_blocks_per_seq,
+                                  int64_t num_blocks, int partition_size,
+                                  void* workspace, size_t workspace_bytes, int dtype,
+                                  void* stream);
 
 /*
  * paged_attention_decode_fp8: paged_attention_decode over E4M3 pools, the

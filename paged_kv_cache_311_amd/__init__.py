@@ -62,6 +62,10 @@ def _declare(lib):
     lib.reshape_and_cache_fp8.restype = c_int
     lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_f, c_f, c_int, c_int, c_int,
                                           c_int, c_i64, c_int, vp]
+    lib.paged_attention_decode_append.restype = c_int
+    lib.paged_attention_decode_append.argtypes = [
+        vp, vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
+        c_i64, c_int, vp, c_sz, c_int, vp]
     lib.paged_attention_prefill.restype = c_int
     lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_i64, c_int, c_int, vp]
@@ -157,7 +161,8 @@ def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per
 
 
 def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-            num_kv_heads, partition_size, workspace, validate, fp8, k_scale, v_scale):
+            num_kv_heads, partition_size, workspace, validate, fp8, k_scale, v_scale,
+            new_key=None, new_value=None):
     import torch
     lib = load_library()
     _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens)
@@ -191,6 +196,14 @@ def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scal
             _stream_of(query))
     if fp8:
         _check(lib.paged_attention_decode_fp8(*common, float(k_scale), float(v_scale), *tail))
+    elif new_key is not None:
+        _all_cuda_contiguous(new_key, new_value)
+        _need(new_key.dtype == query.dtype and new_value.dtype == query.dtype,
+              "new keys and values share the query's dtype")
+        _need(tuple(new_key.shape) == (S, Hkv, D) and tuple(new_value.shape) == (S, Hkv, D),
+              "new keys and values are [S, Hkv, D]")
+        _check(lib.paged_attention_decode_append(*common[:6], _ptr(new_key), _ptr(new_value),
+                                                 common[6], *tail))
     else:
         _check(lib.paged_attention_decode(*common, *tail))
     return out
@@ -207,6 +220,18 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
     """
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0)
+
+
+def paged_attention_decode_append(out, query, key_cache, value_cache, block_tables,
+                                  context_lens, new_key, new_value, scale, num_kv_heads,
+                                  partition_size=0, workspace=None, validate=False):
+    """reshape_and_cache of each sequence's newest token followed by
+    paged_attention_decode, in one call: new_key / new_value [S, Hkv, D]
+    are token L - 1 of each sequence; they are written to that token's slot
+    (table[(L-1)//16]*16 + (L-1)%16) and attended.  16/32-bit pools."""
+    return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                   num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0,
+                   new_key, new_value)
 
 
 def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,

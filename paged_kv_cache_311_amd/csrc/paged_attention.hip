@@ -129,6 +129,12 @@ struct DecodeParams {
   int4* desc;          // [R]  split segment ending in range r: s, hg, P, nb
   float* part_ml;      // [R][2][GC][2]  running max (log2 units), sum
   float* part_acc;     // [R][2][GC][D]  unnormalized accumulator
+  // Appending variant (null otherwise): each sequence's newest token
+  // (position L - 1), its key and value rows [S][Hkv][D] of this launch.
+  // Its tile takes them from here, and one wave per (sequence, kv head)
+  // writes them to the token's slot.
+  const char* new_k;
+  const char* new_v;
 };
 
 struct Tile {
@@ -630,14 +636,50 @@ paged_decode_kernel(const DecodeParams p) {
                                          : (jg + 4 * m) * 16));
     }
   };
-  auto load_tile = [&](Tile& t, int id, int hg) {
-    const int64_t off = (int64_t)id * block_stride + (int64_t)(hg * GC / group) * C::kTileB;
+  auto load_tile = [&](Tile& t, int id, int hg, int s_t, int info_t) {
+    const int g = hg * GC / group;
+    const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
     const char* kb = p.kcache + off;
     const char* vb = p.vcache + off;
+    if (!C::kFp8 && p.new_k != nullptr && (info_t & kSegEnd)) {
+      // the sequence's last block: the lanes of its newest token (row
+      // valid - 1) read that token's rows from the new keys and values
+      const int nt = ((info_t >> 16) & 31) - 1;
+      const int64_t nrow = ((int64_t)s_t * p.num_kv_heads + g) * C::kRowB;
 #pragma unroll
-    for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
+      for (int m = 0; m < NLD; ++m)
+        t.k[m] = load16(row == nt ? p.new_k + nrow + jg * 16 + m * 64 : kb + koff_lane + m * 64);
 #pragma unroll
-    for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
+      for (int m = 0; m < NLD; ++m) {
+        const uint32_t o = voff_lane + m * 1024;
+        t.v[m] = load16((int)(o / C::kRowB) == nt ? p.new_v + nrow + o % C::kRowB : vb + o);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
+#pragma unroll
+      for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
+    }
+  };
+  // Appending: the first head group of each kv head writes the newest
+  // token's key and value rows (held by the lanes that loaded them) into
+  // its slot, once the tile has arrived.
+  auto store_new_token = [&](const Tile& t, int id, int hg, int info_t) {
+    const int g = hg * GC / group;
+    if (hg != g * (group / GC)) return;  // another head group of this kv head
+    const int nt = ((info_t >> 16) & 31) - 1;
+    const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
+    char* kb = const_cast<char*>(p.kcache) + off;
+    char* vb = const_cast<char*>(p.vcache) + off;
+    if (row == nt) {
+#pragma unroll
+      for (int m = 0; m < NLD; ++m) store16(kb + koff_lane + m * 64, t.k[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < NLD; ++m) {
+      const uint32_t o = voff_lane + m * 1024;
+      if ((int)(o / C::kRowB) == nt) store16(vb + o, t.v[m]);
+    }
   };
 
   // the wave's stream of tiles: windows cw (being computed) and nw (next)
@@ -697,7 +739,8 @@ paged_decode_kernel(const DecodeParams p) {
     // make the wait for this tile's data also wait for the next tile's.
     const int id_n = __builtin_amdgcn_readlane(pick(in_cw, cw.id, nw.id), j);
     const int id_c = __builtin_amdgcn_readlane(cw.id, ci);
-    load_tile(tn, more ? id_n : id_c, more ? (info_n & 0xffff) : hg);
+    load_tile(tn, more ? id_n : id_c, more ? (info_n & 0xffff) : hg, more ? s_n : s,
+              more ? info_n : info);
     if constexpr (!C::kOverlapNext) __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
 
     // 3. compute the current tile
@@ -724,6 +767,8 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < GC; ++g) sc[g] = -INFINITY;
       }
+      if (!C::kFp8 && p.new_k != nullptr && (info & kSegEnd))
+        store_new_token(tc, __builtin_amdgcn_readlane(cw.id, ci), hg, info);
       float pr[GC];
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
@@ -825,7 +870,8 @@ paged_decode_kernel(const DecodeParams p) {
   Tile ta, tb;
   {
     const int info = __builtin_amdgcn_readlane(cw.info, 0);
-    load_tile(ta, __builtin_amdgcn_readlane(cw.id, 0), info & 0xffff);
+    load_tile(ta, __builtin_amdgcn_readlane(cw.id, 0), info & 0xffff,
+              __builtin_amdgcn_readlane(cw.s, 0), info);
     load_q(qa, __builtin_amdgcn_readlane(cw.s, 0), info & 0xffff);
   }
   // One exit, at the end of the body: leaving between the two steps leaves
@@ -997,9 +1043,13 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
                        int num_kv_heads, int num_seqs, int num_heads, int head_size,
                        int block_size, int max_blocks_per_seq, int64_t num_blocks,
                        int partition_size, void* workspace, size_t workspace_bytes, int dtype,
-                       int kv_dtype, void* stream) {
+                       int kv_dtype, void* stream, const void* new_key = nullptr,
+                       const void* new_value = nullptr) {
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
+  if ((new_key == nullptr) != (new_value == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (new_key && kv_dtype != dtype) return PKV_ERR_UNSUPPORTED;  // 16/32-bit pools only
+  if (((uintptr_t)new_key | (uintptr_t)new_value) & 15u) return PKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || num_blocks > INT32_MAX)
     return PKV_ERR_INVALID_ARG;
@@ -1059,6 +1109,7 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   // they share the workspace, which each launch leaves ready for the next
   const int esz = dtype == PKV_F32 ? 4 : 2;
   const int64_t row = (int64_t)num_heads * head_size * esz;
+  const int64_t new_row = (int64_t)num_kv_heads * head_size * esz;
   for (int s0 = 0; s0 < num_seqs; s0 += kLdsSeqs) {
     DecodeParams b = a;
     b.num_seqs = num_seqs - s0 < kLdsSeqs ? num_seqs - s0 : kLdsSeqs;
@@ -1066,6 +1117,8 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
     b.query = (const char*)query + s0 * row;
     b.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
     b.context_lens = context_lens + s0;
+    b.new_k = new_key ? (const char*)new_key + s0 * new_row : nullptr;
+    b.new_v = new_value ? (const char*)new_value + s0 * new_row : nullptr;
     hipError_t e;
     if (kv_dtype == PKV_FP8_E4M3) {
       e = dtype == PKV_F16 ? dispatch_d<PKV_F16, PKV_FP8_E4M3>(b, head_size, gc, st)
@@ -1095,6 +1148,19 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
                           1.f, 1.f, num_kv_heads, num_seqs, num_heads, head_size, block_size,
                           max_blocks_per_seq, num_blocks, partition_size, workspace,
                           workspace_bytes, dtype, dtype, stream);
+}
+
+extern "C" int paged_attention_decode_append(
+    void* out, const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
+    const void* new_value, float scale, int num_kv_heads, int num_seqs, int num_heads,
+    int head_size, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+    int partition_size, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!new_key || !new_value) return PKV_ERR_INVALID_ARG;
+  return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                          1.f, 1.f, num_kv_heads, num_seqs, num_heads, head_size, block_size,
+                          max_blocks_per_seq, num_blocks, partition_size, workspace,
+                          workspace_bytes, dtype, dtype, stream, new_key, new_value);
 }
 
 extern "C" int paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,

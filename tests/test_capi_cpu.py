@@ -37,6 +37,7 @@ def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("paged_attention_decode", "reshape_and_cache", "copy_blocks",
               "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
+              "paged_attention_decode_append",
               "paged_attention_workspace_bytes", "pkv_status_string", "pkv_abi_version"):
         assert n in names
 
@@ -66,7 +67,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 4
+    assert lib.pkv_abi_version() == 5
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -263,3 +264,21 @@ def test_prefill_argument_validation(lib):
     assert prefill(lib, out=FAKE + 4) == INVALID          # 8-byte stores
     assert prefill(lib, S=0) == OK                        # nothing to do: no launch
     assert prefill(lib, mq=0) == OK
+
+
+def test_decode_append_argument_validation(lib):
+    def app(**kw):
+        a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, nk=FAKE, nv=FAKE,
+                 scale=0.1, hkv=4, S=2, Hq=8, D=128, bs=16, W=4, NB=64, ps=0, ws=0, wsb=0,
+                 dtype=1, stream=0)
+        a.update(kw)
+        return lib.paged_attention_decode_append(
+            a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["nk"], a["nv"],
+            a["scale"], a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ps"],
+            a["ws"], a["wsb"], a["dtype"], a["stream"])
+    assert app() == WORKSPACE                      # valid up to the workspace
+    assert app(nk=0) == INVALID
+    assert app(nv=0) == INVALID
+    assert app(nk=FAKE + 8) == INVALID             # 16-byte rows
+    assert app(dtype=3) == UNSUPPORTED
+    assert app(S=0) == OK
