@@ -34,6 +34,16 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The decode kernel picks each tile's cache policy
+# with a uniform branch; structurizing that branch adds a path that issues
+# neither load, and the compiler's wait counts then assume it, waiting for
+# the next tile's loads before computing the current one.  Leaving uniform
+# regions unstructurized (they are lowered as scalar branches) keeps them.
+SOURCE_FLAGS = {
+    "paged_attention.hip": ["-mllvm", "-structurizecfg-skip-uniform-regions"],
+}
+
+
 def source_digest():
     """sha256 of every source and header the library is built from, and of
     the compile flags.  Built into the library (pkv_build_id) and checked by
@@ -48,6 +58,8 @@ def source_digest():
         with open(f, "rb") as fh:
             h.update(fh.read())
     h.update(" ".join(FLAGS[:-1]).encode())  # flags other than the include path
+    for src in sorted(SOURCE_FLAGS):
+        h.update((src + " " + " ".join(SOURCE_FLAGS[src])).encode())
     return h.hexdigest()
 
 
@@ -82,7 +94,8 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
-        warn = _run([HIPCC, *FLAGS, stamp, "-c", os.path.join(CSRC, src), "-o", obj])
+        warn = _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), stamp, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
         if verbose and warn.strip():
             print(warn, file=sys.stderr)
         return obj

@@ -510,6 +510,7 @@ constexpr int kPieceLast = 1 << 22;
 constexpr int kSegStart = 1 << 23;
 constexpr int kSegEnd = 1 << 24;
 constexpr int kRangeFirst = 1 << 25;
+constexpr int kShared = 1 << 26;  // a neighbouring sequence maps the same block here
 
 __device__ __forceinline__ int pick(bool c, int a, int b) { return c ? a : b; }
 
@@ -546,11 +547,22 @@ __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const
     const int local = x - excl;
     const int hg = local / nb;
     const int n = local - hg * nb;
-    int64_t b = p.block_tables[(int64_t)s * p.max_blocks + n];
-    b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
+    const int64_t b_raw = p.block_tables[(int64_t)s * p.max_blocks + n];
+    // The sequences of one request (parallel samples, beams) sit side by
+    // side and share their prompt's blocks: a block that the previous or
+    // the next sequence maps at the same index is read by several waves and
+    // is worth keeping in cache; every other block is read once per call.
+    // Both neighbours' entries are read on every path (clamped rows).
+    const int sp = s > 0 ? s - 1 : s;
+    const int sn = s + 1 < p.num_seqs ? s + 1 : s;
+    const int64_t b_prev = p.block_tables[(int64_t)sp * p.max_blocks + n];
+    const int64_t b_next = p.block_tables[(int64_t)sn * p.max_blocks + n];
+    const bool shared = (sp != s && n * kBlockSize < len[sp] && b_prev == b_raw) ||
+                        (sn != s && n * kBlockSize < len[sn] && b_next == b_raw);
+    const int64_t b = b_raw < 0 ? 0 : (b_raw >= p.num_blocks ? p.num_blocks - 1 : b_raw);
     wd.id = (int)b;
     wd.s = s;
-    int f = hg | (min(kBlockSize, len[s] - n * kBlockSize) << 16);
+    int f = hg | (min(kBlockSize, len[s] - n * kBlockSize) << 16) | (shared ? kShared : 0);
     if (n == 0) f |= kSegStart | kPieceFirst;
     if (n == nb - 1) f |= kSegEnd | kPieceLast;
     if (x == x1 - 1) f |= kPieceLast;
@@ -636,6 +648,10 @@ paged_decode_kernel(const DecodeParams p) {
                                          : (jg + 4 * m) * 16));
     }
   };
+  // A tile that only this wave reads in this call is streamed past the
+  // cache; a shared one (kShared) and the last block of an appending
+  // sequence are read with the default policy.  The three paths issue the
+  // same number of loads, so the wait counts do not depend on the path.
   auto load_tile = [&](Tile& t, int id, int hg, int s_t, int info_t) {
     const int g = hg * GC / group;
     const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
@@ -655,10 +671,22 @@ paged_decode_kernel(const DecodeParams p) {
         t.v[m] = load16((int)(o / C::kRowB) == nt ? p.new_v + nrow + o % C::kRowB : vb + o);
       }
     } else {
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kb, C::kTileB);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vb, C::kTileB);
+      if (info_t & kShared) {
 #pragma unroll
-      for (int m = 0; m < NLD; ++m) t.k[m] = load16(kb + koff_lane + m * 64);
+        for (int m = 0; m < NLD; ++m) t.k[m] = load16_buffer<kCacheDefault>(kr, koff_lane + m * 64);
 #pragma unroll
-      for (int m = 0; m < NLD; ++m) t.v[m] = load16(vb + voff_lane + m * 1024);
+        for (int m = 0; m < NLD; ++m)
+          t.v[m] = load16_buffer<kCacheDefault>(vr, voff_lane + m * 1024);
+      } else {
+#pragma unroll
+        for (int m = 0; m < NLD; ++m)
+          t.k[m] = load16_buffer<kCacheNonTemporal>(kr, koff_lane + m * 64);
+#pragma unroll
+        for (int m = 0; m < NLD; ++m)
+          t.v[m] = load16_buffer<kCacheNonTemporal>(vr, voff_lane + m * 1024);
+      }
     }
   };
   // Appending: the first head group of each kv head writes the newest

@@ -154,6 +154,25 @@ __device__ __forceinline__ float lane_float(const u32x4& v, int e) { return floa
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// Streaming reads.  Data read once per call (a key or value tile) is loaded
+// with the non-temporal cache policy, which on gfx950 raises the sustained
+// read rate from HBM (16-B reads of a 2-GiB buffer: ~6.3 TB/s plain,
+// ~7.1 TB/s non-temporal) but gives up reuse from the cache.  The loads go
+// through a raw buffer resource: an intrinsic whose cache policy is an
+// operand, so the optimizer cannot merge it with a plain load of the same
+// address on another path (which would drop the hint).
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor, word 3 (32-bit data)
+constexpr int kCacheDefault = 0;          // buffer instruction cache policy: default
+constexpr int kCacheNonTemporal = 2;      // buffer instruction cache-policy bit: nt
+
+// `bytes` bytes at `base`; offsets outside [0, bytes) read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
+}
+template <int kPolicy>
+__device__ __forceinline__ u32x4 load16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicy));
+}
 __device__ __forceinline__ void store16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
