@@ -49,44 +49,51 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
   store16(vcache + dst, load16(value + src));
 }
 
-// One thread per (token, kv head, 16 elements of the row): 16 input
-// elements (32 or 64 bytes) become one 16-byte chunk of E4M3 codes.
+// One thread per (token, kv head, 4 elements of the row): 4 input elements
+// (8 or 16 bytes) become 4 E4M3 codes (4 bytes).  The encode is a chain of
+// dependent float operations per element, so few elements per thread keep
+// the kernel short when only one token per sequence is written.
+constexpr int kFp8Group = 4;
+
+template <int DT>
+__device__ __forceinline__ u32x4 load_group4(const char* p) {
+  if constexpr (Elt<DT>::kBytes == 4) {
+    return load16(p);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return u32x4{w.x, w.y, 0u, 0u};
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
     const char* __restrict__ key, const char* __restrict__ value,
     const int64_t* __restrict__ slot_mapping, char* __restrict__ kcache,
-    char* __restrict__ vcache, float k_scale, float v_scale, int64_t total_chunks,
+    char* __restrict__ vcache, float k_scale, float v_scale, int64_t total_groups,
     int num_kv_heads, int head_size, int64_t num_slots) {
-  constexpr int kIn = Elt<DT>::kPer16B;  // input elements per 16-B load
   const int64_t idx = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
-  if (idx >= total_chunks) return;
-  const int nch = head_size >> 4;
-  const int c = (int)(idx % nch);
-  const int64_t th = idx / nch;  // token * num_kv_heads + head
+  if (idx >= total_groups) return;
+  const int ngr = head_size / kFp8Group;
+  const int c = (int)(idx % ngr);
+  const int64_t th = idx / ngr;  // token * num_kv_heads + head
   const int g = (int)(th % num_kv_heads);
   const int64_t i = th / num_kv_heads;
   const int64_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;  // padding / out of the pool
   const int64_t blk = slot / kBlockSize;
   const int off = (int)(slot % kBlockSize);
-  const int64_t src = (th * head_size + c * 16) * Elt<DT>::kBytes;
-  const int64_t dst = ((blk * num_kv_heads + g) * kBlockSize + off) * head_size + c * 16;
+  const int64_t src = (th * head_size + c * kFp8Group) * Elt<DT>::kBytes;
+  const int64_t dst = ((blk * num_kv_heads + g) * kBlockSize + off) * head_size + c * kFp8Group;
   auto quantize = [&](const char* in, float scale) {
-    u32x4 codes = {0u, 0u, 0u, 0u};
+    const u32x4 x = load_group4<DT>(in);
+    uint32_t codes = 0u;
 #pragma unroll
-    for (int part = 0; part < 16 / kIn; ++part) {
-      const u32x4 x = load16(in + part * 16);
-#pragma unroll
-      for (int e = 0; e < kIn; ++e) {
-        const int k = part * kIn + e;  // element of the 16
-        const uint32_t q = e4m3_code(elem_to_float<DT>(x, e) / scale);
-        codes[k >> 2] |= q << (8 * (k & 3));
-      }
-    }
+    for (int e = 0; e < kFp8Group; ++e)
+      codes |= e4m3_code(elem_to_float<DT>(x, e) / scale) << (8 * e);
     return codes;
   };
-  store16(kcache + dst, quantize(key + src, k_scale));
-  store16(vcache + dst, quantize(value + src, v_scale));
+  *reinterpret_cast<uint32_t*>(kcache + dst) = quantize(key + src, k_scale);
+  *reinterpret_cast<uint32_t*>(vcache + dst) = quantize(value + src, v_scale);
 }
 
 // grid.x = pair, grid.y = slice of the block; each thread copies kUnroll
@@ -203,7 +210,7 @@ extern "C" int reshape_and_cache_fp8(const void* key, const void* value,
       15u)
     return PKV_ERR_INVALID_ARG;
   if (num_tokens == 0) return PKV_OK;
-  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_size / 16);
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_size / kFp8Group);
   const int64_t grid = (total + kCopyThreads - 1) / kCopyThreads;
   if (grid > (int64_t)(UINT32_MAX / kCopyThreads)) return PKV_ERR_INVALID_ARG;
   (void)hipGetLastError();
