@@ -9,7 +9,9 @@
  *   reshape_and_cache       scatter new tokens' keys/values to their slots;
  *   copy_blocks             block-level copy-on-write of shared blocks;
  * the first two again for pools of 8-bit float (E4M3) codes with one
- * scale per pool (paged_attention_decode_fp8, reshape_and_cache_fp8); and
+ * scale per pool (paged_attention_decode_fp8, reshape_and_cache_fp8);
+ *   paged_attention_decode_append  the first two fused for a decode step
+ *                           in which every sequence appends one token; and
  *   paged_attention_prefill causal attention of a chunk of new tokens per
  *                           sequence (a whole prompt, or the next part of
  *                           one) over the cached tokens, on the same pools.
@@ -24,7 +26,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.  Every pointer argument is device memory owned by the caller
- * (the library allocates nothing and keeps no state; calls are reentrant).
+ * (the library allocates nothing and keeps no state beyond a per-device
+ * memo of kernel occupancy; calls are reentrant).
  * All tensors are dense, row-major, with no padding between rows.
  *
  * Element types (`dtype`): PKV_F32, PKV_F16 (IEEE binary16), PKV_BF16.

@@ -2,10 +2,11 @@
 
 The three operations -- paged_attention_decode, reshape_and_cache and
 copy_blocks -- the fp8 variants of the first two (pools of E4M3 codes with
-one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8) and
-paged_attention_prefill (causal attention of a chunk of new tokens) run
-entirely in the HIP kernels of libpagedkv.so (declared in
-include/pagedkv.h).  This module only marshals torch tensors (device
+one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8),
+paged_attention_decode_append (a decode step that also caches each
+sequence's newest token) and paged_attention_prefill (causal attention of
+a chunk of new tokens) run entirely in the HIP kernels of libpagedkv.so
+(declared in include/pagedkv.h).  This module only marshals torch tensors (device
 memory and the current stream) into the C calls and raises on a nonzero
 status.  There is no fallback: if the library is missing or was not built,
 every call raises.

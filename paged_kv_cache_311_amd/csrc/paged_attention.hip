@@ -28,7 +28,8 @@
 //               accumulator).  The range holding a split segment's last
 //               tile names that segment in a per-range descriptor, and a
 //               second, light kernel merges the pieces of every segment a
-//               descriptor names (one wave each).
+//               descriptor names (a wave each, or a workgroup when the
+//               segment is split many ways).
 //
 // Per tile (one wave):
 //   QK  = MFMA chain: the key tile is the B operand exactly as loaded (lane
@@ -40,7 +41,18 @@
 //   PV  = VALU FMA in float32 over value tiles loaded as contiguous 1 KiB
 //         rows per instruction; probabilities reach the value layout through
 //         a 16 x GC LDS buffer owned by the wave.
-//   The next tile's K and V are loaded while the current one is computed.
+//   The next tile's loads are issued before the current tile is computed
+//   (E4M3 pools compute while they are in flight; 16-bit pools wait for
+//   them first and rely on the SIMD's other wave for the overlap).
+//   A tile only this wave reads in the call is loaded with the
+//   non-temporal cache policy (a faster stream from HBM); a tile that a
+//   neighbouring sequence also maps (shared prompt blocks) keeps the
+//   default policy, so its other readers find it in L2.
+//
+// Appending variant: the same kernel also caches each sequence's newest
+// token -- in its last tile the lanes of that row read the new key and
+// value rows instead of the pool, and one head group per kv head stores
+// them into the slot.
 //
 // Masking: tokens at or beyond the context length in the last block are
 // excluded by select (logit -inf, value zeroed), never by multiplying
@@ -651,7 +663,10 @@ paged_decode_kernel(const DecodeParams p) {
   // A tile that only this wave reads in this call is streamed past the
   // cache; a shared one (kShared) and the last block of an appending
   // sequence are read with the default policy.  The three paths issue the
-  // same number of loads, so the wait counts do not depend on the path.
+  // same number of loads, so the wait counts do not depend on the path (this
+  // file is compiled with uniform regions left unstructurized: structurizing
+  // the branch would add a path that issues no load, and the waits after
+  // the join would assume it).
   auto load_tile = [&](Tile& t, int id, int hg, int s_t, int info_t) {
     const int g = hg * GC / group;
     const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
