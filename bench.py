@@ -19,8 +19,9 @@ region itself when a step is that call alone, else from a second pass of
 the same steps with events around each call; `cpu_baseline` times the float64 CPU
 oracle on a bounded sample of the same batch (single thread);
 `translation` times the same decode call on the same batch laid out with
-every sequence's blocks physically consecutive (identity block tables),
-against the random placement.  `prefill` times the prefill path (the
+every sequence's blocks physically consecutive (identity block tables) and
+in a virtually contiguous pool (HIP virtual-memory ranges backed on
+demand), against the random placement.  `prefill` times the prefill path (the
 chunk's reshape_and_cache, then paged_attention_prefill) on its own
 workloads, in TFLOP/s of causal attention against the MFMA peak.
 
@@ -349,21 +350,57 @@ def contiguous_layout(st):
             torch.from_numpy(tables).to("cuda:0"))
 
 
+def virtual_layout(st):
+    """The same batch in a virtually contiguous pool (pkv_vpool): sequence s
+    at virtual blocks s*W .. s*W + n_s - 1, physical memory mapped in
+    granules behind them only.  Returns (pool, tables) or None if blocks are
+    shared between sequences or the device refuses virtual-memory mapping."""
+    torch, b, w, pkv = st.torch, st.b, st.w, st.pkv
+    bt, lens = b["block_tables"], st.lens
+    S, W = bt.shape
+    need = [-(-int(L) // 16) for L in lens]
+    src = [int(x) for s in range(S) for x in bt[s, :need[s]]]
+    if len(set(src)) != len(src):
+        return None
+    try:
+        vp = pkv.VirtualPool(S * W, w.num_kv_heads, w.head_size, w.kv_dtype or w.dtype)
+    except pkv.PagedKVError:
+        return None
+    vt = np.full_like(bt, -1)
+    for s in range(S):
+        if need[s]:
+            vp.map(s * W, need[s])
+            vt[s, :need[s]] = s * W + np.arange(need[s])
+    # every block a launch reads must be backed (an unmapped read faults)
+    assert all(vp.covers(s * W, need[s]) for s in range(S) if need[s])
+    dst = [int(x) for s in range(S) for x in vt[s, :need[s]]]
+    si = torch.tensor(src, dtype=torch.int64, device="cuda:0")
+    di = torch.tensor(dst, dtype=torch.int64, device="cuda:0")
+    for pool, from_pool in ((vp.key_cache, b["key_cache"]), (vp.value_cache, b["value_cache"])):
+        pool[di] = from_pool[si].view(pool.dtype)
+    torch.cuda.synchronize()
+    return vp, torch.from_numpy(vt).to("cuda:0")
+
+
 def translation_overhead(st, steps):
     """Decode-call time with the batch's random block placement against the
     same batch laid out contiguously (same kernel, same values, identity
-    tables), the two timed alternately."""
+    tables) and in a virtually contiguous pool, the three timed in turn."""
     lay = contiguous_layout(st)
     if lay is None:
         return None
     torch, b, w = st.torch, st.b, st.w
     kc2, vc2, bt2 = lay
     out2 = torch.empty_like(st.out)
+    vlay = virtual_layout(st)
+    out3 = torch.empty_like(st.out)
 
     def call(kc, vc, bt, out):
         st.decode_into(out, kc, vc, bt)
 
     args = [(b["key_cache"], b["value_cache"], st.bt, st.out), (kc2, vc2, bt2, out2)]
+    if vlay is not None:
+        args.append((vlay[0].key_cache, vlay[0].value_cache, vlay[1], out3))
     for _ in range(3):
         for a in args:
             call(*a)
@@ -376,7 +413,8 @@ def translation_overhead(st, steps):
             call(*a)
             ev[j][i][1].record()
     torch.cuda.synchronize()
-    us = [1000.0 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev[j]])) for j in range(2)]
+    us = [1000.0 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev[j]]))
+          for j in range(len(args))]
     r = {"workload": w.key,
          "random_placement_call_us": round(us[0], 2),
          "contiguous_placement_call_us": round(us[1], 2),
@@ -384,6 +422,18 @@ def translation_overhead(st, steps):
          "outputs_bitwise_equal": bool(torch.equal(st.out, out2)),
          "layout": "each sequence's blocks physically consecutive in sequence order "
                    "(identity block tables); same kernel, values and tables' content"}
+    if vlay is not None:
+        vp = vlay[0]
+        r.update({
+            "virtual_contiguous_call_us": round(us[2], 2),
+            "translation_overhead_vs_virtual_pct": round(100.0 * (us[0] / us[2] - 1.0), 2),
+            "virtual_outputs_bitwise_equal": bool(torch.equal(st.out, out3)),
+            "virtual_layout": (f"each sequence's blocks virtually consecutive in a reserved "
+                               f"range, backed by {vp.granularity >> 20}-MiB physical granules "
+                               f"mapped on demand ({vp.mapped_bytes / 2**20:.0f} MiB mapped "
+                               f"for both tensors)")})
+        args.pop()
+        vp.close()
     del kc2, vc2
     return r
 

@@ -67,6 +67,22 @@ def _declare(lib):
     lib.paged_attention_decode_append.argtypes = [
         vp, vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
         c_i64, c_int, vp, c_sz, c_int, vp]
+    lib.pkv_vpool_create.restype = c_int
+    lib.pkv_vpool_create.argtypes = [c_i64, c_i64, ctypes.POINTER(vp)]
+    lib.pkv_vpool_map.restype = c_int
+    lib.pkv_vpool_map.argtypes = [vp, c_i64, c_i64]
+    lib.pkv_vpool_covers.restype = c_int
+    lib.pkv_vpool_covers.argtypes = [vp, c_i64, c_i64]
+    lib.pkv_vpool_keys.restype = vp
+    lib.pkv_vpool_keys.argtypes = [vp]
+    lib.pkv_vpool_values.restype = vp
+    lib.pkv_vpool_values.argtypes = [vp]
+    lib.pkv_vpool_granularity.restype = c_i64
+    lib.pkv_vpool_granularity.argtypes = [vp]
+    lib.pkv_vpool_mapped_bytes.restype = c_i64
+    lib.pkv_vpool_mapped_bytes.argtypes = [vp]
+    lib.pkv_vpool_destroy.restype = None
+    lib.pkv_vpool_destroy.argtypes = [vp]
     lib.paged_attention_prefill.restype = c_int
     lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_i64, c_int, c_int, vp]
@@ -373,3 +389,61 @@ def _validate_tables(block_tables, context_lens, num_blocks):
         ids = bt[s, :-(-int(L) // BLOCK_SIZE)] if L else bt[s, :0]
         _need(not len(ids) or (ids.min() >= 0 and ids.max() < num_blocks),
               f"sequence {s}: block id outside the pool")
+
+
+class _DeviceArray:
+    """A device address seen by torch through the CUDA array interface (no
+    copy, no ownership)."""
+
+    def __init__(self, ptr, shape, typestr):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr,
+                                         "data": (int(ptr), False), "version": 3}
+
+
+class VirtualPool:
+    """A virtually contiguous KV pool (include/pkv_vpool.h): `key_cache` and
+    `value_cache` are tensors [num_blocks, num_kv_heads, 16, head_size] over
+    reserved virtual ranges whose physical memory is mapped on demand, in
+    granules, by `map(first_block, count)`.  Giving each sequence a run of
+    consecutive blocks makes its cache virtually contiguous; every call of
+    this module runs on the pool as on any other.  Reading a block that is
+    not mapped faults: check `covers` first.  `close()` (after the work
+    that reads the pool has finished) releases everything."""
+
+    _TYPESTR = {"f32": "<f4", "f16": "<f2", "bf16": "<i2", "e4m3": "|u1"}
+
+    def __init__(self, num_blocks, num_kv_heads, head_size, dtype):
+        import torch
+        lib = load_library()
+        esz = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[dtype]
+        self.shape = (int(num_blocks), int(num_kv_heads), BLOCK_SIZE, int(head_size))
+        self.block_bytes = int(num_kv_heads) * BLOCK_SIZE * int(head_size) * esz
+        handle = ctypes.c_void_p()
+        _check(lib.pkv_vpool_create(int(num_blocks), self.block_bytes, ctypes.byref(handle)))
+        self._lib, self._p = lib, handle
+        dev = torch.device("cuda", torch.cuda.current_device())
+        tensors = []
+        for base in (lib.pkv_vpool_keys(handle), lib.pkv_vpool_values(handle)):
+            t = torch.as_tensor(_DeviceArray(base, self.shape, self._TYPESTR[dtype]), device=dev)
+            tensors.append(t.view(torch.bfloat16) if dtype == "bf16" else t)
+        self.key_cache, self.value_cache = tensors
+
+    def map(self, first_block, count):
+        _check(self._lib.pkv_vpool_map(self._p, int(first_block), int(count)))
+
+    def covers(self, first_block, count):
+        return bool(self._lib.pkv_vpool_covers(self._p, int(first_block), int(count)))
+
+    @property
+    def granularity(self):
+        return int(self._lib.pkv_vpool_granularity(self._p))
+
+    @property
+    def mapped_bytes(self):
+        return int(self._lib.pkv_vpool_mapped_bytes(self._p))
+
+    def close(self):
+        if self._p is not None:
+            self.key_cache = self.value_cache = None
+            self._lib.pkv_vpool_destroy(self._p)
+            self._p = None

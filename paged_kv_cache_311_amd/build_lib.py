@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(CSRC, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["paged_attention.hip", "cache_ops.hip", "prefill.hip"]
+SOURCES = ["paged_attention.hip", "cache_ops.hip", "prefill.hip", "vpool.hip"]
 HOST_LIB_PATH = os.path.join(HERE, "libpkvhost.so")
 HOST_SOURCES = ["block_manager.cpp"]
 CXX = os.environ.get("CXX", "g++")
@@ -52,7 +52,8 @@ def source_digest():
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) +
                    glob.glob(os.path.join(CSRC, "*.h")) +
-                   [os.path.join(HERE, "..", "include", "pagedkv.h")])
+                   [os.path.join(HERE, "..", "include", "pagedkv.h"),
+                    os.path.join(HERE, "..", "include", "pkv_vpool.h")])
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
