@@ -210,11 +210,13 @@ def test_workspace_reused_across_calls(gpu_lib):
         assert_close(out, ref, w.dtype, f"reuse {w.key} seed {seed}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("key", ["opt13b", "gqa"])
-def test_graph_replay_matches_eager(gpu_lib, key):
-    """One step (reshape_and_cache, then decode) captured in a HIP graph and
-    replayed: every replay, with eager steps in between, gives the eager
-    step's output bit for bit, and that output matches the oracle."""
+def test_graph_replay_matches_eager(gpu_lib, key, fused):
+    """One step (reshape_and_cache, then decode; or the one call that does
+    both) captured in a HIP graph and replayed: every replay, with eager
+    steps in between, gives the eager step's output bit for bit, and that
+    output matches the oracle."""
     if key == "gqa":
         w = wl.custom([5, 700, 33, 1200, 2048, 16], 32, 8, 128, "bf16", max_len=2048)
     else:
@@ -234,6 +236,11 @@ def test_graph_replay_matches_eager(gpu_lib, key):
     out = torch.empty_like(b["query"])
 
     def step():
+        if fused:
+            pkv.paged_attention_decode_append(out, b["query"], b["key_cache"], b["value_cache"],
+                                              bt, cl, key_new, val_new, float(w.scale),
+                                              w.num_kv_heads, workspace=ws)
+            return
         pkv.reshape_and_cache(key_new, val_new, slots, b["key_cache"], b["value_cache"])
         pkv.paged_attention_decode(out, b["query"], b["key_cache"], b["value_cache"], bt, cl,
                                    float(w.scale), w.num_kv_heads, workspace=ws)
