@@ -560,16 +560,19 @@ __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const
     const int hg = local / nb;
     const int n = local - hg * nb;
     const int64_t b_raw = p.block_tables[(int64_t)s * p.max_blocks + n];
-    // The sequences of one request (parallel samples, beams) sit side by
-    // side and share their prompt's blocks: a block that the previous or
-    // the next sequence maps at the same index is read by several waves and
-    // is worth keeping in cache; every other block is read once per call.
-    // Both neighbours' entries are read on every path (clamped rows).
+    // A tile is read by several waves in one call, and is worth keeping in
+    // cache, when its kv head serves more than one head group (each group
+    // reads it), or when its block is shared: the sequences of one request
+    // (parallel samples, beams) sit side by side and share their prompt's
+    // blocks, so a block that the previous or the next sequence maps at the
+    // same index is taken as shared.  Every other tile is read once per
+    // call.  Both neighbours' entries are read on every path (clamped rows).
     const int sp = s > 0 ? s - 1 : s;
     const int sn = s + 1 < p.num_seqs ? s + 1 : s;
     const int64_t b_prev = p.block_tables[(int64_t)sp * p.max_blocks + n];
     const int64_t b_next = p.block_tables[(int64_t)sn * p.max_blocks + n];
-    const bool shared = (sp != s && n * kBlockSize < len[sp] && b_prev == b_raw) ||
+    const bool shared = head_groups > p.num_kv_heads ||
+                        (sp != s && n * kBlockSize < len[sp] && b_prev == b_raw) ||
                         (sn != s && n * kBlockSize < len[sn] && b_next == b_raw);
     const int64_t b = b_raw < 0 ? 0 : (b_raw >= p.num_blocks ? p.num_blocks - 1 : b_raw);
     wd.id = (int)b;
