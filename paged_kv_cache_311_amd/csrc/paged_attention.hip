@@ -134,6 +134,8 @@ struct DecodeParams {
   float scale_log2;    // softmax scale (times the key scale of an E4M3 pool) x log2 e
   float v_scale;       // value scale of an E4M3 pool (1 otherwise)
   int num_seqs, num_heads, num_kv_heads, max_blocks;
+  int group;           // query heads per kv head
+  int hgk;             // head groups per kv head: ceil(group / GC)
   int64_t num_blocks;
   int tile_cap;        // max tiles per range (0: no cap)
   int r_max;           // ranges the workspace holds
@@ -148,6 +150,21 @@ struct DecodeParams {
   const char* new_k;
   const char* new_v;
 };
+
+// Head groups.  A kv head's `group` query heads are cut into hgk groups of
+// GC heads (GC a power of two up to 8, hgk = ceil(group / GC)); the last
+// group of a kv head may be partial.  Its missing heads are computed on a
+// copy of a real one and never stored, so a tile is read once per group of
+// GC heads even when GC does not divide the group.
+__device__ __forceinline__ int kv_head_of(const DecodeParams& p, int hg) { return hg / p.hgk; }
+__device__ __forceinline__ int first_head(const DecodeParams& p, int hg, int gc) {
+  const int g = hg / p.hgk;
+  return g * p.group + (hg - g * p.hgk) * gc;
+}
+__device__ __forceinline__ int heads_in_group(const DecodeParams& p, int hg, int gc) {
+  const int left = p.group - (hg % p.hgk) * gc;
+  return left < gc ? left : gc;
+}
 
 struct Tile {
   // K in MFMA-B layout (lane l: token l%16, chunks (l/16) + 4m), V as
@@ -443,8 +460,10 @@ __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int 
 template <int DT, int D, int GC>
 __device__ __forceinline__ void store_merged(const DecodeParams& p, const Split& sp, int c,
                                              const floatx4& o, float inv) {
+  if (c * 4 / D >= heads_in_group(p, sp.hg, GC)) return;  // a padding head
   char* dst = (char*)p.out +
-              (((int64_t)sp.s * p.num_heads + sp.hg * GC) * D + c * 4) * Elt<DT>::kBytes;
+              (((int64_t)sp.s * p.num_heads + first_head(p, sp.hg, GC)) * D + c * 4) *
+                  Elt<DT>::kBytes;
   store4<DT>(dst, o * inv);
 }
 
@@ -616,8 +635,7 @@ paged_decode_kernel(const DecodeParams p) {
   const int v = wg_l * kWavesPerWG + w;
   const int nwaves = nwg * kWavesPerWG;
 
-  const int head_groups = p.num_heads / GC;
-  const int group = p.num_heads / p.num_kv_heads;
+  const int head_groups = p.num_kv_heads * p.hgk;
   const int T = build_segment_table(p, head_groups, sm_incl, sm_len, sm_wsum, lane, w);
 
   // sequences with no cached token: their output is zero
@@ -653,7 +671,9 @@ paged_decode_kernel(const DecodeParams p) {
   auto load_q = [&](QRegs& q, int s, int hg) {
 #pragma unroll
     for (int c = 0; c < C::kNqg; ++c) {
-      const int head = hg * GC + c * 4 + (row % C::kGcq);
+      const int hi = c * 4 + (row % C::kGcq);  // head within the group
+      const int nv = heads_in_group(p, hg, GC);
+      const int head = first_head(p, hg, GC) + (hi < nv ? hi : nv - 1);
       const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowQ;
       // k-step m reads the query elements of key chunk jg + 4m (E4M3: half
       // m % 2 of chunk jg + 4 (m / 2), 16 codes per chunk)
@@ -671,7 +691,7 @@ paged_decode_kernel(const DecodeParams p) {
   // the branch would add a path that issues no load, and the waits after
   // the join would assume it).
   auto load_tile = [&](Tile& t, int id, int hg, int s_t, int info_t) {
-    const int g = hg * GC / group;
+    const int g = kv_head_of(p, hg);
     const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
     const char* kb = p.kcache + off;
     const char* vb = p.vcache + off;
@@ -711,8 +731,8 @@ paged_decode_kernel(const DecodeParams p) {
   // token's key and value rows (held by the lanes that loaded them) into
   // its slot, once the tile has arrived.
   auto store_new_token = [&](const Tile& t, int id, int hg, int info_t) {
-    const int g = hg * GC / group;
-    if (hg != g * (group / GC)) return;  // another head group of this kv head
+    const int g = kv_head_of(p, hg);
+    if (hg != g * p.hgk) return;  // another head group of this kv head
     const int nt = ((info_t >> 16) & 31) - 1;
     const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
     char* kb = const_cast<char*>(p.kcache) + off;
@@ -860,11 +880,13 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = sum_over_lane_groups<C::kNch>(acc[g][e]);
       }
-      const int h0 = hg * GC;
+      const int h0 = first_head(p, hg, GC);
+      const int nv = heads_in_group(p, hg, GC);
       if (pc_seg_start && (info & kSegEnd)) {  // a whole segment: final output
         if (lane < C::kNch) {
 #pragma unroll
           for (int g = 0; g < GC; ++g) {
+            if (g >= nv) break;  // padding heads
             const float inv = (C::kFp8 ? p.v_scale : 1.f) / l_run[g];
             float o[EPC];
 #pragma unroll
@@ -1024,9 +1046,17 @@ static hipError_t dispatch_d(const DecodeParams& a, int d, int gc, hipStream_t s
   return d == 64 ? dispatch_gc<DT, KT, 64>(a, gc, st) : dispatch_gc<DT, KT, 128>(a, gc, st);
 }
 
+// Heads per head group: the smallest power of two that holds a kv head's
+// query heads, at most 8 (larger groups are cut into groups of 8, the last
+// one possibly partial).  One wave then reads each tile for all of them.
 static int heads_per_wg(int num_heads, int num_kv_heads) {
   const int group = num_heads / num_kv_heads;
-  return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  return group >= 5 ? 8 : group >= 3 ? 4 : group;
+}
+// Head groups of the whole batch row: num_kv_heads * ceil(group / gc).
+static int64_t head_groups_of(int num_heads, int num_kv_heads, int gc) {
+  const int group = num_heads / num_kv_heads;
+  return (int64_t)num_kv_heads * ((group + gc - 1) / gc);
 }
 
 // Largest number of ranges any launch can form (partials are 2 per range).
@@ -1073,7 +1103,8 @@ extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
     return 0;
   const int gc = heads_per_wg(num_heads, num_kv_heads);
   const int per_launch = num_seqs < kLdsSeqs ? num_seqs : kLdsSeqs;
-  const int64_t max_tiles = (int64_t)per_launch * max_blocks_per_seq * (num_heads / gc);
+  const int64_t max_tiles =
+      (int64_t)per_launch * max_blocks_per_seq * head_groups_of(num_heads, num_kv_heads, gc);
   const int64_t r = max_ranges(max_tiles, partition_size / kBlockSize);
   return workspace_layout(r, gc, head_size).total;
 }
@@ -1112,11 +1143,11 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
       15u)
     return PKV_ERR_INVALID_ARG;  // rows are read and written 16 bytes at a time
   const int gc = heads_per_wg(num_heads, num_kv_heads);
-  if (num_heads / gc > 0xFFFF) return PKV_ERR_INVALID_ARG;  // head group: 16 bits
+  const int64_t hgs = head_groups_of(num_heads, num_kv_heads, gc);
+  if (hgs > 0xFFFF) return PKV_ERR_INVALID_ARG;  // head group: 16 bits
   // flattened tile positions within one launch are 32-bit
   const int per_launch = num_seqs < kLdsSeqs ? num_seqs : kLdsSeqs;
-  if ((int64_t)per_launch * max_blocks_per_seq * (num_heads / gc) > INT32_MAX)
-    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)per_launch * max_blocks_per_seq * hgs > INT32_MAX) return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
                                                       head_size, max_blocks_per_seq,
@@ -1137,11 +1168,12 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.hgk = (a.group + gc - 1) / gc;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.tile_cap = partition_size / kBlockSize;
-  const int64_t r = max_ranges((int64_t)per_launch * max_blocks_per_seq * (num_heads / gc),
-                               a.tile_cap);
+  const int64_t r = max_ranges((int64_t)per_launch * max_blocks_per_seq * hgs, a.tile_cap);
   if (r > INT32_MAX) return PKV_ERR_INVALID_ARG;
   a.r_max = (int)r;
   const WorkspaceLayout wl = workspace_layout(r, gc, head_size);

@@ -93,7 +93,11 @@ def test_workspace_bytes(lib):
     assert f(16, 32, 8, 128, 2048, 16, 0) == expected_workspace(4096, 4, 128)
     assert f(16, 32, 8, 128, 2048, 16, 512) == expected_workspace(8192, 4, 128)
     assert f(16, 32, 8, 128, 2048, 16, 16) == expected_workspace(262144, 4, 128)
-    assert f(4, 12, 2, 64, 8, 16, 0) == expected_workspace(4096, 2, 64)   # group 6 -> 2
+    # group 6: one head group of 8 (two padding heads) per kv head
+    assert f(4, 12, 2, 64, 8, 16, 0) == expected_workspace(4096, 8, 64)
+    # group 12: two head groups of 8 per kv head (the second one half full);
+    # 4 seqs x 4096 blocks x 2 kv heads x 2 groups = 65536 tiles, 16-token cap
+    assert f(4, 24, 2, 64, 4096, 16, 16) == expected_workspace(65536, 8, 64)
     # more than 2048 sequences run as launches of 2048: sized for one launch
     assert f(5000, 40, 40, 128, 128, 16, 16) == expected_workspace(2048 * 128 * 40, 1, 128)
     assert f(4, 4, 4, 64, 33, 8, 0) == 0          # unsupported block size

@@ -65,7 +65,9 @@ def test_partition_sizes(gpu_lib, ps):
     assert_close(out, ref, w.dtype, f"partition {ps}")
 
 
-GROUPS = [(4, 4), (8, 4), (8, 2), (8, 1), (16, 2), (6, 2), (12, 2), (10, 2)]
+# includes groups that GC does not divide (padded head groups): 3, 5, 6, 7, 10, 12
+GROUPS = [(4, 4), (8, 4), (8, 2), (8, 1), (16, 2), (6, 2), (12, 2), (10, 2), (28, 4), (20, 4),
+          (3, 1), (12, 1)]
 
 
 @pytest.mark.parametrize("hq,hkv", GROUPS)
