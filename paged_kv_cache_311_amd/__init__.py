@@ -408,7 +408,8 @@ class VirtualPool:
     consecutive blocks makes its cache virtually contiguous; every call of
     this module runs on the pool as on any other.  Reading a block that is
     not mapped faults: check `covers` first.  `close()` (after the work
-    that reads the pool has finished) releases everything."""
+    that reads the pool has finished) releases everything; as a context
+    manager the pool synchronizes the device and closes on exit."""
 
     _TYPESTR = {"f32": "<f4", "f16": "<f2", "bf16": "<i2", "e4m3": "|u1"}
 
@@ -447,3 +448,12 @@ class VirtualPool:
             self.key_cache = self.value_cache = None
             self._lib.pkv_vpool_destroy(self._p)
             self._p = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        import torch
+        torch.cuda.synchronize()  # no launch may still read the pool
+        self.close()
+        return False

@@ -98,8 +98,7 @@ def test_append_on_virtual_pool_matches_paged(gpu_lib):
 
 def test_virtual_pool_mapping(gpu_lib):
     """Granules are mapped on demand, once; coverage reflects them."""
-    vp = pkv.VirtualPool(4096, 8, 128, "f16")   # 32 KiB blocks, 128 MiB reserved per tensor
-    try:
+    with pkv.VirtualPool(4096, 8, 128, "f16") as vp:  # 32 KiB blocks, 128 MiB per tensor
         g = vp.granularity
         per = g // vp.block_bytes
         assert g >= 2 << 20 and vp.mapped_bytes == 2 * g     # the first granule
@@ -114,5 +113,4 @@ def test_virtual_pool_mapping(gpu_lib):
         vp.key_cache[10 * per + 5].fill_(1.5)
         torch.cuda.synchronize()
         assert float(vp.key_cache[10 * per + 5].float().mean()) == 1.5
-    finally:
-        vp.close()
+    assert vp.key_cache is None and vp.mapped_bytes == 0   # closed on exit
