@@ -31,7 +31,8 @@
 //               descriptor names (a wave each, or a workgroup when the
 //               segment is split many ways).
 //
-// Per tile (one wave):
+// Per tile (one wave), with one or two heads per group (and every E4M3 or
+// float32 pool):
 //   QK  = MFMA chain: the key tile is the B operand exactly as loaded (lane
 //         l holds token l%16), the query rows are replicated so every lane
 //         receives the logits of its own token for all heads of the group.
@@ -41,6 +42,20 @@
 //   PV  = VALU FMA in float32 over value tiles loaded as contiguous 1 KiB
 //         rows per instruction; probabilities reach the value layout through
 //         a 16 x GC LDS buffer owned by the wave.
+// With four or eight heads per group and 16-bit pools, both products run on
+// the matrix cores instead:
+//   S^T = K Q^T  (MFMA 16x16x32): A = the key tile as loaded, B = the query
+//         rows, head h of the group on lane column h; lane l receives tokens
+//         4(l/16) .. +3 of head l % 16.
+//   softmax = online and lane-local: a head's 16 logits sit in lanes l,
+//         l^16, l^32, l^48 (row-swap permutes for the max and the sum); the
+//         max is raised only when a tile's exceeds it by 2^8.
+//   O^T += V^T P^T (MFMA 16x16x32): B = the probabilities as the first
+//         product left them, each split into its 16-bit rounding and the
+//         remainder (so the product keeps float32 accuracy); A = the value
+//         tile, stored as rows in the wave's LDS and read back with the
+//         transposing LDS read.  Lane l holds dims 16b + 4(l/16) .. +3 of
+//         head l % 16, so rescales and the final 1/sum are lane-local.
 //   The next tile's loads are issued before the current tile is computed
 //   (E4M3 pools compute while they are in flight; 16-bit pools wait for
 //   them first and rely on the SIMD's other wave for the overlap).
@@ -78,6 +93,17 @@ constexpr int kWavesPerSimdFp8 = 3;             // ... with E4M3 pools
 constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
 constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
+// 16-bit pools with at least this many heads per group compute both
+// products on the matrix cores: the value product in the float32 VALU
+// costs 16 x D FMAs per head and tile, and from four heads up that work,
+// not the stream, sets the pace (measured on one MI355X, 64 query / 8 kv
+// heads over 16 x 32K bfloat16 tokens: 423 -> 351 us; 32 / 8: 354 -> 351;
+// with one head per group the matrix-core path is 4% slower).
+constexpr int kPvMfmaMinGc = 4;
+// Matrix-core path: a head's running max is raised only when a tile's max
+// exceeds it by more than this (log2 units), so the accumulator is rescaled
+// rarely; probabilities then stay below 2^kPvSlack.
+constexpr float kPvSlack = 8.f;
 // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitAllLoads = 0x0F70;
@@ -101,8 +127,15 @@ struct DecodeCfg {
   // MFMA k-steps per chain: one per key chunk, two for E4M3 chunks (16
   // codes widen to two 8-element operands); as many q registers
   static constexpr int kNq = kFp8 ? 2 * kNld : kNld;
+  // Both products on the matrix cores: S^T = K Q^T (head h of the group on
+  // lane column h) and O^T += V^T P^T with the values read transposed from
+  // LDS.  Otherwise QK is Q K^T with replicated query rows and PV runs in
+  // the float32 VALU.
+  static constexpr bool kPvMfma = !kFp8 && DT != PKV_F32 && GC >= kPvMfmaMinGc;
   static constexpr int kGcq = GC < 4 ? GC : 4;       // heads per MFMA chain
-  static constexpr int kNqg = (GC + 3) / 4;          // MFMA chains per tile
+  static constexpr int kNqg = kPvMfma ? 1 : (GC + 3) / 4;  // MFMA chains per tile
+  static constexpr int kVS = D * 2 + 32;             // LDS value row stride (matrix-core path)
+  static constexpr int kNdb = D / 16;                // 16-dim output blocks (matrix-core path)
   static_assert(kNch * 16 == kRowB, "row must be a whole number of 16-B chunks");
   static_assert(kNld * 4 == kNch, "key tile: 4 lane groups x kNld chunks per row");
   static_assert(kNch >= 4 && kNch <= 32, "lane-group reduction assumes 4..32 chunks");
@@ -113,7 +146,8 @@ struct DecodeCfg {
   // for up to four heads per group, otherwise whatever it needs.
   static constexpr bool kNarrow = kEsz <= 2 || D == 64;
   static constexpr int kMinWaves =
-      kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1);
+      kPvMfma ? 2
+              : (kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1));
   static constexpr int kGridWaves = kFp8 ? kWavesPerSimdFp8 : kWavesPerSimd;
   // E4M3 tiles: the next tile's loads stay in flight while the current
   // tile is computed.  16-bit tiles: the wave waits for them as well before
@@ -294,6 +328,24 @@ __device__ __forceinline__ u32x4 widen_e4m3x8(int w0, int w1) {
     r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true));
   }
   return r;
+}
+
+// Four probabilities as eight k slots of a 16-bit MFMA operand: each
+// rounded to the 16-bit type, then the remainder of that rounding (exact
+// in float32), also rounded.  With the values repeated in both halves the
+// product carries p to about 2^-16 of itself (float16: 2^-22), as a
+// float32 product would; one rounding alone would leave 2^-9 (bfloat16).
+template <int DT>
+__device__ __forceinline__ u32x4 split_probs(const float (&pe)[4]) {
+  float hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == PKV_F16) hi[i] = (float)(_Float16)pe[i];
+    else hi[i] = (float)(__bf16)pe[i];
+    lo[i] = pe[i] - hi[i];
+  }
+  return u32x4{pack2<DT>(pe[0], pe[1]), pack2<DT>(pe[2], pe[3]), pack2<DT>(lo[0], lo[1]),
+               pack2<DT>(lo[2], lo[3])};
 }
 
 template <int DT, int KT, int NQ>
@@ -618,7 +670,9 @@ paged_decode_kernel(const DecodeParams p) {
   constexpr int NLD = C::kNld;
   constexpr int EPC = C::kEpc;
 
-  __shared__ float sm_p[kWavesPerWG][kBlockSize * GC];
+  __shared__ float sm_p[kWavesPerWG][C::kPvMfma ? 1 : kBlockSize * GC];
+  // matrix-core path: each wave's value tile as rows, read back transposed
+  __shared__ __attribute__((aligned(16))) char sm_v[kWavesPerWG][C::kPvMfma ? kBlockSize * C::kVS : 16];
   __shared__ int sm_incl[kLdsSeqs];
   __shared__ int sm_len[kLdsSeqs];
   __shared__ int sm_wsum[kWavesPerWG];
@@ -671,7 +725,8 @@ paged_decode_kernel(const DecodeParams p) {
   auto load_q = [&](QRegs& q, int s, int hg) {
 #pragma unroll
     for (int c = 0; c < C::kNqg; ++c) {
-      const int hi = c * 4 + (row % C::kGcq);  // head within the group
+      // head within the group: lane column `row` on the matrix-core path
+      const int hi = C::kPvMfma ? row : c * 4 + (row % C::kGcq);
       const int nv = heads_in_group(p, hg, GC);
       const int head = first_head(p, hg, GC) + (hi < nv ? hi : nv - 1);
       const char* qrow = p.query + ((int64_t)s * p.num_heads + head) * C::kRowQ;
@@ -770,6 +825,12 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
   }
+  // matrix-core path: lane l keeps head l % 16 of the group, its running
+  // max and (partial) sum, and O^T dims 16b + 4(l/16) .. +3 in block b
+  float om_run = -INFINITY, ol_run = 0.f;
+  floatx4 oacc[C::kPvMfma ? C::kNdb : 1];
+#pragma unroll
+  for (int b = 0; b < (C::kPvMfma ? C::kNdb : 1); ++b) oacc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
   bool pc_seg_start = false;
   int pc_slot = 0;
 
@@ -811,17 +872,72 @@ paged_decode_kernel(const DecodeParams p) {
 
     // 3. compute the current tile
     if (info & kPieceFirst) {
+      if constexpr (C::kPvMfma) {
+        om_run = -INFINITY;
+        ol_run = 0.f;
 #pragma unroll
-      for (int g = 0; g < GC; ++g) {
-        m_run[g] = -INFINITY;
-        l_run[g] = 0.f;
+        for (int b = 0; b < C::kNdb; ++b) oacc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+      } else {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
+        for (int g = 0; g < GC; ++g) {
+          m_run[g] = -INFINITY;
+          l_run[g] = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
+        }
       }
       pc_seg_start = (info & kSegStart) != 0;
       pc_slot = cw.r * 2 + ((info & kRangeFirst) ? 0 : 1);
     }
-    {
+    if constexpr (C::kPvMfma) {
+      // S^T = K Q^T: lane l gets tokens 4(l/16) .. +3 of head l % 16
+      floatx4 rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < C::kNq; ++m) rr = mfma32<DT>(tc.k[m], qa[0][m], rr);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = 4 * jg + i < valid ? rr[i] * p.scale_log2 : -INFINITY;
+      if (p.new_k != nullptr && (info & kSegEnd))
+        store_new_token(tc, __builtin_amdgcn_readlane(cw.id, ci), hg, info);
+      // the value tile into the wave's LDS rows, rows past the context zeroed
+      char* sv = sm_v[w];
+#pragma unroll
+      for (int ld = 0; ld < NLD; ++ld) {
+        const int tok = ld * C::kTpl + lane / C::kNch;
+        u32x4 vv = tc.v[ld];
+        if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
+        store16(sv + tok * C::kVS + (lane % C::kNch) * 16, vv);
+      }
+      __builtin_amdgcn_wave_barrier();
+      // online softmax, lane-local (a head's 16 tokens sit in lanes l, l^16,
+      // l^32, l^48)
+      const float m_tile = max4rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      const bool grow = m_tile > om_run + kPvSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_tile : om_run;
+        const float alpha = __builtin_amdgcn_exp2f(om_run - m_new);
+        om_run = m_new;
+        ol_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < C::kNdb; ++b) oacc[b] *= alpha;
+      }
+      float pe[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(x[i] - om_run);
+      ol_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+      // P^T as the B operand: k slots 8(l/16) .. +3 hold the four
+      // probabilities rounded to the 16-bit type, slots +4 .. +7 what that
+      // rounding left out; the values fill both halves alike
+      const u32x4 pb = split_probs<DT>(pe);
+      // O^T += V^T P^T: lane l reads dim 16b + l % 16 of tokens 4(l/16) .. +3
+      const char* vsrc = sv + (4 * jg + (row >> 2)) * C::kVS + (row & 3) * 8;
+#pragma unroll
+      for (int b = 0; b < C::kNdb; ++b) {
+        const uint2 va = read_tr16(vsrc + 32 * b);
+        oacc[b] = mfma32<DT>(u32x4{va.x, va.y, va.x, va.y}, pb, oacc[b]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
       float sc[GC];
 #pragma unroll
       for (int c = 0; c < C::kNqg; ++c) {
@@ -872,7 +988,32 @@ paged_decode_kernel(const DecodeParams p) {
       }
       __builtin_amdgcn_wave_barrier();
     }
-    if (info & kPieceLast) {
+    if (C::kPvMfma && (info & kPieceLast)) {
+      // the head's sum over its four lanes; the accumulator is complete
+      const float l_tot = sum4rows(ol_run);
+      const int h0 = first_head(p, hg, GC);
+      const int nv = heads_in_group(p, hg, GC);
+      if (pc_seg_start && (info & kSegEnd)) {  // a whole segment: final output
+        if (row < nv) {
+          const float inv = 1.f / l_tot;
+          char* dst = (char*)p.out + (((int64_t)s * p.num_heads + h0 + row) * D + 4 * jg) * C::kEszQ;
+#pragma unroll
+          for (int b = 0; b < C::kNdb; ++b) store4<DT>(dst + 16 * b * C::kEszQ, oacc[b] * inv);
+        }
+      } else if (row < GC) {  // a piece of a split segment: float32 partials
+        const int64_t slot = pc_slot;
+        float* dst = p.part_acc + (slot * GC + row) * D + 4 * jg;
+#pragma unroll
+        for (int b = 0; b < C::kNdb; ++b)
+          store16(dst + 16 * b, u32x4{bits_of(oacc[b][0]), bits_of(oacc[b][1]),
+                                      bits_of(oacc[b][2]), bits_of(oacc[b][3])});
+        if (jg == 0) {
+          p.part_ml[(slot * GC + row) * 2 + 0] = om_run;
+          p.part_ml[(slot * GC + row) * 2 + 1] = l_tot;
+        }
+      }
+    }
+    if (!C::kPvMfma && (info & kPieceLast)) {
       // piece totals: l over the 16 token lanes; acc over lanes sharing a chunk
 #pragma unroll
       for (int g = 0; g < GC; ++g) {

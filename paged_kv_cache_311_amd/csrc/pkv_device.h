@@ -225,4 +225,60 @@ __device__ __forceinline__ float uniform(float x) {
                             __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
+// ------------------------------------------- matrix-core operand moves --
+// Four 16-bit elements of one column from four rows, through the gfx950
+// transposing LDS read.  In each group of 16 lanes, lane a + 4e passes the
+// address of 4 consecutive elements of row e (columns 4a .. 4a+3); lane
+// 4a + b then receives column 4a + b of rows 0..3 (checked on the GPU).
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr16(const char* lds_addr) {
+  const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(lds_addr));
+  return uint2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+               (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
+}
+
+// The value of lane l ^ 16 and of lane l ^ 32, combined with max / sum
+// across the four lanes l, l^16, l^32, l^48 (one row's lanes), through the
+// row-swapping permutes.
+__device__ __forceinline__ float max4rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)b[0]), __builtin_bit_cast(float, (int)b[1]));
+}
+__device__ __forceinline__ float sum4rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
+// Two floats rounded (nearest-even) to the 16-bit type, packed lo | hi << 16.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == PKV_F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, b2{(__bf16)lo, (__bf16)hi});
+  }
+}
+
+// One 16x16x32 product of 16-bit operands, float32 accumulation.
+template <int DT>
+__device__ __forceinline__ floatx4 mfma32(const u32x4& a, const u32x4& b, const floatx4& c) {
+  if constexpr (DT == PKV_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                  __builtin_bit_cast(half8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 }  // namespace pkv

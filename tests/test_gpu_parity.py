@@ -87,18 +87,38 @@ def test_head_grouping_and_types(gpu_lib, dtype, d, hq, hkv):
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024]
 
 
+# 4 and 8 heads per group (12 / 1: a group of 8 and a partial one of 4)
+# take the matrix-core path with 16-bit pools, 1 head the VALU path
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 8), (12, 1)])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_edge_lengths(gpu_lib, dtype):
-    w = wl.custom(EDGE_LENS, 8, 2, 128, dtype, max_len=1024, partition_size=512)
+def test_edge_lengths(gpu_lib, dtype, hq, hkv):
+    w = wl.custom(EDGE_LENS, hq, hkv, 128, dtype, max_len=1024, partition_size=512)
     b = wl.make_batch(w, 99, DEV)
     kc0, vc0 = clone_pools(b)
     out = run_decode(b)
     ref = oracle_decode_subset(b, kc0, vc0, list(range(len(EDGE_LENS))))
-    assert_close(out, ref, dtype, f"edge lengths {dtype}")
+    assert_close(out, ref, dtype, f"edge lengths {dtype} {hq}/{hkv}")
     assert torch.count_nonzero(out[0]) == 0          # L = 0 gives zeros
     # L = 1: a single weight of exactly 1, so the output is v_0 rounded back
     v0 = b["value_cache"][int(b["block_tables"][1, 0]), :, 0, :]
-    assert torch.equal(bits(out[1].view(2, 4, 128)[:, 0]), bits(v0))
+    g = hq // hkv
+    assert torch.equal(bits(out[1].view(hkv, g, 128)[:, 0]), bits(v0))
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (16, 2), (12, 1)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_sharp_softmax(gpu_lib, dtype, hq, hkv):
+    """Queries scaled by 8 (a power of two: exact in both formats) make the
+    logits 8 times larger, so a sequence's running max jumps past the lazy
+    rescale threshold many times and the weights are far from uniform."""
+    lens = [1, 17, 300, 1000, 2047]
+    w = wl.custom(lens, hq, hkv, 128, dtype, max_len=2048, partition_size=512)
+    b = wl.make_batch(w, 7 + hq + hkv, DEV)
+    b["query"].mul_(8)
+    kc0, vc0 = clone_pools(b)
+    out = run_decode(b)
+    ref = oracle_decode_subset(b, kc0, vc0, list(range(len(lens))))
+    assert_close(out, ref, dtype, f"sharp softmax {dtype} {hq}/{hkv}")
 
 
 def test_placement_permutation_is_bitwise_invariant(gpu_lib):
