@@ -131,15 +131,16 @@ struct DecodeCfg {
   // lane column h) and O^T += V^T P^T with the values read transposed from
   // LDS.  Otherwise QK is Q K^T with replicated query rows and PV runs in
   // the float32 VALU.
-  static constexpr bool kPvMfma = !kFp8 && DT != PKV_F32 && GC >= kPvMfmaMinGc;
+  static constexpr bool kPvMfma = !kFp8 && DT != PKV_F32 && (GC >= kPvMfmaMinGc || GC == 16);
   static constexpr int kGcq = GC < 4 ? GC : 4;       // heads per MFMA chain
   static constexpr int kNqg = kPvMfma ? 1 : (GC + 3) / 4;  // MFMA chains per tile
   static constexpr int kVS = D * 2 + 32;             // LDS value row stride (matrix-core path)
   static constexpr int kNdb = D / 16;                // 16-dim output blocks (matrix-core path)
+  static_assert(GC <= 8 || kPvMfma, "16 heads per group: matrix-core path only");
   static_assert(kNch * 16 == kRowB, "row must be a whole number of 16-B chunks");
   static_assert(kNld * 4 == kNch, "key tile: 4 lane groups x kNld chunks per row");
   static_assert(kNch >= 4 && kNch <= 32, "lane-group reduction assumes 4..32 chunks");
-  static_assert(GC == 1 || GC == 2 || GC == 4 || GC == 8, "heads per workgroup");
+  static_assert(GC == 1 || GC == 2 || GC == 4 || GC == 8 || GC == 16, "heads per group");
   // Waves per SIMD the register allocator must leave room for: 3 (168
   // VGPRs) where the kernel fits without spilling (one head per group with
   // 16-bit K/V or 64-wide rows, two heads with 64-wide rows), 2 (256 VGPRs)
@@ -450,7 +451,7 @@ template <int D, int GC>
 __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int kstep,
                             int lane, FoldState<D, GC>& st) {
   using F = FoldState<D, GC>;
-  constexpr int kBatch = F::kCpl == 1 ? 8 : 4;
+  constexpr int kBatch = F::kCpl == 1 ? 8 : (F::kCpl <= 4 ? 4 : 2);
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     st.M[g] = -INFINITY;
@@ -1178,7 +1179,10 @@ static hipError_t dispatch_gc(const DecodeParams& a, int gc, hipStream_t st) {
     case 1: return launch_decode<DT, KT, D, 1>(a, st);
     case 2: return launch_decode<DT, KT, D, 2>(a, st);
     case 4: return launch_decode<DT, KT, D, 4>(a, st);
-    default: return launch_decode<DT, KT, D, 8>(a, st);
+    case 8: return launch_decode<DT, KT, D, 8>(a, st);
+    default:
+      if constexpr (KT == DT && DT != PKV_F32) return launch_decode<DT, KT, D, 16>(a, st);
+      return hipErrorInvalidValue;  // never chosen for these pools
   }
 }
 
@@ -1188,10 +1192,13 @@ static hipError_t dispatch_d(const DecodeParams& a, int d, int gc, hipStream_t s
 }
 
 // Heads per head group: the smallest power of two that holds a kv head's
-// query heads, at most 8 (larger groups are cut into groups of 8, the last
-// one possibly partial).  One wave then reads each tile for all of them.
-static int heads_per_wg(int num_heads, int num_kv_heads) {
+// query heads, at most 16 where both products run on the matrix cores
+// (16-bit pools, whose lane columns hold 16 heads) and 8 otherwise (larger
+// groups are cut into groups of that size, the last one possibly partial).
+// One wave then reads each tile for all of them.
+static int heads_per_wg(int num_heads, int num_kv_heads, bool matrix_pv) {
   const int group = num_heads / num_kv_heads;
+  if (matrix_pv && group >= 9) return 16;
   return group >= 5 ? 8 : group >= 3 ? 4 : group;
 }
 // Head groups of the whole batch row: num_kv_heads * ceil(group / gc).
@@ -1242,12 +1249,18 @@ extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
       head_size <= 0 || max_blocks_per_seq <= 0 || block_size != kBlockSize ||
       !partition_ok(partition_size))
     return 0;
-  const int gc = heads_per_wg(num_heads, num_kv_heads);
+  // the pools' format is not an argument: size for both head-group choices
   const int per_launch = num_seqs < kLdsSeqs ? num_seqs : kLdsSeqs;
-  const int64_t max_tiles =
-      (int64_t)per_launch * max_blocks_per_seq * head_groups_of(num_heads, num_kv_heads, gc);
-  const int64_t r = max_ranges(max_tiles, partition_size / kBlockSize);
-  return workspace_layout(r, gc, head_size).total;
+  size_t total = 0;
+  for (const bool matrix_pv : {false, true}) {
+    const int gc = heads_per_wg(num_heads, num_kv_heads, matrix_pv);
+    const int64_t max_tiles =
+        (int64_t)per_launch * max_blocks_per_seq * head_groups_of(num_heads, num_kv_heads, gc);
+    const int64_t r = max_ranges(max_tiles, partition_size / kBlockSize);
+    const size_t t = workspace_layout(r, gc, head_size).total;
+    total = t > total ? t : total;
+  }
+  return total;
 }
 
 namespace pkv {
@@ -1283,7 +1296,9 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   if (((uintptr_t)query | (uintptr_t)key_cache | (uintptr_t)value_cache | (uintptr_t)out) &
       15u)
     return PKV_ERR_INVALID_ARG;  // rows are read and written 16 bytes at a time
-  const int gc = heads_per_wg(num_heads, num_kv_heads);
+  // 16 heads per group only where both products run on the matrix cores
+  const bool matrix_pv = kv_dtype == dtype && dtype != PKV_F32;
+  const int gc = heads_per_wg(num_heads, num_kv_heads, matrix_pv);
   const int64_t hgs = head_groups_of(num_heads, num_kv_heads, gc);
   if (hgs > 0xFFFF) return PKV_ERR_INVALID_ARG;  // head group: 16 bits
   // flattened tile positions within one launch are 32-bit

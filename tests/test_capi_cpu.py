@@ -95,9 +95,14 @@ def test_workspace_bytes(lib):
     assert f(16, 32, 8, 128, 2048, 16, 16) == expected_workspace(262144, 4, 128)
     # group 6: one head group of 8 (two padding heads) per kv head
     assert f(4, 12, 2, 64, 8, 16, 0) == expected_workspace(4096, 8, 64)
-    # group 12: two head groups of 8 per kv head (the second one half full);
-    # 4 seqs x 4096 blocks x 2 kv heads x 2 groups = 65536 tiles, 16-token cap
-    assert f(4, 24, 2, 64, 4096, 16, 16) == expected_workspace(65536, 8, 64)
+    # group 12: two head groups of 8 per kv head (the second one half full)
+    # with E4M3 or float32 pools, one group of 16 with 16-bit pools; the size
+    # covers both: 4 seqs x 4096 blocks x 2 kv heads x 2 groups = 65536
+    # tiles (or 32768 with groups of 16) at a 16-token cap
+    assert f(4, 24, 2, 64, 4096, 16, 16) == max(expected_workspace(65536, 8, 64),
+                                                 expected_workspace(32768, 16, 64))
+    # with no cap the range count is the same, and groups of 16 need more
+    assert f(4, 32, 2, 128, 64, 16, 0) == expected_workspace(4096, 16, 128)
     # more than 2048 sequences run as launches of 2048: sized for one launch
     assert f(5000, 40, 40, 128, 128, 16, 16) == expected_workspace(2048 * 128 * 40, 1, 128)
     assert f(4, 4, 4, 64, 33, 8, 0) == 0          # unsupported block size

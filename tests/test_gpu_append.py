@@ -143,7 +143,7 @@ def test_append_partition_sizes(gpu_lib, ps):
     append_and_check(wl.make_batch(w, 4243, DEV), partition_size=ps, seed=ps)
 
 
-GROUPS = [(4, 4), (8, 4), (8, 2), (8, 1), (16, 2), (6, 2), (12, 2), (10, 2), (32, 8), (28, 4),
+GROUPS = [(4, 4), (8, 4), (8, 2), (8, 1), (16, 2), (6, 2), (12, 2), (10, 2), (32, 8), (28, 4), (32, 2),
           (12, 1)]
 
 

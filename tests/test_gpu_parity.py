@@ -65,9 +65,11 @@ def test_partition_sizes(gpu_lib, ps):
     assert_close(out, ref, w.dtype, f"partition {ps}")
 
 
-# includes groups that GC does not divide (padded head groups): 3, 5, 6, 7, 10, 12
+# includes groups that GC does not divide (padded head groups): 3, 5, 6, 7, 10, 12, 20;
+# groups beyond 8 run as groups of 16 with 16-bit pools (12: one padded group;
+# 20: 16 + 4) and of 8 otherwise
 GROUPS = [(4, 4), (8, 4), (8, 2), (8, 1), (16, 2), (6, 2), (12, 2), (10, 2), (28, 4), (20, 4),
-          (3, 1), (12, 1)]
+          (3, 1), (12, 1), (32, 2), (40, 2)]
 
 
 @pytest.mark.parametrize("hq,hkv", GROUPS)
@@ -105,7 +107,7 @@ def test_edge_lengths(gpu_lib, dtype, hq, hkv):
     assert torch.equal(bits(out[1].view(hkv, g, 128)[:, 0]), bits(v0))
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (16, 2), (12, 1)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (16, 2), (12, 1), (32, 2)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_sharp_softmax(gpu_lib, dtype, hq, hkv):
     """Queries scaled by 8 (a power of two: exact in both formats) make the
