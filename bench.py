@@ -26,7 +26,8 @@ chunk's reshape_and_cache, then paged_attention_prefill) on its own
 workloads, in TFLOP/s of causal attention against the MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b]
-                    [--also long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,long_gqa_fp8]
+                    [--also long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,long_gqa_fp8,
+                            gqa8_long,gqa16_long]
                     [--no-cpu-baseline]
                     [--no-translation]
 """
@@ -57,7 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--also",
-                    default="long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,long_gqa_fp8")
+                    default="long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,long_gqa_fp8,"
+                            "gqa8_long,gqa16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill_chunk,prefill_gqa",
                     help="prefill workloads to time ('' for none)")

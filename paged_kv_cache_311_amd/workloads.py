@@ -137,6 +137,12 @@ WORKLOADS = {
         Workload("long_gqa_fp8", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
                  ("factor", 1.25), "decode", 32768, kv_dtype="e4m3",
                  k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE),
+        # wider grouped-query shapes than long_gqa's 4 query heads per kv
+        # head, at its lengths: 8 per kv head, and 16 per kv head
+        Workload("gqa8_long", 12, 16, 64, 8, 128, "bf16", ("fixed", 32768),
+                 ("factor", 1.25), "decode", 32768),
+        Workload("gqa16_long", 13, 16, 32, 2, 128, "bf16", ("fixed", 32768),
+                 ("factor", 1.25), "decode", 32768),
         Workload("beam", 11, 64, 40, 40, 128, "f16", ("beam", 256, 1024, 24),
                  ("factor", 1.25), "beam", 1056, prompts=16, samples=4),
         Workload("prefill_chunk", 8, 16, 40, 40, 128, "f16", ("prefill", 0, 1536, 512, 512),

@@ -46,7 +46,8 @@ def test_reduced_workload_every_output(gpu_lib, key, si):
     full_step_and_check(b)
 
 
-@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa", "beam"])
+@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa", "beam",
+                                 "gqa8_long", "gqa16_long"])
 def test_full_size_sampled(gpu_lib, key):
     """Full workload, launch configuration of the benchmark, oracle on a sample."""
     w = W[key]
