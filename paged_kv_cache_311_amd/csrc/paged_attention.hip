@@ -93,13 +93,14 @@ constexpr int kWavesPerSimdFp8 = 3;             // ... with E4M3 pools
 constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
 constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
-// 16-bit pools with at least this many heads per group compute both
+// 16-bit queries with at least this many heads per group compute both
 // products on the matrix cores: the value product in the float32 VALU
 // costs 16 x D FMAs per head and tile, and from four heads up that work,
 // not the stream, sets the pace (measured on one MI355X, 64 query / 8 kv
 // heads over 16 x 32K bfloat16 tokens: 423 -> 351 us; 32 / 8: 354 -> 351;
 // with one head per group the matrix-core path is 4% slower).
 constexpr int kPvMfmaMinGc = 4;
+constexpr int kPvMfmaMinGcFp8 = 4;              // ... with E4M3 pools
 // Matrix-core path: a head's running max is raised only when a tile's max
 // exceeds it by more than this (log2 units), so the accumulator is rescaled
 // rarely; probabilities then stay below 2^kPvSlack.
@@ -131,7 +132,8 @@ struct DecodeCfg {
   // lane column h) and O^T += V^T P^T with the values read transposed from
   // LDS.  Otherwise QK is Q K^T with replicated query rows and PV runs in
   // the float32 VALU.
-  static constexpr bool kPvMfma = !kFp8 && DT != PKV_F32 && (GC >= kPvMfmaMinGc || GC == 16);
+  static constexpr bool kPvMfma =
+      DT != PKV_F32 && (GC >= (kFp8 ? kPvMfmaMinGcFp8 : kPvMfmaMinGc) || GC == 16);
   static constexpr int kGcq = GC < 4 ? GC : 4;       // heads per MFMA chain
   static constexpr int kNqg = kPvMfma ? 1 : (GC + 3) / 4;  // MFMA chains per tile
   static constexpr int kVS = D * 2 + 32;             // LDS value row stride (matrix-core path)
@@ -147,7 +149,7 @@ struct DecodeCfg {
   // for up to four heads per group, otherwise whatever it needs.
   static constexpr bool kNarrow = kEsz <= 2 || D == 64;
   static constexpr int kMinWaves =
-      kPvMfma ? 2
+      kPvMfma ? (kFp8 ? 3 : 2)
               : (kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1));
   static constexpr int kGridWaves = kFp8 ? kWavesPerSimdFp8 : kWavesPerSimd;
   // E4M3 tiles: the next tile's loads stay in flight while the current
@@ -347,6 +349,25 @@ __device__ __forceinline__ u32x4 split_probs(const float (&pe)[4]) {
   }
   return u32x4{pack2<DT>(pe[0], pe[1]), pack2<DT>(pe[2], pe[3]), pack2<DT>(lo[0], lo[1]),
                pack2<DT>(lo[2], lo[3])};
+}
+
+// S^T = K Q^T for one tile: the key tile (E4M3 codes widened, as in
+// qk_mfma) is the A operand and the query rows the B operand, so lane l
+// receives tokens 4(l/16) .. +3 of head l % 16.
+template <int DT, int KT, int NQ>
+__device__ __forceinline__ floatx4 kq_mfma(const u32x4 (&q)[NQ], const Tile& t) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < NQ; ++m) {
+    if constexpr (KT == PKV_FP8_E4M3) {
+      const u32x4 kc = t.k[m / 2];
+      acc = mfma32<DT>(widen_e4m3x8<DT>((int)kc[2 * (m % 2)], (int)kc[2 * (m % 2) + 1]), q[m],
+                       acc);
+    } else {
+      acc = mfma32<DT>(t.k[m], q[m], acc);
+    }
+  }
+  return acc;
 }
 
 template <int DT, int KT, int NQ>
@@ -892,22 +913,29 @@ paged_decode_kernel(const DecodeParams p) {
     }
     if constexpr (C::kPvMfma) {
       // S^T = K Q^T: lane l gets tokens 4(l/16) .. +3 of head l % 16
-      floatx4 rr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < C::kNq; ++m) rr = mfma32<DT>(tc.k[m], qa[0][m], rr);
+      const floatx4 rr = kq_mfma<DT, KT, C::kNq>(qa[0], tc);
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = 4 * jg + i < valid ? rr[i] * p.scale_log2 : -INFINITY;
-      if (p.new_k != nullptr && (info & kSegEnd))
-        store_new_token(tc, __builtin_amdgcn_readlane(cw.id, ci), hg, info);
-      // the value tile into the wave's LDS rows, rows past the context zeroed
+      if constexpr (!C::kFp8) {
+        if (p.new_k != nullptr && (info & kSegEnd))
+          store_new_token(tc, __builtin_amdgcn_readlane(cw.id, ci), hg, info);
+      }
+      // the value tile into the wave's LDS rows as 16-bit elements (E4M3
+      // codes widened exactly), rows past the context zeroed
       char* sv = sm_v[w];
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         const int tok = ld * C::kTpl + lane / C::kNch;
         u32x4 vv = tc.v[ld];
         if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
-        store16(sv + tok * C::kVS + (lane % C::kNch) * 16, vv);
+        if constexpr (C::kFp8) {
+          char* dst = sv + tok * C::kVS + (lane % C::kNch) * 32;
+          store16(dst, widen_e4m3x8<DT>((int)vv[0], (int)vv[1]));
+          store16(dst + 16, widen_e4m3x8<DT>((int)vv[2], (int)vv[3]));
+        } else {
+          store16(sv + tok * C::kVS + (lane % C::kNch) * 16, vv);
+        }
       }
       __builtin_amdgcn_wave_barrier();
       // online softmax, lane-local (a head's 16 tokens sit in lanes l, l^16,
@@ -994,9 +1022,10 @@ paged_decode_kernel(const DecodeParams p) {
       const float l_tot = sum4rows(ol_run);
       const int h0 = first_head(p, hg, GC);
       const int nv = heads_in_group(p, hg, GC);
+      const float vs = C::kFp8 ? p.v_scale : 1.f;  // partials hold the values' scale
       if (pc_seg_start && (info & kSegEnd)) {  // a whole segment: final output
         if (row < nv) {
-          const float inv = 1.f / l_tot;
+          const float inv = vs / l_tot;
           char* dst = (char*)p.out + (((int64_t)s * p.num_heads + h0 + row) * D + 4 * jg) * C::kEszQ;
 #pragma unroll
           for (int b = 0; b < C::kNdb; ++b) store4<DT>(dst + 16 * b * C::kEszQ, oacc[b] * inv);
@@ -1006,8 +1035,8 @@ paged_decode_kernel(const DecodeParams p) {
         float* dst = p.part_acc + (slot * GC + row) * D + 4 * jg;
 #pragma unroll
         for (int b = 0; b < C::kNdb; ++b)
-          store16(dst + 16 * b, u32x4{bits_of(oacc[b][0]), bits_of(oacc[b][1]),
-                                      bits_of(oacc[b][2]), bits_of(oacc[b][3])});
+          store16(dst + 16 * b, u32x4{bits_of(oacc[b][0] * vs), bits_of(oacc[b][1] * vs),
+                                      bits_of(oacc[b][2] * vs), bits_of(oacc[b][3] * vs)});
         if (jg == 0) {
           p.part_ml[(slot * GC + row) * 2 + 0] = om_run;
           p.part_ml[(slot * GC + row) * 2 + 1] = l_tot;
@@ -1181,7 +1210,7 @@ static hipError_t dispatch_gc(const DecodeParams& a, int gc, hipStream_t st) {
     case 4: return launch_decode<DT, KT, D, 4>(a, st);
     case 8: return launch_decode<DT, KT, D, 8>(a, st);
     default:
-      if constexpr (KT == DT && DT != PKV_F32) return launch_decode<DT, KT, D, 16>(a, st);
+      if constexpr (DT != PKV_F32) return launch_decode<DT, KT, D, 16>(a, st);
       return hipErrorInvalidValue;  // never chosen for these pools
   }
 }
@@ -1193,7 +1222,7 @@ static hipError_t dispatch_d(const DecodeParams& a, int d, int gc, hipStream_t s
 
 // Heads per head group: the smallest power of two that holds a kv head's
 // query heads, at most 16 where both products run on the matrix cores
-// (16-bit pools, whose lane columns hold 16 heads) and 8 otherwise (larger
+// (16-bit queries, whose lane columns hold 16 heads) and 8 otherwise (larger
 // groups are cut into groups of that size, the last one possibly partial).
 // One wave then reads each tile for all of them.
 static int heads_per_wg(int num_heads, int num_kv_heads, bool matrix_pv) {
@@ -1297,7 +1326,7 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
       15u)
     return PKV_ERR_INVALID_ARG;  // rows are read and written 16 bytes at a time
   // 16 heads per group only where both products run on the matrix cores
-  const bool matrix_pv = kv_dtype == dtype && dtype != PKV_F32;
+  const bool matrix_pv = dtype != PKV_F32;
   const int gc = heads_per_wg(num_heads, num_kv_heads, matrix_pv);
   const int64_t hgs = head_groups_of(num_heads, num_kv_heads, gc);
   if (hgs > 0xFFFF) return PKV_ERR_INVALID_ARG;  // head group: 16 bits

@@ -111,7 +111,7 @@ def test_fp8_full_size_sampled(gpu_lib, key):
     full_step_and_check(b, seqs=sample_seqs(b["context_lens"]))
 
 
-GROUPS = [(4, 4), (8, 2), (8, 1), (16, 2), (6, 2), (10, 2), (28, 4), (12, 1)]
+GROUPS = [(4, 4), (8, 2), (8, 1), (16, 2), (6, 2), (10, 2), (28, 4), (12, 1), (32, 2)]
 
 
 @pytest.mark.parametrize("hq,hkv", GROUPS)
