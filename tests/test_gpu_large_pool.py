@@ -89,6 +89,22 @@ def test_decode_beyond_4gib(gpu_lib, big, ps):
     assert n < 200 and torch.equal(bits(out), bits(out2))
 
 
+@pytest.mark.parametrize("group", [4, 16])
+def test_grouped_decode_beyond_4gib(gpu_lib, big, group):
+    """4 and 16 query heads per kv head: the matrix-core path (both products
+    on MFMA, values through LDS) on the same pool beyond 4 GiB."""
+    b = big
+    g = torch.Generator(device=DEV).manual_seed(11 + group)
+    q = torch.randn((len(LENS), HKV * group, D), generator=g, device=DEV).half()
+    out = torch.empty_like(q)
+    pkv.paged_attention_decode(out, q, b["kc"], b["vc"], dev_i32(b["bt"]), dev_i32(b["lens"]),
+                               float(SCALE), HKV, partition_size=512, validate=True)
+    torch.cuda.synchronize()
+    kh, vh, tables, _ = sub_pool(b["kc"], b["vc"], b["bt"], b["lens"])
+    ref = oracle.decode_attention(wl.to_host(q), kh, vh, tables, b["lens"], SCALE, HKV, "f16")
+    assert_close(out, ref, "f16", f"decode, {group} heads per kv head, pool beyond 4 GiB")
+
+
 def test_cache_ops_and_append_beyond_4gib(gpu_lib, big):
     """copy_blocks between high blocks, reshape_and_cache into high slots,
     then the decode call that caches each sequence's newest token there."""
