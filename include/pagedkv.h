@@ -148,9 +148,10 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
  * Bytes of workspace paged_attention_decode needs for these sizes.  One
  * launch (at most 2048 sequences) splits its (block, kv head) tiles into at
  * most ranges = max(4096, tiles / (partition_size / 16)) equal ranges; the
- * workspace holds a 256-byte header, a 16-byte descriptor per range and two
- * float32 partial states per range (head_size + 2 floats for each query head
- * of a group), each part rounded up to 256 bytes.  Depends only on the
+ * workspace holds a 256-byte header, two 16-byte descriptors per range and
+ * two float32 partial states per range (head_size + 2 floats for each query
+ * head of a group: up to 16 heads with 16-bit queries when a kv head serves
+ * more than 8, else up to 8), each part rounded up to 256 bytes.  Depends only on the
  * arguments (no device query).  Returns 0 for invalid sizes, which
  * paged_attention_decode then rejects.
  */

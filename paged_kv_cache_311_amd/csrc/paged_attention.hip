@@ -178,6 +178,7 @@ struct DecodeParams {
   int r_max;           // ranges the workspace holds
   int* header;         // [2]  ranges R and tiles per range q of this call
   int4* desc;          // [R]  split segment ending in range r: s, hg, P, nb
+  int4* desc_first;    // [R]  split segment holding range r's first tile: s, hg, P, nb
   float* part_ml;      // [R][2][GC][2]  running max (log2 units), sum
   float* part_acc;     // [R][2][GC][D]  unnormalized accumulator
   // Appending variant (null otherwise): each sequence's newest token
@@ -438,6 +439,17 @@ template <int D, int GC>
 struct FoldState {
   static constexpr int kChunks = GC * D / 4;
   static constexpr int kCpl = (kChunks + kWave - 1) / kWave;
+  // pieces whose loads go out together (registers: kBatch x kCpl chunks)
+  static constexpr int kBatch = kCpl == 1 ? 8 : (kCpl <= 4 && GC < 16 ? 4 : 2);
+  // Slices of a segment's merge over the waves of its ranges hold at least
+  // 8 chunks each; they pay only when a state has more of them than the
+  // four waves of a workgroup could take.  Then a workgroup merges a
+  // segment in at most two batches per wave and slices take longer ones
+  // (at once for groups of 16 heads, whose workgroup merge would spill).
+  static constexpr int kMaxSlices = (kChunks + 7) / 8;
+  static constexpr bool kSliced = kMaxSlices > kWavesPerWG;
+  static constexpr int kWorkgroupPieces =
+      !kSliced ? 0x7fffffff : (GC >= 16 ? 8 : 2 * kWavesPerWG * kBatch);
   float M[GC], S[GC];
   floatx4 O[kCpl];
 };
@@ -472,7 +484,7 @@ template <int D, int GC>
 __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int kstep,
                             int lane, FoldState<D, GC>& st) {
   using F = FoldState<D, GC>;
-  constexpr int kBatch = F::kCpl == 1 ? 8 : (F::kCpl <= 4 ? 4 : 2);
+  constexpr int kBatch = F::kBatch;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     st.M[g] = -INFINITY;
@@ -606,6 +618,69 @@ __device__ void merge_by_workgroup(const DecodeParams& p, const Split& sp, int l
   __syncthreads();
 }
 
+// A segment split into more pieces than a workgroup merges in two batches
+// is merged by the waves of the ranges it spans.  With n ranges whose first
+// tile lies in the segment (at most one per 8 chunks), the k-th of them
+// takes the k-th of n contiguous runs of the [GC][D] accumulator's 16-B
+// chunks.  Its lanes are 8 chunk
+// lanes x 8 piece lanes: lane (c, i) folds chunk c of pieces i, i + 8, ...
+// (8 pieces' loads go out together; 8 chunk lanes read 128 contiguous bytes
+// of a piece), then the 8 piece lanes of each chunk are combined.
+constexpr int kSliceChunkLanes = 8;
+constexpr int kSlicePieceLanes = kWave / kSliceChunkLanes;
+constexpr int kSliceUnroll = 8;
+
+template <int DT, int D, int GC>
+__device__ void merge_slice(const DecodeParams& p, const Split& sp, int r, int lane) {
+  constexpr int kChunks = GC * D / 4;
+  const int first = sp.rf + (sp.rf_tail ? 1 : 0);  // range rf starts in another segment
+  // slices of at least kSliceChunkLanes chunks: a wave's round trip then
+  // brings a full row of chunk lanes (narrow states use the first few ranges)
+  const int n = min(sp.rf + sp.np - first, FoldState<D, GC>::kMaxSlices);
+  const int cpp = (kChunks + n - 1) / n;
+  const int cbeg = (r - first) * cpp;
+  const int cend = min(cbeg + cpp, kChunks);
+  const int cl = lane % kSliceChunkLanes;
+  const int pl = lane / kSliceChunkLanes;
+  for (int c0 = cbeg; c0 < cend; c0 += kSliceChunkLanes) {
+    const int c = min(c0 + cl, cend - 1);
+    const int g = c * 4 / D;
+    float M = -INFINITY, S = 0.f;
+    floatx4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < sp.np; i0 += kSlicePieceLanes * kSliceUnroll) {
+      float mm[kSliceUnroll], ll[kSliceUnroll];
+      u32x4 aa[kSliceUnroll];
+#pragma unroll
+      for (int u = 0; u < kSliceUnroll; ++u) {
+        const int i = min(i0 + pl + u * kSlicePieceLanes, sp.np - 1);
+        const int64_t sl = piece_slot(sp, i);
+        mm[u] = p.part_ml[(sl * GC + g) * 2 + 0];
+        ll[u] = p.part_ml[(sl * GC + g) * 2 + 1];
+        aa[u] = load16(p.part_acc + sl * GC * D + c * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < kSliceUnroll; ++u) {
+        if (i0 + pl + u * kSlicePieceLanes >= sp.np) break;
+        const float Mn = fmaxf(M, mm[u]);  // every piece's max is finite
+        const float a = __builtin_amdgcn_exp2f(M - Mn);
+        const float b = __builtin_amdgcn_exp2f(mm[u] - Mn);
+        S = S * a + ll[u] * b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] = fmaf(O[e], a, b * float_of(aa[u][e]));
+        M = Mn;
+      }
+    }
+    // lanes without a piece hold max -inf and weigh 0
+    const float Mw = max_over_lane_groups<kSliceChunkLanes>(M);
+    const float wt = __builtin_amdgcn_exp2f(M - Mw);
+    const float Sw = sum_over_lane_groups<kSliceChunkLanes>(S * wt);
+    floatx4 Ow;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ow[e] = sum_over_lane_groups<kSliceChunkLanes>(O[e] * wt);
+    if (pl == 0 && c0 + cl < cend) store_merged<DT, D, GC>(p, sp, c0 + cl, Ow, 1.f / Sw);
+  }
+}
+
 // ------------------------------------------------------------ main kernel --
 constexpr int kPrepAhead = 3;   // tiles left in a window when the next one is prepared
 
@@ -679,6 +754,11 @@ __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const
       // a range's first piece is the last piece of a split segment exactly
       // when the segment began in an earlier range and ends in this one
       p.desc[r] = (n > 0 && nb - n <= x1 - x0) ? int4{s, hg, x - n, nb} : int4{-1, 0, 0, 0};
+      // and the segment this range starts in, when it spans several ranges
+      // (for merges in slices)
+      if (p.desc_first != nullptr)
+        p.desc_first[r] =
+            (n > 0 || nb - n > x1 - x0) ? int4{s, hg, x - n, nb} : int4{-1, 0, 0, 0};
     }
     wd.info = f;
   }
@@ -1125,19 +1205,24 @@ paged_decode_kernel(const DecodeParams p) {
 }
 
 // ----------------------------------------------------------- merge kernel --
-// Workgroups take four ranges at a time; a range whose descriptor names a
-// split segment gets that segment's pieces merged into its output.  A wave
-// loads its range's descriptor together with the header (the workspace
-// holds r_max descriptors, so the load is in bounds before R is known).
+// A wave per range, workgroups taking four ranges at a time.  A range whose
+// descriptor names a split segment of few pieces merges it alone; the four
+// waves together merge a segment of more pieces; every range of a segment
+// split into still more pieces takes its slice of that segment's merge.  A
+// wave loads the next descriptors while it merges (the workspace holds
+// r_max of each, so the loads are in bounds before R is known).
 template <int DT, int D, int GC>
-__global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void paged_decode_merge_kernel(const DecodeParams p) {
+  using F = FoldState<D, GC>;
   __shared__ MergeSmem<D, GC> sm;
   __shared__ int4 sm_desc[kWavesPerWG];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = sread(threadIdx.x >> 6);
   const int stride = gridDim.x * kWavesPerWG;
+  const int4 none = int4{-1, 0, 0, 0};
   int base = blockIdx.x * kWavesPerWG;
-  int4 dn = base + w < p.r_max ? p.desc[base + w] : int4{-1, 0, 0, 0};
+  int4 dn = base + w < p.r_max ? p.desc[base + w] : none;
+  int4 fn = F::kSliced && base + w < p.r_max ? p.desc_first[base + w] : none;
   RangeMap m;
   const int R = p.header[0];
   m.R = R;
@@ -1145,14 +1230,20 @@ __global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const Deco
   m.T = 0;  // range ends are not needed here
   for (; base < R; base += stride) {
     const int r = base + w;
-    const int4 d = r < R ? dn : int4{-1, 0, 0, 0};
-    if (r + stride < min(R, p.r_max)) dn = p.desc[r + stride];
-    // each wave merges its own range's segment if it has few pieces ...
+    const int4 d = r < R ? dn : none;
+    const int4 f = r < R ? fn : none;
+    if (r + stride < min(R, p.r_max)) {
+      dn = p.desc[r + stride];
+      if constexpr (F::kSliced) fn = p.desc_first[r + stride];
+    }
     if (d.x >= 0) {
       const Split sp = split_of(d, m);
       if (sp.np <= kSoloPieces) merge_by_wave<DT, D, GC>(p, sp, lane);
     }
-    // ... and the four waves together take those with many
+    if (F::kSliced && f.x >= 0) {
+      const Split sp = split_of(f, m);
+      if (sp.np > F::kWorkgroupPieces) merge_slice<DT, D, GC>(p, sp, r, lane);
+    }
     if (lane == 0) sm_desc[w] = d;
     __syncthreads();
 #pragma unroll 1
@@ -1160,7 +1251,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_merge_kernel(const Deco
       const int4 du = sm_desc[u];
       if (du.x < 0) continue;
       const Split sp = split_of(du, m);
-      if (sp.np > kSoloPieces) merge_by_workgroup<DT, D, GC>(p, sp, lane, w, sm);
+      if (sp.np > kSoloPieces && sp.np <= F::kWorkgroupPieces)
+        merge_by_workgroup<DT, D, GC>(p, sp, lane, w, sm);
     }
     __syncthreads();
   }
@@ -1191,7 +1283,8 @@ static int resident_workgroups(const void* kernel, int waves_per_simd) {
 }
 
 template <int DT, int KT, int D, int GC>
-static hipError_t launch_decode(const DecodeParams& a, hipStream_t st) {
+static hipError_t launch_decode(DecodeParams a, hipStream_t st) {
+  if (!FoldState<D, GC>::kSliced) a.desc_first = nullptr;  // no merges in slices
   const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC>);
   const int nwg = resident_workgroups(k, DecodeCfg<DT, KT, D, GC>::kGridWaves);
   if (nwg <= 0) return hipErrorInvalidDevice;
@@ -1246,18 +1339,20 @@ static int64_t max_ranges(int64_t max_tiles, int tile_cap) {
   return r;
 }
 
-// Workspace: header [2 ints], range descriptors [r][4 ints], then (max,
-// sum) [r][2][gc][2] and accumulators [r][2][gc][head_size] in float32;
-// each part 256-B aligned.  Every call writes what it reads.
+// Workspace: header [2 ints], two range descriptors [r][4 ints] each (the
+// split segment ending in the range, the one its first tile lies in), then
+// (max, sum) [r][2][gc][2] and accumulators [r][2][gc][head_size] in
+// float32; each part 256-B aligned.  Every call writes what it reads.
 struct WorkspaceLayout {
-  size_t header, desc, part_ml, part_acc, total;
+  size_t header, desc, desc_first, part_ml, part_acc, total;
 };
 static WorkspaceLayout workspace_layout(int64_t r, int gc, int head_size) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WorkspaceLayout l;
   l.header = 0;
   l.desc = 256;
-  l.part_ml = up(l.desc + (size_t)r * 16);
+  l.desc_first = up(l.desc + (size_t)r * 16);
+  l.part_ml = up(l.desc_first + (size_t)r * 16);
   l.part_acc = up(l.part_ml + (size_t)r * 2 * gc * 2 * sizeof(float));
   l.total = up(l.part_acc + (size_t)r * 2 * gc * head_size * sizeof(float));
   return l;
@@ -1364,6 +1459,7 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   const WorkspaceLayout wl = workspace_layout(r, gc, head_size);
   a.header = (int*)((char*)workspace + wl.header);
   a.desc = (int4*)((char*)workspace + wl.desc);
+  a.desc_first = (int4*)((char*)workspace + wl.desc_first);
   a.part_ml = (float*)((char*)workspace + wl.part_ml);
   a.part_acc = (float*)((char*)workspace + wl.part_acc);
   hipStream_t st = (hipStream_t)stream;

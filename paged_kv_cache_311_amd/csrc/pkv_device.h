@@ -220,6 +220,15 @@ __device__ __forceinline__ float sum_over_lane_groups(float x) {
   return x;
 }
 
+// Max of x over the same lanes as sum_over_lane_groups.
+template <int STRIDE>
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  if constexpr (STRIDE <= 4) x = fmaxf(x, dpp_f<kDppRowRor4>(x));
+  if constexpr (STRIDE <= 8) x = fmaxf(x, dpp_f<kDppRowRor8>(x));
+  if constexpr (STRIDE <= 16) x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+
 __device__ __forceinline__ float uniform(float x) {
   return __builtin_bit_cast(float,
                             __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));

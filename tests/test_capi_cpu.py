@@ -75,11 +75,11 @@ def test_status_strings(lib):
 
 
 def expected_workspace(ranges, gc, head_size):
-    """The documented layout: a 256-B header, 16-B range descriptors, then
-    (max, sum) and accumulator partials for 2 pieces per range, each part
-    rounded up to 256 bytes."""
+    """The documented layout: a 256-B header, two 16-B descriptors per range,
+    then (max, sum) and accumulator partials for 2 pieces per range, each
+    part rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
-    return (256 + up(ranges * 16) + up(ranges * 2 * gc * 2 * 4)
+    return (256 + 2 * up(ranges * 16) + up(ranges * 2 * gc * 2 * 4)
             + up(ranges * 2 * gc * head_size * 4))
 
 

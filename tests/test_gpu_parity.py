@@ -124,6 +124,22 @@ def test_sharp_softmax(gpu_lib, dtype, hq, hkv):
     assert_close(out, ref, dtype, f"sharp softmax {dtype} {hq}/{hkv}")
 
 
+@pytest.mark.parametrize("ps", [16, 48])
+@pytest.mark.parametrize("hq,hkv", [(8, 4), (8, 2), (16, 2), (32, 2), (24, 1)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_many_piece_merges(gpu_lib, dtype, hq, hkv, ps):
+    """Pieces of one or three tiles split segments up to 128 ways: the merge
+    folds them in one wave, in a workgroup, or in slices over the waves of
+    the segment's ranges (2 to 16 heads per group, partial groups too)."""
+    lens = [2048, 1500, 700, 33, 1]
+    w = wl.custom(lens, hq, hkv, 128, dtype, max_len=2048, partition_size=ps)
+    b = wl.make_batch(w, 17 + hq + ps, DEV)
+    kc0, vc0 = clone_pools(b)
+    out = run_decode(b)
+    ref = oracle_decode_subset(b, kc0, vc0, list(range(len(lens))))
+    assert_close(out, ref, dtype, f"many pieces {dtype} {hq}/{hkv} ps={ps}")
+
+
 def test_placement_permutation_is_bitwise_invariant(gpu_lib):
     w = dataclasses.replace(W["opt13b"], num_seqs=8)
     b = wl.make_batch(w, 777, DEV)
