@@ -132,8 +132,12 @@ const char* pkv_build_id(void);
  * sequences run as consecutive launches of 2048.
  *
  * Accumulation is float32 for every dtype; the output is rounded to
- * nearest-even into `dtype`.  num_seqs * max_blocks_per_seq * (num_heads /
- * heads per workgroup) must be below 2^31.
+ * nearest-even into `dtype`.  With 16-bit queries and four or more query
+ * heads per kv head, both products run on the matrix cores: the
+ * probabilities enter the second one as their 16-bit rounding plus the
+ * remainder of that rounding, so it keeps float32 accuracy.
+ * num_seqs * max_blocks_per_seq * (num_heads / heads per workgroup) must be
+ * below 2^31.
  */
 int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            const void* value_cache, const int32_t* block_tables,
