@@ -150,6 +150,21 @@ def test_fp8_edge_lengths(gpu_lib, dtype):
     assert torch.equal(bits(got), bits(want))
 
 
+@pytest.mark.parametrize("ps", [16, 48])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (32, 2)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fp8_many_piece_merges(gpu_lib, dtype, hq, hkv, ps):
+    """E4M3 pools on the matrix-core path with segments split up to 128 ways:
+    the merges in a workgroup and in slices over the segment's ranges."""
+    lens = [2048, 1500, 700, 33, 1]
+    w = wl.custom(lens, hq, hkv, 128, dtype, max_len=2048, partition_size=ps, **ODD)
+    b = wl.make_batch(w, 23 + hq + ps, DEV)
+    kc0, vc0 = clone_pools(b)
+    out = run_decode(b)
+    ref = oracle_decode_subset(b, kc0, vc0, list(range(len(lens))))
+    assert_close(out, ref, dtype, f"e4m3 many pieces {dtype} {hq}/{hkv} ps={ps}")
+
+
 @pytest.mark.parametrize("ps", [0, 16, 128, 512, 4096])
 def test_fp8_partition_sizes(gpu_lib, ps):
     w = fp8_variant("opt13b", num_seqs=6)
