@@ -10,6 +10,14 @@ attention are one call, paged_attention_decode_append (--no-fuse keeps
 them apart).  Inputs are resident in HBM
 before the timed region; K steps are timed between two synchronizations.
 
+Each workload is measured in a child process of its own (the headline one,
+with the CPU baseline and the translation legs, first), as a serving process
+allocates its pools once at start-up; this process touches no GPU and only
+spawns and collects.  --same-process measures them all in one process (then
+later workloads run on pools allocated after earlier ones were freed, which
+reads 1-4% slower), and so does a run with empty --also and --prefill lists,
+as under a profiler.
+
 Prints ONE JSON line.  `value` is whole-step KV throughput in GB/s: the
 key/value bytes the attention must read (sum of context lengths x 2 x
 kv_heads x head_size x element bytes) divided by the step time.
@@ -36,6 +44,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -70,6 +79,11 @@ def parse():
                     help="cache new tokens with reshape_and_cache instead of the decode call")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="cap on tokens per piece (default: the workload's, 0 = none)")
+    ap.add_argument("--same-process", action="store_true",
+                    help="measure every workload in this one process (later ones then run "
+                         "on pools allocated after earlier ones were freed)")
+    ap.add_argument("--child", default="",
+                    help=argparse.SUPPRESS)  # internal: measure one workload, print its result
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (steps "
                          "times), to scale HBM byte counters; prints one JSON line")
@@ -508,6 +522,52 @@ def _cpu_model():
     return "unknown"
 
 
+def run_child(a, job):
+    """Measure in a child process of its own and return its JSON result.
+
+    Called only from a parent that has not initialised the GPU (it spawns,
+    the children measure)."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--child", job, "--workload", a.workload,
+           "--steps", str(a.steps), "--warmup", str(a.warmup),
+           "--cpu-seconds", str(a.cpu_seconds)]
+    if a.partition_size is not None:
+        cmd += ["--partition-size", str(a.partition_size)]
+    for flag in ("no_fuse", "no_cpu_baseline", "no_translation"):
+        if getattr(a, flag):
+            cmd.append("--" + flag.replace("_", "-"))
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    if r.returncode != 0:
+        print(f"bench.py: measuring {job} failed (status {r.returncode})", file=sys.stderr)
+        sys.exit(1)
+    return json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1])
+
+
+def child(a):
+    """One measurement in this process: the headline workload with the CPU
+    baseline and the translation legs ("main"), or one other workload."""
+    import torch
+    import paged_kv_cache_311_amd as pkv
+    from paged_kv_cache_311_amd import workloads as wl
+    pkv.load_library()
+    if a.child == "main":
+        w = wl.WORKLOADS[a.workload]
+        print(f"# measuring {w.key}", file=sys.stderr, flush=True)
+        r, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size, not a.no_fuse)
+        cpu = None if a.no_cpu_baseline else cpu_baseline(st, a.cpu_seconds)
+        trans = None if a.no_translation else translation_overhead(st, a.steps)
+        out = {"main": r, "cpu": cpu, "trans": trans}
+    else:
+        w = wl.WORKLOADS[a.child]
+        print(f"# measuring {w.key}", file=sys.stderr, flush=True)
+        if w.step == "prefill":
+            out = measure_prefill(w, w.default_seed, a.steps, a.warmup)
+        else:
+            out, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size,
+                              not a.no_fuse)
+    torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -515,17 +575,41 @@ def main():
               "(this path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.child:
+        child(a)
+        return
+    if a.copy_calibration_mib:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        copy_calibration(a.copy_calibration_mib, a.steps)
+        return
+    from paged_kv_cache_311_amd import workloads as wl
+    w = wl.WORKLOADS[a.workload]
+    also = [k for k in a.also.split(",") if k and k != w.key]
+    pre = [k for k in a.prefill.split(",") if k]
+    if also or pre:
+        if not a.same_process:
+            # One process per workload, as a serving process allocates its
+            # pools once at start-up: measured in one process after others
+            # were freed, later workloads run 1-4% slower (long_gqa 336 ->
+            # 350 us per call).  This process touches no GPU (counting
+            # devices does not initialise it) and only spawns.
+            if torch.cuda.device_count() < 1:
+                print("bench.py needs a GPU", file=sys.stderr)
+                sys.exit(2)
+            m = run_child(a, "main")
+            main_r, cpu, trans = m["main"], m["cpu"], m["trans"]
+            others = {k: run_child(a, k) for k in also}
+            prefill = {k: run_child(a, k) for k in pre}
+            emit(a, w, main_r, cpu, trans, others, prefill)
+            return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if a.copy_calibration_mib:
-        copy_calibration(a.copy_calibration_mib, a.steps)
-        return
     import paged_kv_cache_311_amd as pkv
-    from paged_kv_cache_311_amd import workloads as wl
     pkv.load_library()
 
-    w = wl.WORKLOADS[a.workload]
     print(f"# measuring {w.key}", file=sys.stderr, flush=True)
     main_r, st = measure(w, w.default_seed, a.steps, a.warmup, a.partition_size,
                          not a.no_fuse)
@@ -535,7 +619,7 @@ def main():
     torch.cuda.empty_cache()
 
     others = {}
-    for key in [k for k in a.also.split(",") if k and k != w.key]:
+    for key in also:
         print(f"# measuring {key}", file=sys.stderr, flush=True)
         ow = wl.WORKLOADS[key]
         r, st = measure(ow, ow.default_seed, a.steps, a.warmup, a.partition_size,
@@ -545,12 +629,16 @@ def main():
         torch.cuda.empty_cache()
 
     prefill = {}
-    for key in [k for k in a.prefill.split(",") if k]:
+    for key in pre:
         print(f"# measuring {key}", file=sys.stderr, flush=True)
         pw = wl.WORKLOADS[key]
         prefill[key] = measure_prefill(pw, pw.default_seed, a.steps, a.warmup)
         torch.cuda.empty_cache()
+    emit(a, w, main_r, cpu, trans, others, prefill)
 
+
+def emit(a, w, main_r, cpu, trans, others, prefill):
+    """Print the one JSON line."""
     dec_ms = main_r["decode_call_ms_avg"]
     achieved = main_r["decode_GBps"]
     line = {
