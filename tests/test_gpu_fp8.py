@@ -150,6 +150,21 @@ def test_fp8_edge_lengths(gpu_lib, dtype):
     assert torch.equal(bits(got), bits(want))
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (32, 2)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fp8_sharp_softmax(gpu_lib, dtype, hq, hkv):
+    """Queries scaled by 8 (exact): logits 8 times larger, so the running max
+    jumps past the lazy rescale threshold of the matrix-core path often."""
+    lens = [1, 17, 300, 1000, 2047]
+    w = wl.custom(lens, hq, hkv, 128, dtype, max_len=2048, partition_size=512, **ODD)
+    b = wl.make_batch(w, 9 + hq + hkv, DEV)
+    b["query"].mul_(8)
+    kc0, vc0 = clone_pools(b)
+    out = run_decode(b)
+    ref = oracle_decode_subset(b, kc0, vc0, list(range(len(lens))))
+    assert_close(out, ref, dtype, f"e4m3 sharp softmax {dtype} {hq}/{hkv}")
+
+
 @pytest.mark.parametrize("ps", [16, 48])
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (32, 2)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

@@ -252,7 +252,7 @@ def test_workspace_reused_across_calls(gpu_lib):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("key", ["opt13b", "gqa"])
+@pytest.mark.parametrize("key", ["opt13b", "gqa", "gqa16"])
 def test_graph_replay_matches_eager(gpu_lib, key, fused):
     """One step (reshape_and_cache, then decode; or the one call that does
     both) captured in a HIP graph and replayed: every replay, with eager
@@ -260,6 +260,8 @@ def test_graph_replay_matches_eager(gpu_lib, key, fused):
     output matches the oracle."""
     if key == "gqa":
         w = wl.custom([5, 700, 33, 1200, 2048, 16], 32, 8, 128, "bf16", max_len=2048)
+    elif key == "gqa16":  # 16 heads per group; segments split 32 ways, merged in slices
+        w = wl.custom([5, 700, 33, 1200, 2048, 16], 32, 2, 128, "bf16", max_len=2048)
     else:
         w = dataclasses.replace(W["opt13b"], num_seqs=8)
     b = wl.make_batch(w, 7, DEV)
