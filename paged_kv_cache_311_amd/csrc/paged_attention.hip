@@ -477,6 +477,70 @@ __device__ __forceinline__ int64_t piece_slot(const Split& sp, int k) {
   return (int64_t)(sp.rf + k) * 2 + ((k == 0 && sp.rf_tail) ? 1 : 0);
 }
 
+// One piece's partials as a lane holds them: (max, sum) per head, and the
+// lane's chunks of the accumulator.
+template <int D, int GC>
+struct PieceRegs {
+  float ml[GC][2];
+  u32x4 ac[FoldState<D, GC>::kCpl];
+};
+
+template <int D, int GC>
+__device__ __forceinline__ void load_piece(const DecodeParams& p, int64_t sl, int lane,
+                                           PieceRegs<D, GC>& x) {
+  using F = FoldState<D, GC>;
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    x.ml[g][0] = p.part_ml[(sl * GC + g) * 2 + 0];
+    x.ml[g][1] = p.part_ml[(sl * GC + g) * 2 + 1];
+  }
+#pragma unroll
+  for (int j = 0; j < F::kCpl; ++j) {
+    const int c = min(lane + j * kWave, F::kChunks - 1);
+    x.ac[j] = load16(p.part_acc + sl * GC * D + c * 4);
+  }
+}
+
+template <int D, int GC>
+__device__ __forceinline__ void fold_init(FoldState<D, GC>& st) {
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    st.M[g] = -INFINITY;
+    st.S[g] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < FoldState<D, GC>::kCpl; ++j) st.O[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+// st <- st folded with one more piece (every piece's max is finite)
+template <int D, int GC>
+__device__ __forceinline__ void fold_one(FoldState<D, GC>& st, const PieceRegs<D, GC>& x,
+                                         int lane) {
+  using F = FoldState<D, GC>;
+  float a[GC], bb[GC];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    const float mk = x.ml[g][0];
+    const float Mn = fmaxf(st.M[g], mk);
+    a[g] = __builtin_amdgcn_exp2f(st.M[g] - Mn);
+    bb[g] = __builtin_amdgcn_exp2f(mk - Mn);
+    st.S[g] = st.S[g] * a[g] + x.ml[g][1] * bb[g];
+    st.M[g] = Mn;
+  }
+#pragma unroll
+  for (int j = 0; j < F::kCpl; ++j) {
+    const int g = min(lane + j * kWave, F::kChunks - 1) * 4 / D;
+    float ag = a[0], bg = bb[0];
+#pragma unroll
+    for (int gg = 1; gg < GC; ++gg) {
+      ag = g == gg ? a[gg] : ag;
+      bg = g == gg ? bb[gg] : bg;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.O[j][e] = fmaf(st.O[j][e], ag, bg * float_of(x.ac[j][e]));
+  }
+}
+
 // Fold pieces k0, k0 + kstep, ... < np into `st`.  Loads go out in batches
 // with no wait between them (indices past the end are clamped to piece k0
 // and skipped when folding), so a batch costs one memory round trip.
@@ -485,30 +549,13 @@ __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int 
                             int lane, FoldState<D, GC>& st) {
   using F = FoldState<D, GC>;
   constexpr int kBatch = F::kBatch;
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    st.M[g] = -INFINITY;
-    st.S[g] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < F::kCpl; ++j) st.O[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  fold_init<D, GC>(st);
   for (int kb = k0; kb < sp.np; kb += kBatch * kstep) {
-    float ml[kBatch][GC][2];
-    u32x4 ac[kBatch][F::kCpl];
+    PieceRegs<D, GC> x[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int k = kb + b * kstep;
-      const int64_t sl = piece_slot(sp, k < sp.np ? k : k0);
-#pragma unroll
-      for (int g = 0; g < GC; ++g) {
-        ml[b][g][0] = p.part_ml[(sl * GC + g) * 2 + 0];
-        ml[b][g][1] = p.part_ml[(sl * GC + g) * 2 + 1];
-      }
-#pragma unroll
-      for (int j = 0; j < F::kCpl; ++j) {
-        const int c = min(lane + j * kWave, F::kChunks - 1);
-        ac[b][j] = load16(p.part_acc + sl * GC * D + c * 4);
-      }
+      load_piece<D, GC>(p, piece_slot(sp, k < sp.np ? k : k0), lane, x[b]);
     }
     // keep the whole batch's loads ahead of the folding (the scheduler
     // would otherwise interleave them, one round trip per piece)
@@ -516,29 +563,7 @@ __device__ void fold_pieces(const DecodeParams& p, const Split& sp, int k0, int 
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       if (kb + b * kstep >= sp.np) break;
-      float a[GC], bb[GC];
-#pragma unroll
-      for (int g = 0; g < GC; ++g) {
-        const float mk = ml[b][g][0];
-        const float Mn = fmaxf(st.M[g], mk);
-        a[g] = __builtin_amdgcn_exp2f(st.M[g] - Mn);
-        bb[g] = __builtin_amdgcn_exp2f(mk - Mn);
-        st.S[g] = st.S[g] * a[g] + ml[b][g][1] * bb[g];
-        st.M[g] = Mn;
-      }
-#pragma unroll
-      for (int j = 0; j < F::kCpl; ++j) {
-        const int g = min(lane + j * kWave, F::kChunks - 1) * 4 / D;
-        float ag = a[0], bg = bb[0];
-#pragma unroll
-        for (int gg = 1; gg < GC; ++gg) {
-          ag = g == gg ? a[gg] : ag;
-          bg = g == gg ? bb[gg] : bg;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st.O[j][e] = fmaf(st.O[j][e], ag, bg * float_of(ac[b][j][e]));
-      }
+      fold_one<D, GC>(st, x[b], lane);
     }
   }
 }
@@ -553,12 +578,11 @@ __device__ __forceinline__ void store_merged(const DecodeParams& p, const Split&
   store4<DT>(dst, o * inv);
 }
 
-// A segment of few pieces: one wave folds them all and writes the output.
+// The merged output of a segment from its folded state.
 template <int DT, int D, int GC>
-__device__ void merge_by_wave(const DecodeParams& p, const Split& sp, int lane) {
+__device__ __forceinline__ void store_state(const DecodeParams& p, const Split& sp,
+                                            const FoldState<D, GC>& st, int lane) {
   using F = FoldState<D, GC>;
-  F st;
-  fold_pieces<D, GC>(p, sp, 0, 1, lane, st);
 #pragma unroll
   for (int j = 0; j < F::kCpl; ++j) {
     const int c = lane + j * kWave;
@@ -570,6 +594,14 @@ __device__ void merge_by_wave(const DecodeParams& p, const Split& sp, int lane) 
       store_merged<DT, D, GC>(p, sp, c, st.O[j], 1.f / sg);
     }
   }
+}
+
+// A segment of few pieces: one wave folds them all and writes the output.
+template <int DT, int D, int GC>
+__device__ void merge_by_wave(const DecodeParams& p, const Split& sp, int lane) {
+  FoldState<D, GC> st;
+  fold_pieces<D, GC>(p, sp, 0, 1, lane, st);
+  store_state<DT, D, GC>(p, sp, st, lane);
 }
 
 // A segment of many pieces: wave w folds pieces w, w+4, ...; the four wave
@@ -1223,6 +1255,19 @@ __global__ __launch_bounds__(kThreads, 2) void paged_decode_merge_kernel(const D
   int base = blockIdx.x * kWavesPerWG;
   int4 dn = base + w < p.r_max ? p.desc[base + w] : none;
   int4 fn = F::kSliced && base + w < p.r_max ? p.desc_first[base + w] : none;
+  // Most split segments of a batch of short contexts are cut once, between
+  // the end of range r - 1 and the start of range r: the partials of those
+  // two pieces are loaded with the first descriptor, and used if it names
+  // exactly that split (one round trip saved; slots 2r - 1 and 2r are
+  // inside the workspace whatever it holds).
+  constexpr bool kSpec = F::kCpl <= 2;
+  PieceRegs<D, GC> spec[kSpec ? 2 : 1];
+  const int r_spec = base + w;
+  if constexpr (kSpec) {
+    const int64_t s1 = r_spec < p.r_max ? 2 * (int64_t)r_spec : 0;
+    load_piece<D, GC>(p, s1 > 0 ? s1 - 1 : 0, lane, spec[0]);
+    load_piece<D, GC>(p, s1, lane, spec[1]);
+  }
   RangeMap m;
   const int R = p.header[0];
   m.R = R;
@@ -1238,7 +1283,15 @@ __global__ __launch_bounds__(kThreads, 2) void paged_decode_merge_kernel(const D
     }
     if (d.x >= 0) {
       const Split sp = split_of(d, m);
-      if (sp.np <= kSoloPieces) merge_by_wave<DT, D, GC>(p, sp, lane);
+      if (kSpec && r == r_spec && sp.np == 2 && sp.rf == r - 1 && sp.rf_tail) {
+        F st;
+        fold_init<D, GC>(st);
+        fold_one<D, GC>(st, spec[0], lane);
+        fold_one<D, GC>(st, spec[kSpec ? 1 : 0], lane);
+        store_state<DT, D, GC>(p, sp, st, lane);
+      } else if (sp.np <= kSoloPieces) {
+        merge_by_wave<DT, D, GC>(p, sp, lane);
+      }
     }
     if (F::kSliced && f.x >= 0) {
       const Split sp = split_of(f, m);
