@@ -1259,8 +1259,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_decode_merge_kernel(const D
   // the end of range r - 1 and the start of range r: the partials of those
   // two pieces are loaded with the first descriptor, and used if it names
   // exactly that split (one round trip saved; slots 2r - 1 and 2r are
-  // inside the workspace whatever it holds).
-  constexpr bool kSpec = F::kCpl <= 2;
+  // inside the workspace whatever it holds).  Only for states of one chunk
+  // per lane (one or two heads per group): wider groups come with long
+  // contexts split many ways, where the loads would be wasted.
+  constexpr bool kSpec = F::kCpl == 1;
   PieceRegs<D, GC> spec[kSpec ? 2 : 1];
   const int r_spec = base + w;
   if constexpr (kSpec) {
