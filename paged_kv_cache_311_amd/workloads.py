@@ -24,6 +24,8 @@ sampling over a shared prompt, long contexts):
   long_gqa       32 query heads over 8 kv heads of 128, bf16, 16 seqs of
                  32,768 tokens, pool 1.25x the need; contexts are split
                  into pieces merged through float32 (max, sum) states.
+  long_gqa_p512  long_gqa with the contexts split into partitions of 512
+                 tokens (64 pieces per sequence and kv head).
   opt13b_fp8,    the same shapes and lengths with pools of OCP E4M3 codes
   long_gqa_fp8   and one scale per pool (keys 1/64, values 3/128); queries,
                  outputs and new tokens stay fp16 / bf16.
@@ -131,6 +133,10 @@ WORKLOADS = {
                  prompts=32, samples=8),
         Workload("long_gqa", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
                  ("factor", 1.25), "decode", 32768),
+        # the same, split into the configured context partitions of 512
+        # tokens (32 blocks): 64 pieces per (sequence, kv head)
+        Workload("long_gqa_p512", 5, 16, 32, 8, 128, "bf16", ("fixed", 32768),
+                 ("factor", 1.25), "decode", 32768, partition_size=512),
         Workload("opt13b_fp8", 2, 64, 40, 40, 128, "f16", ("uniform", 1, 2048),
                  ("factor", 1.25), "decode", 2048, kv_dtype="e4m3",
                  k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE),

@@ -16,7 +16,7 @@ import paged_kv_cache_311_amd as pkv
 from paged_kv_cache_311_amd import workloads as wl
 from tests.gpu_helpers import (DEV, TOL, assert_close, bits, blocks_read_by, clone_pools,
                                dev_i32, full_step_and_check, gather_blocks,
-                               oracle_decode_subset, oracle_pool, run_decode, sample_seqs)
+                               oracle_decode_subset, oracle_pool, run_decode, sample_seqs, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +46,8 @@ def test_reduced_workload_every_output(gpu_lib, key, si):
     full_step_and_check(b)
 
 
-@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa", "beam",
-                                 "gqa8_long", "gqa16_long"])
+@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "sampling_cow", "long_gqa",
+                                 "long_gqa_p512", "beam", "gqa8_long", "gqa16_long"])
 def test_full_size_sampled(gpu_lib, key):
     """Full workload, launch configuration of the benchmark, oracle on a sample."""
     w = W[key]
@@ -159,22 +159,82 @@ def test_placement_permutation_is_bitwise_invariant(gpu_lib):
     assert torch.equal(bits(out), bits(out2))
 
 
-def test_split_matches_single_pass_closely(gpu_lib):
+def decode_with_header(b, ps):
+    """Decode with a workspace of our own; returns the output and the
+    launch's range map as the kernel recorded it in the workspace header:
+    (ranges, tiles per range)."""
+    w = b["workload"]
+    ws = torch.zeros(pkv.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads,
+                                         w.head_size, b["block_tables"].shape[1], ps),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(b["query"])
+    pkv.paged_attention_decode(out, b["query"], b["key_cache"], b["value_cache"],
+                               dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
+                               float(w.scale), w.num_kv_heads, partition_size=ps,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    hdr = ws[:8].view(torch.int32).cpu().tolist()
+    return out, (hdr[0], hdr[1])
+
+
+def test_split_policies_match_the_oracle(gpu_lib):
+    """One 32K-token grouped-query sequence at 512- and 4096-token pieces
+    and at the balanced default: each against the oracle."""
     w = dataclasses.replace(W["long_gqa"], num_seqs=1)
     b = wl.make_batch(w, 31337, DEV)
-    a = run_decode(b, partition_size=512).float()
-    c = run_decode(b, partition_size=4096).float()
-    d = run_decode(b, partition_size=0).float()
-    assert (a - c).abs().max().item() <= TOL["bf16"]
-    assert (a - d).abs().max().item() <= TOL["bf16"]
+    kc0, vc0 = clone_pools(b)
+    ref = oracle_decode_subset(b, kc0, vc0, [0])
+    maps = {}
+    for ps in (512, 4096, 0):
+        out, maps[ps] = decode_with_header(b, ps)
+        assert_close(out, ref, "bf16", f"one 32K sequence, partition {ps}: map {maps[ps]}")
+    assert maps[512][1] <= 32 and maps[4096][1] <= 256
 
 
-@pytest.mark.parametrize("ps", [0, 512])
-def test_long_gqa_reduced_with_cap(gpu_lib, ps):
-    """The 32K-token grouped-query workload at both piece policies."""
-    w = dataclasses.replace(W["long_gqa"], num_seqs=2, partition_size=ps)
+# (sequences, partition size): at 8 sequences the 512-token cap binds (the
+# balanced share of the grid is 64 tiles per range on 256 CUs, the cap 32),
+# at 2 sequences only a 128-token cap does (balanced: 16 tiles per range)
+@pytest.mark.parametrize("seqs,ps", [(2, 0), (2, 128), (8, 0), (8, 512)])
+def test_long_gqa_reduced_with_cap(gpu_lib, seqs, ps):
+    """The 32K-token grouped-query workload cut to a few sequences, at the
+    balanced split and at a piece cap that binds: the workspace header
+    shows which launch ran."""
+    w = dataclasses.replace(W["long_gqa"], num_seqs=seqs, partition_size=ps)
     b = wl.make_batch(w, 555, DEV)
-    full_step_and_check(b)
+    kc0, vc0 = clone_pools(b)
+    out, (R, q) = decode_with_header(b, ps)
+    T = seqs * 2048 * w.num_kv_heads          # tiles: blocks x head groups of 4 heads
+    say(f"    {seqs} seqs, partition {ps}: {R} ranges of {q} tiles")
+    assert R == -(-T // q)
+    if ps:
+        assert q == ps // 16, "the cap must bind in this case"
+    else:
+        nwaves = -(-T // q)                    # one range per wave when balanced
+        assert q > 32 if seqs == 8 else q > 8
+        assert nwaves <= 4096
+    seqs_checked = list(range(seqs)) if seqs <= 2 else [0, seqs - 1]
+    ref = oracle_decode_subset(b, kc0, vc0, seqs_checked)
+    assert_close(out[seqs_checked], ref, "bf16", f"long_gqa {seqs} seqs ps={ps}")
+
+
+def test_long_gqa_configured_partitions(gpu_lib):
+    """The long-context grouped-query workload exactly as configured: 16
+    sequences of 32,768 bf16 tokens, 32 query / 8 kv heads, split-context
+    partitions of 512 tokens (32 blocks) merged through float32 (max, sum)
+    states.  Every segment (sequence, kv head) of 2048 tiles is cut into 64
+    pieces, so the launch has 8192 ranges of 32 tiles; sampled sequences are
+    checked against the oracle."""
+    w = W["long_gqa_p512"]
+    assert w.partition_size == 512 and w.num_seqs == 16
+    b = wl.make_batch(w, w.default_seed, DEV)
+    kc0, vc0 = clone_pools(b)
+    out, (R, q) = decode_with_header(b, 512)
+    say(f"    long_gqa at 512-token partitions: {R} ranges of {q} tiles")
+    assert (R, q) == (8192, 32)
+    seqs = sample_seqs(b["context_lens"])
+    ref = oracle_decode_subset(b, kc0, vc0, seqs)
+    assert_close(out[seqs], ref, "bf16", f"long_gqa_p512 seqs={seqs}")
+    assert torch.isfinite(out.float()).all()
 
 
 def test_many_short_sequences_and_empties(gpu_lib):
