@@ -27,7 +27,8 @@
  * ---------------------------------------
  * Memory.  Every pointer argument is device memory owned by the caller
  * (the library allocates nothing and keeps no state beyond a per-device
- * memo of kernel occupancy; calls are reentrant).
+ * memo of kernel occupancy and, for paged_attention_decode_noalloc only,
+ * its fixed scratch array; calls are reentrant).
  * All tensors are dense, row-major, with no padding between rows.
  *
  * Element types (`dtype`): PKV_F32, PKV_F16 (IEEE binary16), PKV_BF16.
@@ -79,7 +80,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 5 */
+int pkv_abi_version(void);  /* 6 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -147,6 +148,37 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            int64_t num_blocks, int partition_size,
                            void* workspace, size_t workspace_bytes, int dtype,
                            void* stream);
+
+/*
+ * paged_attention_decode_noalloc: paged_attention_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The split-context workspace is a fixed device array of
+ * PKV_NOALLOC_SCRATCH_BYTES inside the library, one per device the library
+ * runs on, held until the process ends; the call allocates nothing (no
+ * hipMalloc, no allocating library routine).  Its first call on a device
+ * looks up that device's copy (with the device current).
+ *
+ * Arguments, results and errors are those of paged_attention_decode (16-
+ * and 32-bit pools, no new-token rows), with one more: sizes whose
+ * workspace would not fit the array -- ranges = max(waves of this device's
+ * grid, tiles of one launch / (partition_size / 16)), laid out as the
+ * workspace above for the head-group size this dtype uses -- return
+ * PKV_ERR_WORKSPACE before anything is enqueued.
+ *
+ * Every call on one device shares that device's array, and the array keeps
+ * the last call's contents (each call writes everything it reads, so
+ * nothing needs clearing).  Calls that overlap on one device -- on two
+ * streams, or from two threads without ordering -- race on it: order them.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale,
+                                   int num_kv_heads, int num_seqs, int num_heads,
+                                   int head_size, int block_size, int max_blocks_per_seq,
+                                   int64_t num_blocks, int partition_size, int dtype,
+                                   void* stream);
 
 /*
  * Bytes of workspace paged_attention_decode needs for these sizes.  One

@@ -49,6 +49,10 @@ def _declare(lib):
     lib.paged_attention_decode.argtypes = [
         vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
         c_i64, c_int, vp, c_sz, c_int, vp]
+    lib.paged_attention_decode_noalloc.restype = c_int
+    lib.paged_attention_decode_noalloc.argtypes = [
+        vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
+        c_i64, c_int, c_int, vp]
     lib.paged_attention_workspace_bytes.restype = c_sz
     lib.paged_attention_workspace_bytes.argtypes = [c_int] * 7
     lib.reshape_and_cache.restype = c_int
@@ -237,6 +241,35 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
     """
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0)
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, scale, num_kv_heads, partition_size=0):
+    """paged_attention_decode with the split-context workspace in the
+    library's fixed per-device scratch array (PKV_NOALLOC_SCRATCH_BYTES):
+    nothing is allocated, here or in the library.  Calls on one device share
+    that array, so calls that overlap on one device race.  Sizes whose
+    workspace would not fit raise PagedKVError."""
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens)
+    for t in (out, key_cache, value_cache):
+        _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, Hq, D = query.shape
+    NB, Hkv, bs, D2 = key_cache.shape
+    _need(tuple(out.shape) == (S, Hq, D), "out must match query")
+    _need(tuple(value_cache.shape) == tuple(key_cache.shape), "pools must match")
+    _need(D2 == D and Hkv == num_kv_heads, "pool shape does not match query")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables [S, W]")
+    _need(tuple(context_lens.shape) == (S,), "context_lens [S]")
+    _check(lib.paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), int(num_kv_heads), S, Hq, D, bs,
+        block_tables.shape[1], NB, int(partition_size), _dtype_code(query),
+        _stream_of(query)))
+    return out
 
 
 def paged_attention_decode_append(out, query, key_cache, value_cache, block_tables,

@@ -78,7 +78,6 @@
 #include <stdint.h>
 
 #include <mutex>
-#include <vector>
 
 #include "pkv_device.h"
 
@@ -1316,14 +1315,24 @@ __global__ __launch_bounds__(kThreads, 2) void paged_decode_merge_kernel(const D
 // ------------------------------------------------------------------ host --
 // Resident workgroups of a kernel on the current device (memoized: the
 // answer depends only on the device and the kernel's resources).
+// The memo is a fixed table (no heap allocation on any call); once full,
+// further answers are computed afresh each time.
+struct OccupancyMemo {
+  int dev;
+  const void* kernel;
+  int wgs;
+};
+constexpr int kOccupancyMemo = 512;
+
 static int resident_workgroups(const void* kernel, int waves_per_simd) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   static std::mutex mu;
-  static std::vector<std::pair<std::pair<int, const void*>, int>> memo;
+  static OccupancyMemo memo[kOccupancyMemo];
+  static int memo_n = 0;
   std::lock_guard<std::mutex> lock(mu);
-  for (auto& e : memo)
-    if (e.first.first == dev && e.first.second == kernel) return e.second;
+  for (int i = 0; i < memo_n; ++i)
+    if (memo[i].dev == dev && memo[i].kernel == kernel) return memo[i].wgs;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -1333,7 +1342,7 @@ static int resident_workgroups(const void* kernel, int waves_per_simd) {
   if (per_cu > waves_per_simd) per_cu = waves_per_simd;
   int n = cus * (per_cu > 0 ? per_cu : 1);
   n = n > kMaxWGs ? kMaxWGs : n;
-  memo.push_back({{dev, kernel}, n});
+  if (memo_n < kOccupancyMemo) memo[memo_n++] = OccupancyMemo{dev, kernel, n};
   return n;
 }
 
@@ -1417,6 +1426,35 @@ static bool partition_ok(int ps) {
   return ps == 0 || (ps >= kBlockSize && ps <= kMaxPartition && ps % kBlockSize == 0);
 }
 
+// ----------------------------------------- scratch of the allocation-free call --
+// paged_attention_decode_noalloc keeps the split-context workspace (header,
+// range descriptors, float32 partials) in this file-scope device array
+// instead of caller memory.  Every device the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address of this device's copy
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever passed to a kernel.  The decode
+// kernel writes every header field, descriptor and partial the merge kernel
+// reads, so nothing in it needs clearing between calls; two calls that
+// overlap on one device share it and race.
+constexpr size_t kScratchBytes = (size_t)PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+static void* scratch_address(int dev) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
 }  // namespace pkv
 
 extern "C" size_t paged_attention_workspace_bytes(int num_seqs, int num_heads,
@@ -1454,7 +1492,7 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
                        int block_size, int max_blocks_per_seq, int64_t num_blocks,
                        int partition_size, void* workspace, size_t workspace_bytes, int dtype,
                        int kv_dtype, void* stream, const void* new_key = nullptr,
-                       const void* new_value = nullptr) {
+                       const void* new_value = nullptr, bool static_scratch = false) {
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if ((new_key == nullptr) != (new_value == nullptr)) return PKV_ERR_INVALID_ARG;
@@ -1483,11 +1521,37 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   // flattened tile positions within one launch are 32-bit
   const int per_launch = num_seqs < kLdsSeqs ? num_seqs : kLdsSeqs;
   if ((int64_t)per_launch * max_blocks_per_seq * hgs > INT32_MAX) return PKV_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PKV_OK;
-  const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
-                                                      head_size, max_blocks_per_seq,
-                                                      block_size, partition_size);
-  if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  const int tile_cap = partition_size / kBlockSize;
+  const int64_t launch_tiles = (int64_t)per_launch * max_blocks_per_seq * hgs;
+  int64_t r;
+  if (static_scratch) {
+    // The file-scope scratch of this device stands in for the workspace,
+    // sized for the waves this device's grid can hold rather than for any
+    // device: the grid never exceeds cus x waves per SIMD workgroups.
+    if (num_seqs == 0) return PKV_OK;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return PKV_ERR_HIP;
+    const int gw = kv_dtype == PKV_FP8_E4M3 ? kWavesPerSimdFp8 : kWavesPerSimd;
+    const int64_t wgs = (int64_t)cus * gw < kMaxWGs ? (int64_t)cus * gw : kMaxWGs;
+    r = wgs * kWavesPerWG;
+    if (tile_cap > 0 && (launch_tiles + tile_cap - 1) / tile_cap > r)
+      r = (launch_tiles + tile_cap - 1) / tile_cap;
+    if (r > INT32_MAX || workspace_layout(r, gc, head_size).total > kScratchBytes)
+      return PKV_ERR_WORKSPACE;
+    workspace = scratch_address(dev);
+    if (workspace == nullptr) return PKV_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  } else {
+    if (num_seqs == 0) return PKV_OK;
+    const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                                        head_size, max_blocks_per_seq,
+                                                        block_size, partition_size);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    r = max_ranges(launch_tiles, tile_cap);
+    if (r > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  }
   if ((uintptr_t)workspace & 15u) return PKV_ERR_INVALID_ARG;
 
   DecodeParams a{};
@@ -1507,9 +1571,7 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   a.hgk = (a.group + gc - 1) / gc;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.tile_cap = partition_size / kBlockSize;
-  const int64_t r = max_ranges((int64_t)per_launch * max_blocks_per_seq * hgs, a.tile_cap);
-  if (r > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  a.tile_cap = tile_cap;
   a.r_max = (int)r;
   const WorkspaceLayout wl = workspace_layout(r, gc, head_size);
   a.header = (int*)((char*)workspace + wl.header);
@@ -1591,4 +1653,18 @@ extern "C" int paged_attention_decode_fp8(void* out, const void* query, const vo
                           k_scale, v_scale, num_kv_heads, num_seqs, num_heads, head_size,
                           block_size, max_blocks_per_seq, num_blocks, partition_size, workspace,
                           workspace_bytes, dtype, PKV_FP8_E4M3, stream);
+}
+
+extern "C" int paged_attention_decode_noalloc(void* out, const void* query,
+                                              const void* key_cache, const void* value_cache,
+                                              const int32_t* block_tables,
+                                              const int32_t* context_lens, float scale,
+                                              int num_kv_heads, int num_seqs, int num_heads,
+                                              int head_size, int block_size,
+                                              int max_blocks_per_seq, int64_t num_blocks,
+                                              int partition_size, int dtype, void* stream) {
+  return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                          1.f, 1.f, num_kv_heads, num_seqs, num_heads, head_size, block_size,
+                          max_blocks_per_seq, num_blocks, partition_size, nullptr, 0, dtype,
+                          dtype, stream, nullptr, nullptr, true);
 }

@@ -37,7 +37,7 @@ def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("paged_attention_decode", "reshape_and_cache", "copy_blocks",
               "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
-              "paged_attention_decode_append",
+              "paged_attention_decode_append", "paged_attention_decode_noalloc",
               "paged_attention_workspace_bytes", "pkv_status_string", "pkv_abi_version"):
         assert n in names
 
@@ -67,7 +67,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 5
+    assert lib.pkv_abi_version() == 6
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -148,6 +148,29 @@ def test_decode_argument_validation(lib):
     assert decode(lib, ws=FAKE, wsb=16) == WORKSPACE      # ... and must be large enough
     assert decode(lib, ws=FAKE + 8, wsb=1 << 40) == INVALID   # ... and 16-B aligned
     assert decode(lib, S=0) == OK                         # empty batch: no launch
+
+
+def test_decode_noalloc_argument_validation(lib):
+    """The allocation-free decode validates its arguments as the workspace
+    call does, before any device query (here, without a GPU, a call that
+    passes validation stops at the device query)."""
+    def na(**kw):
+        a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, hkv=4,
+                 S=2, Hq=8, D=128, bs=16, W=4, NB=64, ps=0, dtype=1, stream=0)
+        a.update(kw)
+        return lib.paged_attention_decode_noalloc(
+            a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["hkv"],
+            a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ps"], a["dtype"],
+            a["stream"])
+    assert na(out=0) == INVALID
+    assert na(cl=0) == INVALID
+    assert na(Hq=6) == INVALID
+    assert na(bs=32) == UNSUPPORTED
+    assert na(D=96) == UNSUPPORTED
+    assert na(dtype=3) == UNSUPPORTED                   # E4M3 pools: the _fp8 call
+    assert na(ps=24) == INVALID
+    assert na(query=FAKE + 8) == INVALID
+    assert na(S=0) == OK                                # empty batch: no device touched
 
 
 def test_cache_ops_argument_validation(lib):
