@@ -16,9 +16,10 @@
 //               sequence-major order, giving T tiles in total.
 //   range     = an equal share of consecutive tiles of that flattened
 //               order.  The grid holds two resident waves per SIMD and
-//               every wave takes ranges v, v + NWV, ...  so each wave
-//               streams the same number of bytes whatever the length mix
-//               (no empty or straggling workgroups).  With two waves per
+//               every wave takes an equal run of consecutive ranges (one,
+//               unless a cap on the tokens per piece makes them shorter), so
+//               each wave streams the same number of bytes whatever the
+//               length mix (no empty or straggling workgroups).  With two waves per
 //               SIMD rather than more, the hardware's preference for the
 //               oldest wave leaves less of a spread in finishing times.
 //   piece     = the part of one segment inside one range.  A wave keeps an
@@ -92,6 +93,7 @@ constexpr int kWavesPerSimdFp8 = 3;             // ... with E4M3 pools
 constexpr int kMinTilesPerRange = 4;
 constexpr int kMaxPartition = 4096;             // tokens per piece, when capped
 constexpr int kSoloPieces = 8;                  // merged by one wave up to this many
+constexpr int kMergeRounds = 8;                 // merge grid: at most this x the decode grid
 // 16-bit queries with at least this many heads per group compute both
 // products on the matrix cores: the value product in the float32 VALU
 // costs 16 x D FMAs per head and tile, and from four heads up that work,
@@ -107,6 +109,10 @@ constexpr float kPvSlack = 8.f;
 // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitAllLoads = 0x0F70;
+
+// Sequences one launch covers: their segment table lives in LDS.  The
+// host splits larger batches into consecutive launches.
+constexpr int kLdsSeqs = 2048;
 
 // DT: query / output element; KT: pool element (DT itself, or E4M3 codes
 // with 16-bit queries).
@@ -158,6 +164,25 @@ struct DecodeCfg {
   // 15% faster on the 32K-token grouped workload with E4M3 pools, 3.7%
   // slower with bfloat16 pools).
   static constexpr bool kOverlapNext = kFp8;
+  // Float32 partials of split pieces are staged in the wave's LDS and
+  // written to the workspace when the wave ends (or when its stage is
+  // full).  A store counts against the same wait counter as the tile
+  // loads, so a partial stored in the middle of a wave's stream holds up
+  // its next tile until the store is acknowledged: measured on one MI355X,
+  // 16 x 32K bf16 tokens at 512-token partitions (four pieces per wave,
+  // every wave at a piece end at the same time), the decode kernel takes
+  // 373 us storing them as it goes against 336 us not storing them.  A
+  // staged record holds acc [GC][D] then (max, sum) per head, padded to
+  // 16 bytes; the stage gets what the workgroup's LDS share leaves (the
+  // resident workgroups of a CU split its 160 KiB), at most 8 records.
+  static constexpr int kPartFloats = GC * D + 2 * GC;
+  static constexpr int kPartStride = (kPartFloats + 3) / 4 * 4;
+  static constexpr int kLdsFixed =
+      kLdsSeqs * 8 + kWavesPerWG * (kPvMfma ? kBlockSize * kVS + 4 : kBlockSize * GC * 4 + 16) +
+      64;
+  static constexpr int kLdsPerWg = 160 * 1024 / kGridWaves - 1024;
+  static constexpr int kStageFit = (kLdsPerWg - kLdsFixed) / kWavesPerWG / (kPartStride * 4);
+  static constexpr int kStageRecs = kStageFit < 1 ? 0 : (kStageFit > 8 ? 8 : kStageFit);
 };
 
 struct DecodeParams {
@@ -234,9 +259,6 @@ __device__ __forceinline__ int clamp_len(int L, int max_tokens) {
 
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlockSize - 1) / kBlockSize; }
 
-// Sequences one launch covers: their segment table lives in LDS.  The
-// host splits larger batches into consecutive launches.
-constexpr int kLdsSeqs = 2048;
 
 // Segment table of this launch's sequences, built in LDS by every thread of
 // the workgroup: len[s] = clamped context length, incl[s] = tiles of
@@ -292,7 +314,8 @@ __device__ __forceinline__ int seq_of(const int* incl, int S, int x) {
 
 // How the T flattened tiles are cut into ranges: R ranges of q tiles (the
 // last one shorter), range r covering tiles [r q, min((r + 1) q, T)).  Wave
-// v takes ranges v, v + NWV, ...  Both kernels derive the same map.
+// v of NWV takes ranges [v R / NWV, (v + 1) R / NWV).  Both kernels derive
+// the same map.
 struct RangeMap {
   int q, R, T;
   __device__ __forceinline__ int start(int r) const { return r * q; }
@@ -689,12 +712,17 @@ __device__ void merge_slice(const DecodeParams& p, const Split& sp, int r, int l
         ll[u] = p.part_ml[(sl * GC + g) * 2 + 1];
         aa[u] = load16(p.part_acc + sl * GC * D + c * 4);
       }
+      // keep the batch's loads ahead of the folding, and fold without
+      // branches (a lane past the last piece folds with weight 0): a branch
+      // per piece lets the compiler sink each load into its branch, one
+      // round trip per piece
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kSliceUnroll; ++u) {
-        if (i0 + pl + u * kSlicePieceLanes >= sp.np) break;
-        const float Mn = fmaxf(M, mm[u]);  // every piece's max is finite
-        const float a = __builtin_amdgcn_exp2f(M - Mn);
-        const float b = __builtin_amdgcn_exp2f(mm[u] - Mn);
+        const bool ok = i0 + pl + u * kSlicePieceLanes < sp.np;
+        const float Mn = ok ? fmaxf(M, mm[u]) : M;  // every piece's max is finite
+        const float a = ok ? __builtin_amdgcn_exp2f(M - Mn) : 1.f;
+        const float b = ok ? __builtin_amdgcn_exp2f(mm[u] - Mn) : 0.f;
         S = S * a + ll[u] * b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) O[e] = fmaf(O[e], a, b * float_of(aa[u][e]));
@@ -806,6 +834,8 @@ paged_decode_kernel(const DecodeParams p) {
   __shared__ float sm_p[kWavesPerWG][C::kPvMfma ? 1 : kBlockSize * GC];
   // matrix-core path: each wave's value tile as rows, read back transposed
   __shared__ __attribute__((aligned(16))) char sm_v[kWavesPerWG][C::kPvMfma ? kBlockSize * C::kVS : 16];
+  __shared__ __attribute__((aligned(16)))
+  float sm_stage[kWavesPerWG][C::kStageRecs > 0 ? C::kStageRecs * C::kPartStride : 4];
   __shared__ int sm_incl[kLdsSeqs];
   __shared__ int sm_len[kLdsSeqs];
   __shared__ int sm_wsum[kWavesPerWG];
@@ -843,8 +873,13 @@ paged_decode_kernel(const DecodeParams p) {
     p.header[0] = map.R;
     p.header[1] = map.q;
   }
-  const int r0 = v;
-  if (r0 >= map.R) return;
+  // Wave v takes the consecutive ranges [r_first, r_end), an equal share
+  // (within one) of them: its tiles are one contiguous run of the flattened
+  // order, and when there are fewer ranges than waves the busy waves are
+  // spread evenly over the wave numbering (so over XCDs and CUs).
+  const int r_first = (int)((int64_t)v * map.R / nwaves);
+  const int r_end = (int)((int64_t)(v + 1) * map.R / nwaves);
+  if (r_first >= r_end) return;
 
   float* pw = sm_p[w];
   const int row = lane & 15;
@@ -937,7 +972,8 @@ paged_decode_kernel(const DecodeParams p) {
   };
 
   // the wave's stream of tiles: windows cw (being computed) and nw (next)
-  Window cw = prepare_window(p, map, sm_incl, sm_len, head_groups, r0, map.start(r0), lane);
+  Window cw =
+      prepare_window(p, map, sm_incl, sm_len, head_groups, r_first, map.start(r_first), lane);
   Window nw = cw;
   bool have_nw = false;
   bool no_more = false;  // no range after the current one
@@ -968,19 +1004,52 @@ paged_decode_kernel(const DecodeParams p) {
   int pc_slot = 0;
 
   bool done = false;  // the wave's last tile is computed
+
+  // Staged partials: record k of the wave's stage belongs to workspace slot
+  // stage_slot of lane k; n_staged records are waiting.
+  float* const stage = sm_stage[w];
+  int n_staged = 0;
+  int stage_slot = 0;
+  auto flush_stage = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_wave_barrier();
+    for (int k = 0; k < n_staged; ++k) {
+      const int64_t slot = __builtin_amdgcn_readlane(stage_slot, k);
+      const float* src = stage + k * C::kPartStride;
+      for (int c = lane; c < GC * D / 4; c += kWave)
+        store16(p.part_acc + slot * GC * D + c * 4, *reinterpret_cast<const u32x4*>(src + c * 4));
+      if (lane < 2 * GC) p.part_ml[slot * GC * 2 + lane] = src[GC * D + lane];
+    }
+    __builtin_amdgcn_wave_barrier();
+    n_staged = 0;
+  };
+  // The record a piece's partials go into: the next free one of the stage
+  // (a full stage leaves the piece to store its partials at once).
+  auto stage_record = [&](int slot) __attribute__((always_inline)) -> float* {
+    if (lane == n_staged) stage_slot = slot;
+    return stage + (n_staged++) * C::kPartStride;
+  };
+  // the next window: of this range, or the wave's next range
+  auto prepare_next = [&]() __attribute__((always_inline)) {
+    const int r2 = cw.ends_range ? cw.r + 1 : cw.r;
+    // both flags set on both paths: a store through a selected address
+    // would keep them in memory
+    have_nw = r2 < r_end;
+    no_more = r2 >= r_end;
+    if (r2 < r_end)
+      nw = prepare_window(p, map, sm_incl, sm_len, head_groups, r2,
+                          cw.ends_range ? map.start(r2) : cw.x + cw.cnt, lane);
+  };
   auto step = [&](const Tile& tc, Tile& tn) __attribute__((always_inline)) {
     if (done) return;
-    // 1. look ahead: prepare the next window (of this range or the next)
-    if (!have_nw && !no_more && cw.cnt - ci <= kPrepAhead) {
-      const int r2 = cw.ends_range ? cw.r + nwaves : cw.r;
-      // both flags set on both paths: a store through a selected address
-      // would keep them in memory
-      have_nw = r2 < map.R;
-      no_more = r2 >= map.R;
-      if (r2 < map.R)
-        nw = prepare_window(p, map, sm_incl, sm_len, head_groups, r2,
-                            cw.ends_range ? map.start(r2) : cw.x + cw.cnt, lane);
-    }
+    // 1. look ahead: the next window is prepared a few tiles before this one
+    // runs out.  Its block-table gather is waited for at once (its flags
+    // need the ids), so with 16-bit pools, which wait for the next tile
+    // before computing anyway, it is prepared after that tile's loads are
+    // issued and the two round trips overlap -- unless the next tile is
+    // already the next window's first.
+    const bool prep = !have_nw && !no_more && cw.cnt - ci <= kPrepAhead;
+    const bool prep_first = prep && (C::kOverlapNext || ci + 1 >= cw.cnt);
+    if (prep_first) prepare_next();
 
     // 2. issue the loads of the next tile
     const int info = __builtin_amdgcn_readlane(cw.info, ci);
@@ -1001,6 +1070,7 @@ paged_decode_kernel(const DecodeParams p) {
     const int id_c = __builtin_amdgcn_readlane(cw.id, ci);
     load_tile(tn, more ? id_n : id_c, more ? (info_n & 0xffff) : hg, more ? s_n : s,
               more ? info_n : info);
+    if (prep && !prep_first) prepare_next();
     if constexpr (!C::kOverlapNext) __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
 
     // 3. compute the current tile
@@ -1141,6 +1211,17 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
           for (int b = 0; b < C::kNdb; ++b) store4<DT>(dst + 16 * b * C::kEszQ, oacc[b] * inv);
         }
+      } else if (C::kStageRecs > 0 && n_staged < C::kStageRecs) {  // split piece: staged
+        float* rec = stage_record(pc_slot);
+        if (row < GC) {
+#pragma unroll
+          for (int b = 0; b < C::kNdb; ++b)
+            *reinterpret_cast<floatx4*>(rec + row * D + 4 * jg + 16 * b) = oacc[b] * vs;
+          if (jg == 0) {
+            rec[GC * D + 2 * row] = om_run;
+            rec[GC * D + 2 * row + 1] = l_tot;
+          }
+        }
       } else if (row < GC) {  // a piece of a split segment: float32 partials
         const int64_t slot = pc_slot;
         float* dst = p.part_acc + (slot * GC + row) * D + 4 * jg;
@@ -1179,6 +1260,26 @@ paged_decode_kernel(const DecodeParams p) {
             for (int e = 0; e < EPC; e += C::kEpcQ) store_chunk<DT>(dst + e * C::kEszQ, o + e);
           }
         }
+      } else if (C::kStageRecs > 0 && n_staged < C::kStageRecs) {  // split piece: staged
+        const float vs = C::kFp8 ? p.v_scale : 1.f;  // partials hold the values' scale
+        float* rec = stage_record(pc_slot);
+        if (lane < C::kNch) {
+#pragma unroll
+          for (int g = 0; g < GC; ++g) {
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4)
+              *reinterpret_cast<floatx4*>(rec + g * D + lane * EPC + e) =
+                  floatx4{acc[g][e] * vs, acc[g][e + 1] * vs, acc[g][e + 2] * vs,
+                          acc[g][e + 3] * vs};
+          }
+        }
+        if (lane == 0) {
+#pragma unroll
+          for (int g = 0; g < GC; ++g) {
+            rec[GC * D + 2 * g] = m_run[g];
+            rec[GC * D + 2 * g + 1] = l_run[g];
+          }
+        }
       } else {  // a piece of a split segment: float32 partials
         const int64_t slot = pc_slot;
         const float vs = C::kFp8 ? p.v_scale : 1.f;  // partials hold the values' scale
@@ -1202,9 +1303,11 @@ paged_decode_kernel(const DecodeParams p) {
       }
     }
 
-    // 4. the next tile opens a piece: its q goes into the registers this
-    // tile has finished with, and arrives with that tile's own data
-    if (more && (info_n & kPieceFirst)) load_q(qa, s_n, info_n & 0xffff);
+    // 4. the next tile opens a new segment: its q goes into the registers
+    // this tile has finished with, and arrives with that tile's own data (a
+    // wave's tiles are one contiguous run, so a piece that does not start
+    // its segment continues the previous piece's and keeps its q)
+    if (more && (info_n & kSegStart)) load_q(qa, s_n, info_n & 0xffff);
 
     // 5. advance
     if (++ci == cw.cnt) {
@@ -1233,6 +1336,7 @@ paged_decode_kernel(const DecodeParams p) {
     step(tb, ta);
     if (done) break;
   }
+  if constexpr (C::kStageRecs > 0) flush_stage();
 }
 
 // ----------------------------------------------------------- merge kernel --
@@ -1352,10 +1456,22 @@ static hipError_t launch_decode(DecodeParams a, hipStream_t st) {
   const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC>);
   const int nwg = resident_workgroups(k, DecodeCfg<DT, KT, D, GC>::kGridWaves);
   if (nwg <= 0) return hipErrorInvalidDevice;
+  // The merge kernel takes a range per wave per round.  Without a cap there
+  // are at most as many ranges as decode waves; with one, up to tiles / cap:
+  // enough workgroups for one round (at most kMergeRounds times the decode
+  // grid), so merges in slices of many-piece segments all run at once.
+  int64_t ranges = (int64_t)nwg * kWavesPerWG;
+  if (a.tile_cap > 0) {
+    const int64_t tiles = (int64_t)a.num_seqs * a.max_blocks * a.num_kv_heads * a.hgk;
+    const int64_t rc = (tiles + a.tile_cap - 1) / a.tile_cap;
+    ranges = rc > ranges ? rc : ranges;
+  }
+  int64_t mwg = (ranges + kWavesPerWG - 1) / kWavesPerWG;
+  mwg = mwg < (int64_t)nwg * kMergeRounds ? mwg : (int64_t)nwg * kMergeRounds;
   hipLaunchKernelGGL((paged_decode_kernel<DT, KT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
                      a);
-  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
-                     a);
+  hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3((unsigned)mwg),
+                     dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
