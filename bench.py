@@ -23,9 +23,10 @@ key/value bytes the attention must read (sum of context lengths x 2 x
 kv_heads x head_size x element bytes) divided by the step time.
 `roofline` covers the dominant kernel call, paged_attention_decode (or its
 appending variant), timed with events on the launch stream: over the timed
-region itself when a step is that call alone, else from a second pass of
-the same steps with events around each call; `cpu_baseline` times the float64 CPU
-oracle on a bounded sample of the same batch (single thread);
+region itself when a step is that call alone, else over a timed region of
+the call alone repeated on the step's final pools; `cpu_baseline` times the float64 CPU
+oracle on a bounded sample of the same batch (one thread, then one process
+per core of the host share, at most 16);
 `translation` times the same decode call on the same batch laid out with
 every sequence's blocks physically consecutive (identity block tables) and
 in a virtually contiguous pool (HIP virtual-memory ranges backed on
@@ -34,8 +35,8 @@ chunk's reshape_and_cache, then paged_attention_prefill) on its own
 workloads, in TFLOP/s of causal attention against the MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b]
-                    [--also long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,long_gqa_fp8,
-                            gqa8_long,gqa16_long]
+                    [--also long_gqa_p512,long_gqa,llama13b_conv,sampling_cow,beam,
+                            opt13b_fp8,long_gqa_fp8,gqa8_long,gqa16_long]
                     [--no-cpu-baseline]
                     [--no-translation]
 """
@@ -67,8 +68,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--also",
-                    default="long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,long_gqa_fp8,"
-                            "gqa8_long,gqa16_long")
+                    default="long_gqa_p512,long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,"
+                            "long_gqa_fp8,gqa8_long,gqa16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill_chunk,prefill_gqa",
                     help="prefill workloads to time ('' for none)")
@@ -114,6 +115,18 @@ def copy_calibration(mib, steps):
 def kv_bytes(w, lens):
     return (int(np.asarray(lens, np.int64).sum()) * 2 * w.num_kv_heads * w.head_size
             * w.kv_elem_bytes)
+
+
+def kv_unique_bytes(w, tables, lens):
+    """K/V bytes of the distinct cached tokens: a physical block that several
+    sequences map (a prompt shared by samples or beams) counts once, with
+    the most tokens any of them uses in it."""
+    used = {}
+    for s, L in enumerate(np.asarray(lens, np.int64)):
+        for n in range(-(-int(L) // 16)):
+            b = int(tables[s, n])
+            used[b] = max(used.get(b, 0), min(16, int(L) - 16 * n))
+    return sum(used.values()) * 2 * w.num_kv_heads * w.head_size * w.kv_elem_bytes
 
 
 def decode_algorithmic_bytes(w, lens):
@@ -213,7 +226,9 @@ class Step:
         """Times `steps` steps between two events and two synchronizations
         (nothing else recorded in between: an event per call would add a
         few microseconds to every step), then the same steps again with an
-        event pair around each call, for the call's own duration."""
+        event pair around each call, for the call's own duration, and, when
+        a step is more than the call, `steps` calls of the call alone
+        between two events (its average duration without per-call events)."""
         torch = self.torch
         for _ in range(warmup):
             self.updates()
@@ -240,6 +255,20 @@ class Step:
             ev[i][1].record()
         torch.cuda.synchronize()
         dec = np.asarray([a.elapsed_time(c) for a, c in ev])
+        self.call_only_ms = None
+        if not self.only_the_call():
+            # the state after the updates: repeating the call alone recomputes
+            # the same outputs from the same pools
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            self.decode()
+            torch.cuda.synchronize()
+            c0.record()
+            for _ in range(steps):
+                self.decode()
+            c1.record()
+            torch.cuda.synchronize()
+            self.call_only_ms = c0.elapsed_time(c1) / steps
         return step_ms, dec, wall
 
 
@@ -286,19 +315,23 @@ class PrefillStep:
 
     run = Step.run
 
+    def only_the_call(self):
+        return False
+
 
 def measure_prefill(w, seed, steps, warmup):
     st = PrefillStep(w, seed)
     step_ms, call_ms, wall = st.run(steps, warmup)
     fl = prefill_flops(w, st.b)
-    call_avg = float(call_ms.mean())
+    call_avg = st.call_only_ms  # the prefill call alone, between two events
     qsl = st.b["query_start_loc"]
     return {
         "workload": w.key, "seed": seed, "seqs": w.num_seqs, "heads": w.num_heads,
         "kv_heads": w.num_kv_heads, "head_size": w.head_size, "dtype": w.dtype,
         "new_tokens": int(qsl[-1]), "context_tokens": int(st.b["context_lens"].sum()),
         "flops_per_step": fl, "ms_per_step": step_ms,
-        "prefill_call_ms_avg": call_avg, "prefill_call_ms_min": float(call_ms.min()),
+        "prefill_call_ms_avg": call_avg, "prefill_call_ms_events_avg": float(call_ms.mean()),
+        "prefill_call_ms_min": float(call_ms.min()),
         "step_TFLOPs": fl / (step_ms * 1e-3) / 1e12,
         "prefill_TFLOPs": fl / (call_avg * 1e-3) / 1e12,
         "new_tokens_per_s": int(qsl[-1]) / (step_ms * 1e-3),
@@ -317,8 +350,8 @@ def measure(w, seed, steps, warmup, ps, fuse=True):
     if st.fused:  # the call also writes each sequence's new key and value rows
         algo += 2 * w.num_seqs * w.num_kv_heads * w.head_size * w.kv_elem_bytes
     # the call's average duration: over the timed region itself when a step
-    # is nothing but the call, else from the pass with events around each call
-    dec_avg = step_ms if st.only_the_call() else float(dec_ms.mean())
+    # is nothing but the call, else from a timed region of the call alone
+    dec_avg = step_ms if st.only_the_call() else st.call_only_ms
     r = {
         "workload": w.key, "seed": seed, "seqs": w.num_seqs,
         "heads": w.num_heads, "kv_heads": w.num_kv_heads, "head_size": w.head_size,
@@ -331,7 +364,8 @@ def measure(w, seed, steps, warmup, ps, fuse=True):
         "decode_tokens_per_s": w.num_seqs / (step_ms * 1e-3),
         "decode_call_ms_avg": dec_avg,
         "decode_call_timing": ("timed region (a step is the call alone)" if st.only_the_call()
-                               else "events around each call, second pass"),
+                               else "timed region of the call alone, repeated on the "
+                                    "step's final pools"),
         "decode_call_ms_events_avg": float(dec_ms.mean()),
         "decode_call_ms_min": float(dec_ms.min()), "decode_call_ms_max": float(dec_ms.max()),
         "decode_algorithmic_bytes": algo,
@@ -340,6 +374,12 @@ def measure(w, seed, steps, warmup, ps, fuse=True):
     }
     r["pct_of_hbm_peak"] = 100.0 * r["kv_GBps"] / HBM_PEAK_GBPS
     r["decode_pct_of_hbm_peak"] = 100.0 * r["decode_GBps"] / HBM_PEAK_GBPS
+    uniq = kv_unique_bytes(w, st.b["block_tables"], st.lens)
+    if uniq != kvb:  # blocks shared between sequences: logical and unique bytes
+        r["kv_unique_bytes_per_step"] = uniq
+        r["kv_shared_fraction"] = 1.0 - uniq / kvb
+        r["kv_unique_GBps"] = uniq / (step_ms * 1e-3) / 1e9
+        r["decode_unique_GBps"] = (algo - kvb + uniq) / (dec_avg * 1e-3) / 1e9
     return r, st
 
 
@@ -470,17 +510,52 @@ def traffic_for_current_kernel(workload):
     return entry.get("hbm_bytes_per_call")
 
 
-def cpu_baseline(st, budget_s):
-    """The float64 oracle, single thread, on the first sequences of the batch."""
-    from threadpoolctl import threadpool_limits
+def _oracle_pass(q, kc, vc, tables, lens, w_args, seqs, budget_s):
+    """The float64 oracle over `seqs` of the sample, one at a time and round
+    and round, until `budget_s` seconds are spent: (decodes, tokens, s)."""
     import oracle
+    scale, hkv, dtype, fp8 = w_args
+    done, tokens, t_used = 0, 0, 0.0
+    t0 = time.perf_counter()
+    while t_used < budget_s and seqs:
+        for s in seqs:
+            oracle.decode_attention(q, kc, vc, tables, lens, scale, hkv, dtype, seqs=[s], **fp8)
+            done += 1
+            tokens += int(lens[s])
+            t_used = time.perf_counter() - t0
+            if t_used >= budget_s:
+                break
+    return done, tokens, t_used
+
+
+def _oracle_worker(job):
+    """One process of the all-cores leg: the sample memory-mapped from the
+    files the parent wrote, sequences i, i + n, ... of it, one thread."""
+    from threadpoolctl import threadpool_limits
+    folder, i, n, w_args, budget_s = job
+    a = {k: np.load(os.path.join(folder, k + ".npy"), mmap_mode="r")
+         for k in ("q", "kc", "vc", "tables", "lens")}
+    seqs = list(range(i, len(a["lens"]), n))
+    with threadpool_limits(limits=1):
+        return _oracle_pass(a["q"], a["kc"], a["vc"], a["tables"], np.asarray(a["lens"]),
+                            w_args, seqs, budget_s)
+
+
+def cpu_baseline(st, budget_s):
+    """The float64 oracle on the host, on the first sequences of the batch:
+    one thread, then one process per core of this process's CPU share (at
+    most 16, the host share of one GPU), each on its own sequences."""
+    import multiprocessing
+    import shutil
+    import tempfile
+    from threadpoolctl import threadpool_limits
     from paged_kv_cache_311_amd import workloads as wl
     w, b = st.w, st.b
     bt, lens = b["block_tables"], b["context_lens"]
     n_max = min(w.num_seqs, 64)
     ids = sorted({int(x) for s in range(n_max) for x in bt[s, :-(-int(lens[s]) // 16)]})
     remap = {x: i for i, x in enumerate(ids)}
-    idx = st.torch.tensor(ids, dtype=st.torch.int64, device="cuda:0")
+    idx = st.torch.tensor(ids, dtype=st.torch.int64, device=b["key_cache"].device)
     kc = wl.to_host(b["key_cache"].index_select(0, idx))
     vc = wl.to_host(b["value_cache"].index_select(0, idx))
     tables = np.full_like(bt[:n_max], -1)
@@ -488,27 +563,46 @@ def cpu_baseline(st, budget_s):
         n = -(-int(lens[s]) // 16)
         tables[s, :n] = [remap[int(x)] for x in bt[s, :n]]
     q = wl.to_host(b["query"])[:n_max]
+    sample_lens = np.asarray(lens[:n_max])
     fp8 = (dict(kv_dtype="e4m3", k_scale=w.k_scale, v_scale=w.v_scale) if w.fp8 else {})
-    done, tokens, t_used = 0, 0, 0.0
+    w_args = (w.scale, w.num_kv_heads, w.dtype, fp8)
+    per_token = 2 * w.num_kv_heads * w.head_size * w.kv_elem_bytes
+
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while t_used < budget_s:       # whole passes over the sample until the budget
-            for s in range(n_max):
-                oracle.decode_attention(q, kc, vc, tables, lens[:n_max], w.scale,
-                                        w.num_kv_heads, w.dtype, seqs=[s], **fp8)
-                done += 1
-                tokens += int(lens[s])
-                t_used = time.perf_counter() - t0
-                if t_used >= budget_s:
-                    break
-    kvb = tokens * 2 * w.num_kv_heads * w.head_size * w.kv_elem_bytes
+        done1, tok1, t1 = _oracle_pass(q, kc, vc, tables, sample_lens, w_args,
+                                       list(range(n_max)), budget_s)
+    single = {"value": tok1 * per_token / t1 / 1e9, "unit": "GB/s", "cores": 1,
+              "decode_tokens_per_s": done1 / t1, "seconds": t1,
+              "sample": f"{done1} sequence-decodes ({tok1} KV tokens) in {t1:.1f} s"}
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    folder = tempfile.mkdtemp(prefix="pkv_oracle_", dir=shm)
+    try:
+        for k, v in (("q", q), ("kc", kc), ("vc", vc), ("tables", tables),
+                     ("lens", sample_lens)):
+            np.save(os.path.join(folder, k + ".npy"), v)
+        del kc, vc
+        jobs = [(folder, i, cores, w_args, budget_s) for i in range(cores)]
+        # fresh interpreters (this process has initialised the GPU)
+        with multiprocessing.get_context("spawn").Pool(cores) as pool:
+            res = pool.map(_oracle_worker, jobs)
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    rate = sum(tok * per_token / t for _, tok, t in res if t > 0)
+    decodes = sum(d / t for d, _, t in res if t > 0)
+    done_all = sum(d for d, _, _ in res)
+    tok_all = sum(tok for _, tok, _ in res)
     return {
-        "value": kvb / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"float64 numpy oracle, one thread, the first {n_max} of {w.num_seqs} "
-                   f"sequences of the {w.key} batch, {done} sequence-decodes "
-                   f"({tokens} KV tokens) in {t_used:.1f} s"),
-        "seconds": t_used, "decode_tokens_per_s": done / t_used,
-        "cpu_model": _cpu_model(),
+        "value": rate / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": (f"float64 numpy oracle, {cores} processes of one thread each over the "
+                   f"first {n_max} of {w.num_seqs} sequences of the {w.key} batch (process i "
+                   f"takes sequences i, i + {cores}, ...): {done_all} sequence-decodes "
+                   f"({tok_all} KV tokens) in about {budget_s:.0f} s each; rate = sum of the "
+                   f"processes' rates"),
+        "decode_tokens_per_s": decodes, "seconds": max(t for _, _, t in res),
+        "single_thread": single, "cpu_model": _cpu_model(),
+        "cpus_visible": len(os.sched_getaffinity(0)),
     }
 
 

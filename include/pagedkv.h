@@ -97,9 +97,9 @@ const char* pkv_build_id(void);
  * kv head g = h / (num_heads / num_kv_heads):
  *     out[s][h] = sum_t softmax_t(scale * q[s][h] . k_t) v_t,  t = 0..L-1,
  * where k_t, v_t are token t's key and value in kv head g, read from the
- * pools through block_tables[s] ([VAS] eq. (1); the kernel "follows the
- * block table while reading keys and values", [IV] "Architecture, step by
- * step", step 3).  L counts every cached token, including the one written
+ * pools through block_tables[s] ([VAS] eq. (1); keys and values are
+ * read through the sequence's table, [IV] "Architecture, step by step",
+ * step 3).  L counts every cached token, including the one written
  * this step.  L = 0 gives out[s][h] = 0.  Slots at or past L and blocks
  * past ceil(L/16) are never used, whatever they hold (NaN included).
  *

@@ -5,12 +5,12 @@ TEST INFRASTRUCTURE: see the package docstring.
 What is computed.  During decoding every sequence keeps the key and value
 vector of each token it has seen, per layer and per attention head
 ([TEQ] "Why the KV cache is an allocator problem").  The cache of a
-sequence is split into fixed-size blocks of 16 tokens; a per-sequence
-block table maps logical block numbers to physical blocks that may sit
-anywhere in a shared pool ([TEQ] "The OS already solved this in the
-1960s"; [IV] "Architecture, step by step", steps 1-3; [AITJ] "How logical
-blocks, physical blocks and the block table work").  The attention
-kernel follows the block table while reading keys and values ([IV] step
+sequence is cut into 16-token blocks; each sequence keeps a table whose
+n-th entry names the pool block that holds its n-th run of 16 tokens, and
+those blocks may lie anywhere in one shared pool ([TEQ] "The OS already
+solved this in the 1960s"; [IV] "Architecture, step by step", steps 1-3;
+[AITJ] "How logical blocks, physical blocks and the block table work").
+Attention reads each token's key and value through that table ([IV] step
 3).  Paging changes only where the bytes live, not the arithmetic
 ([AITJ] "What PagedAttention actually solves"), so the result is exactly
 textbook scaled dot-product attention [VAS eq. 1] of the single new query

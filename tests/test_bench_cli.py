@@ -58,3 +58,35 @@ def test_child_command_line(monkeypatch):
         assert cmd[cmd.index(flag) + 1] == val
     assert "--no-fuse" in cmd and "--no-translation" in cmd
     assert "--no-cpu-baseline" not in cmd
+
+
+def test_cpu_baseline_legs_on_the_host():
+    """The CPU baseline's two legs (one thread; one process per core of the
+    host share) run the oracle on a sample of a batch built on the CPU."""
+    import dataclasses
+    import types
+    import torch
+    import bench
+    from paged_kv_cache_311_amd import workloads as wl
+    w = dataclasses.replace(wl.WORKLOADS["opt13b"], num_seqs=6, num_heads=4, num_kv_heads=4,
+                            lengths=("uniform", 1, 200), max_len=200)
+    b = wl.make_batch(w, 5, "cpu")
+    st = types.SimpleNamespace(w=w, b=b, torch=torch)
+    r = bench.cpu_baseline(st, 0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= 16 and r["cores"] == min(len(os.sched_getaffinity(0)), 16)
+    assert r["single_thread"]["cores"] == 1 and r["single_thread"]["value"] > 0
+
+
+def test_unique_bytes_count_shared_blocks_once():
+    import dataclasses
+    import numpy as np
+    import bench
+    from paged_kv_cache_311_amd import workloads as wl
+    w = dataclasses.replace(wl.WORKLOADS["opt13b"], num_kv_heads=2, head_size=64)
+    per_token = 2 * 2 * 64 * 2
+    # two sequences share block 7 (full); each has a private last block
+    tables = np.array([[7, 3, -1], [7, 5, 9]], np.int32)
+    lens = np.array([20, 40])
+    assert bench.kv_unique_bytes(w, tables, lens) == (16 + 4 + 16 + 8) * per_token
+    assert bench.kv_bytes(w, lens) == 60 * per_token

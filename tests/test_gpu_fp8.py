@@ -1,8 +1,11 @@
 """Parity of the E4M3 pool path with the CPU oracle on an MI355X (marked gpu).
 
-Pools hold OCP E4M3 codes with one float32 scale per pool ("PagedAttention
-KV cache memory management" [AITJ], "Operational trade-offs and limits":
-an eight-bit cache halves the bytes each token holds).  reshape_and_cache_fp8
+Pools hold OCP E4M3 codes with one float32 scale per pool.  The pages set
+KV-cache quantization (cached values in a lower-precision representation)
+beside paging as the remedy for too many bytes per token ("PagedAttention
+KV cache memory management" [AITJ], "PagedAttention vs KV-cache
+quantization vs prefix caching") and name no format; the 8-bit E4M3 format
+is this project's choice, half the bytes of a 16-bit pool.  reshape_and_cache_fp8
 and copy_blocks on such pools are compared bit for bit with the oracle;
 paged_attention_decode_fp8 within the tolerances of the other parity tests
 (5e-3 for float16/bfloat16 queries, plus half an output ulp for bfloat16),
