@@ -36,7 +36,8 @@ workloads, in TFLOP/s of causal attention against the MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b]
                     [--also long_gqa_p512,long_gqa,llama13b_conv,sampling_cow,beam,
-                            opt13b_fp8,long_gqa_fp8,gqa8_long,gqa16_long]
+                            sampling_cow_shuffled,beam_shuffled,opt13b_fp8,long_gqa_fp8,
+                            gqa8_long,gqa16_long]
                     [--no-cpu-baseline]
                     [--no-translation]
 """
@@ -68,8 +69,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--also",
-                    default="long_gqa_p512,long_gqa,llama13b_conv,sampling_cow,beam,opt13b_fp8,"
-                            "long_gqa_fp8,gqa8_long,gqa16_long")
+                    default="long_gqa_p512,long_gqa,llama13b_conv,sampling_cow,beam,"
+                            "sampling_cow_shuffled,beam_shuffled,opt13b_fp8,long_gqa_fp8,"
+                            "gqa8_long,gqa16_long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill_chunk,prefill_gqa",
                     help="prefill workloads to time ('' for none)")
@@ -173,6 +175,10 @@ class Step:
             self.key = torch.randn(shape, generator=g, device=dev).to(b["query"].dtype)
             self.value = torch.randn(shape, generator=g, device=dev).to(b["query"].dtype)
         self.slots = torch.from_numpy(np.asarray(slots, np.int64)).to(dev)
+        # the runtime's reference counts above one, as the decode call's
+        # cache-policy flags (workloads whose sequences share blocks)
+        self.flags = (torch.from_numpy(b["block_shared"]).to(dev)
+                      if "block_shared" in b else None)
         pairs = b.get("cow_pairs")
         self.pairs = (torch.from_numpy(pairs).to(dev)
                       if pairs is not None and len(pairs) else None)
@@ -196,17 +202,18 @@ class Step:
             self.pkv.reshape_and_cache(self.key, self.value, self.slots, b["key_cache"],
                                        b["value_cache"])
 
-    def decode_into(self, out, kc, vc, bt):
+    def decode_into(self, out, kc, vc, bt, flags=None):
         b, w = self.b, self.w
         if w.fp8:
             self.pkv.paged_attention_decode_fp8(out, b["query"], kc, vc, bt, self.cl,
                                                 float(w.scale), w.k_scale, w.v_scale,
                                                 w.num_kv_heads, partition_size=self.ps,
-                                                workspace=self.ws)
+                                                workspace=self.ws, block_shared=flags)
         else:
             self.pkv.paged_attention_decode(out, b["query"], kc, vc, bt, self.cl,
                                             float(w.scale), w.num_kv_heads,
-                                            partition_size=self.ps, workspace=self.ws)
+                                            partition_size=self.ps, workspace=self.ws,
+                                            block_shared=flags)
 
     def decode(self):
         b, w = self.b, self.w
@@ -214,9 +221,9 @@ class Step:
             self.pkv.paged_attention_decode_append(
                 self.out, b["query"], b["key_cache"], b["value_cache"], self.bt, self.cl,
                 self.key, self.value, float(w.scale), w.num_kv_heads, partition_size=self.ps,
-                workspace=self.ws)
+                workspace=self.ws, block_shared=self.flags)
         else:
-            self.decode_into(self.out, b["key_cache"], b["value_cache"], self.bt)
+            self.decode_into(self.out, b["key_cache"], b["value_cache"], self.bt, self.flags)
 
     def only_the_call(self):
         """True when a step issues nothing but the decode call."""

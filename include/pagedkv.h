@@ -80,7 +80,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 6 */
+int pkv_abi_version(void);  /* 7 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -126,6 +126,24 @@ const char* pkv_build_id(void);
  *                 aligned; caller-owned, contents need no initialization.
  *                 Calls that use one workspace must not overlap (one
  *                 stream, or ordered).
+ *   block_shared  optional (NULL allowed): uint8 [num_blocks], device
+ *                 memory, nonzero for a block that more than one sequence
+ *                 of the batch maps -- the runtime's reference count above
+ *                 one ([TEQ] "Paging's second gift: copy-on-write").  It
+ *                 only chooses how tiles are cached: a shared block's tiles
+ *                 are kept in L2 for its other readers, every other tile is
+ *                 streamed past the cache.  With flags, a batch of at most
+ *                 512 sequences is also worked through sorted by each
+ *                 sequence's first block, so siblings (samples, beams of
+ *                 one request), which share it, are read together wherever
+ *                 they sit in the batch.  The flags' values never change
+ *                 the result; a call with flags may cut the contexts into
+ *                 pieces elsewhere than one without, so the two can differ
+ *                 by rounding (both within the stated accuracy).  NULL: the
+ *                 batch order is kept, and a block counts as shared when
+ *                 the previous or the next sequence maps it at the same
+ *                 index, so siblings must sit side by side to keep their
+ *                 prompt blocks in cache.
  *
  * Work is balanced over the GPU: the grid holds two waves per SIMD, each
  * streaming an equal share of all (block, kv head) tiles of the batch,
@@ -147,7 +165,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            int head_size, int block_size, int max_blocks_per_seq,
                            int64_t num_blocks, int partition_size,
                            void* workspace, size_t workspace_bytes, int dtype,
-                           void* stream);
+                           const uint8_t* block_shared, void* stream);
 
 /*
  * paged_attention_decode_noalloc: paged_attention_decode without a
@@ -160,7 +178,8 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
  * looks up that device's copy (with the device current).
  *
  * Arguments, results and errors are those of paged_attention_decode (16-
- * and 32-bit pools, no new-token rows), with one more: sizes whose
+ * and 32-bit pools, no new-token rows, no block_shared flags: the
+ * neighbour rule decides the cache policy), with one more: sizes whose
  * workspace would not fit the array -- ranges = max(waves of this device's
  * grid, tiles of one launch / (partition_size / 16)), laid out as the
  * workspace above for the head-group size this dtype uses -- return
@@ -289,7 +308,7 @@ int paged_attention_decode_append(void* out, const void* query, void* key_cache,
                                   int block_size, int max_blocks_per_seq,
                                   int64_t num_blocks, int partition_size,
                                   void* workspace, size_t workspace_bytes, int dtype,
-                                  void* stream);
+                                  const uint8_t* block_shared, void* stream);
 
 /*
  * paged_attention_decode_fp8: paged_attention_decode over E4M3 pools, the
@@ -307,7 +326,8 @@ int paged_attention_decode_fp8(void* out, const void* query, const void* key_cac
                                int num_heads, int head_size, int block_size,
                                int max_blocks_per_seq, int64_t num_blocks,
                                int partition_size, void* workspace,
-                               size_t workspace_bytes, int dtype, void* stream);
+                               size_t workspace_bytes, int dtype,
+                               const uint8_t* block_shared, void* stream);
 
 /*
  * paged_attention_prefill

@@ -48,7 +48,7 @@ def _declare(lib):
     lib.paged_attention_decode.restype = c_int
     lib.paged_attention_decode.argtypes = [
         vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
-        c_i64, c_int, vp, c_sz, c_int, vp]
+        c_i64, c_int, vp, c_sz, c_int, vp, vp]
     lib.paged_attention_decode_noalloc.restype = c_int
     lib.paged_attention_decode_noalloc.argtypes = [
         vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -63,14 +63,14 @@ def _declare(lib):
     lib.paged_attention_decode_fp8.restype = c_int
     lib.paged_attention_decode_fp8.argtypes = [
         vp, vp, vp, vp, vp, vp, c_f, c_f, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
-        c_i64, c_int, vp, c_sz, c_int, vp]
+        c_i64, c_int, vp, c_sz, c_int, vp, vp]
     lib.reshape_and_cache_fp8.restype = c_int
     lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_f, c_f, c_int, c_int, c_int,
                                           c_int, c_i64, c_int, vp]
     lib.paged_attention_decode_append.restype = c_int
     lib.paged_attention_decode_append.argtypes = [
         vp, vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
-        c_i64, c_int, vp, c_sz, c_int, vp]
+        c_i64, c_int, vp, c_sz, c_int, vp, vp]
     lib.pkv_vpool_create.restype = c_int
     lib.pkv_vpool_create.argtypes = [c_i64, c_i64, ctypes.POINTER(vp)]
     lib.pkv_vpool_map.restype = c_int
@@ -183,7 +183,7 @@ def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per
 
 def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
             num_kv_heads, partition_size, workspace, validate, fp8, k_scale, v_scale,
-            new_key=None, new_value=None):
+            new_key=None, new_value=None, block_shared=None):
     import torch
     lib = load_library()
     _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens)
@@ -213,8 +213,13 @@ def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scal
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     common = (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
               _ptr(context_lens), float(scale))
+    if block_shared is not None:
+        _all_cuda_contiguous(block_shared)
+        _need(block_shared.dtype in (torch.uint8, torch.bool) and
+              tuple(block_shared.shape) == (NB,), "block_shared must be uint8 [num_blocks]")
+    flags = _ptr(block_shared) if block_shared is not None else ctypes.c_void_p(0)
     tail = (int(num_kv_heads), S, Hq, D, bs, W, NB, int(partition_size), ws_ptr, ws_len, code,
-            _stream_of(query))
+            flags, _stream_of(query))
     if fp8:
         _check(lib.paged_attention_decode_fp8(*common, float(k_scale), float(v_scale), *tail))
     elif new_key is not None:
@@ -232,15 +237,19 @@ def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scal
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
                            context_lens, scale, num_kv_heads, partition_size=0,
-                           workspace=None, validate=False):
+                           workspace=None, validate=False, block_shared=None):
     """One decode step of paged attention, written into `out` [S, Hq, D].
 
     key_cache / value_cache: [num_blocks, num_kv_heads, 16, head_size];
     block_tables int32 [S, W]; context_lens int32 [S]; query/out [S, Hq, D].
     `workspace` (uint8 device tensor) is allocated here if needed and None.
+    `block_shared` (uint8 [num_blocks], optional): nonzero for blocks that
+    more than one sequence maps (reference count above one); it chooses the
+    cache policy only, never the result.
     """
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                   num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0)
+                   num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0,
+                   block_shared=block_shared)
 
 
 def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
@@ -274,24 +283,27 @@ def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tab
 
 def paged_attention_decode_append(out, query, key_cache, value_cache, block_tables,
                                   context_lens, new_key, new_value, scale, num_kv_heads,
-                                  partition_size=0, workspace=None, validate=False):
+                                  partition_size=0, workspace=None, validate=False,
+                                  block_shared=None):
     """reshape_and_cache of each sequence's newest token followed by
     paged_attention_decode, in one call: new_key / new_value [S, Hkv, D]
     are token L - 1 of each sequence; they are written to that token's slot
     (table[(L-1)//16]*16 + (L-1)%16) and attended.  16/32-bit pools."""
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0,
-                   new_key, new_value)
+                   new_key, new_value, block_shared)
 
 
 def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,
                                context_lens, scale, k_scale, v_scale, num_kv_heads,
-                               partition_size=0, workspace=None, validate=False):
+                               partition_size=0, workspace=None, validate=False,
+                               block_shared=None):
     """paged_attention_decode over pools of E4M3 codes (float8_e4m3fn or
     uint8 tensors): keys are code values times k_scale, values times
     v_scale.  query/out float16 or bfloat16."""
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                   num_kv_heads, partition_size, workspace, validate, True, k_scale, v_scale)
+                   num_kv_heads, partition_size, workspace, validate, True, k_scale, v_scale,
+                   block_shared=block_shared)
 
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,

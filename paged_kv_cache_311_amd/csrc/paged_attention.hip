@@ -113,6 +113,9 @@ constexpr int kWaitAllLoads = 0x0F70;
 // Sequences one launch covers: their segment table lives in LDS.  The
 // host splits larger batches into consecutive launches.
 constexpr int kLdsSeqs = 2048;
+// Batches of at most this many sequences can be laid out sorted (see
+// sort_by_first_block).
+constexpr int kSortSeqs = 512;
 
 // DT: query / output element; KT: pool element (DT itself, or E4M3 codes
 // with 16-bit queries).
@@ -178,8 +181,8 @@ struct DecodeCfg {
   static constexpr int kPartFloats = GC * D + 2 * GC;
   static constexpr int kPartStride = (kPartFloats + 3) / 4 * 4;
   static constexpr int kLdsFixed =
-      kLdsSeqs * 8 + kWavesPerWG * (kPvMfma ? kBlockSize * kVS + 4 : kBlockSize * GC * 4 + 16) +
-      64;
+      kLdsSeqs * 8 + kSortSeqs * 4 +
+      kWavesPerWG * (kPvMfma ? kBlockSize * kVS + 4 : kBlockSize * GC * 4 + 16) + 64;
   static constexpr int kLdsPerWg = 160 * 1024 / kGridWaves - 1024;
   static constexpr int kStageFit = (kLdsPerWg - kLdsFixed) / kWavesPerWG / (kPartStride * 4);
   static constexpr int kStageRecs = kStageFit < 1 ? 0 : (kStageFit > 8 ? 8 : kStageFit);
@@ -211,6 +214,9 @@ struct DecodeParams {
   // writes them to the token's slot.
   const char* new_k;
   const char* new_v;
+  // Optional (null: the neighbour rule): per pool block, nonzero when more
+  // than one sequence maps it.
+  const uint8_t* block_shared;
 };
 
 // Head groups.  A kv head's `group` query heads are cut into hgk groups of
@@ -260,15 +266,121 @@ __device__ __forceinline__ int clamp_len(int L, int max_tokens) {
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlockSize - 1) / kBlockSize; }
 
 
+// With the caller's sharing flags, the sequences of a batch of at most
+// kSortSeqs are laid out in the flattened order sorted by their first
+// block: the siblings of a request (parallel samples, beams) share their
+// prompt's blocks from the first one on, so they then sit side by side
+// whatever their order in the batch, and the waves that read a shared
+// block read it at about the same time, mostly from L2.  One wave sorts
+// the keys (first block mod 2^20, sequence) in registers with a bitonic
+// network; the keys are distinct, so the order is deterministic.  Larger
+// batches, and calls without flags, keep the batch order.
+
+__device__ __forceinline__ bool sorts_batch(const DecodeParams& p) {
+  return p.block_shared != nullptr && p.num_seqs <= kSortSeqs;
+}
+
+// Places e in 1 .. n-1 of a wave's key array (element e = r * 64 + lane)
+// whose first block (key >> 11) differs from element e - 1's.
+template <int R>
+__device__ __forceinline__ int first_block_runs(const uint32_t (&key)[R], int n, int lane) {
+  int runs = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * kWave + lane;
+    const uint32_t up = (uint32_t)__shfl_up((int)key[r], 1, kWave);
+    const uint32_t last = (uint32_t)__shfl((int)key[r > 0 ? r - 1 : 0], kWave - 1, kWave);
+    const uint32_t prev = lane > 0 ? up : last;
+    runs += (e > 0 && e < n && (prev >> 11) != (key[r] >> 11)) ? 1 : 0;
+  }
+  return wave_sum_i(runs);
+}
+
+// order[i] = the sequence at position i of the flattened order, for the
+// first num_seqs <= N positions (one wave; N a power of two from 64 to
+// kSortSeqs, element e = r * 64 + lane in register r).
+template <int N>
+__device__ void sort_by_first_block(const DecodeParams& p, const int* len, int* order,
+                                    int lane) {
+  constexpr int R = N / kWave;
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * kWave + lane;
+    uint32_t k = 0xFFFFFFFFu;  // past the batch: sorted last
+    if (e < p.num_seqs) {
+      const uint32_t fb =
+          len[e] > 0 ? (uint32_t)p.block_tables[(int64_t)e * p.max_blocks] & 0xFFFFFu : 0xFFFFFu;
+      k = (fb << 11) | (uint32_t)e;  // e < 2^11
+    }
+    key[r] = k;
+  }
+  const int runs_batch = first_block_runs<R>(key, p.num_seqs, lane);
+  // bitonic network, ascending
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kWave) {  // partners in two registers of the same lane
+        const int rj = j / kWave;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r & rj) continue;
+          const int e = r * kWave + lane;
+          const bool up = (e & k) == 0;
+          const uint32_t a = key[r], b = key[r | rj];
+          const bool swap = up ? a > b : a < b;
+          key[r] = swap ? b : a;
+          key[r | rj] = swap ? a : b;
+        }
+      } else {  // partners in lanes lane ^ j: every register's exchange
+                // is issued before any is used
+        uint32_t o[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) o[r] = (uint32_t)__shfl_xor((int)key[r], j, kWave);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int e = r * kWave + lane;
+          const bool keep_min = ((e & k) == 0) == ((e & j) == 0);
+          key[r] = keep_min ? min(key[r], o[r]) : max(key[r], o[r]);
+        }
+      }
+    }
+  }
+  // A batch whose sibling groups are already contiguous keeps its own
+  // order: the sorted order has as many runs of equal first blocks as the
+  // batch order exactly then.  (Measured on one MI355X, decode call us,
+  // beam search / parallel sampling batches with the siblings side by
+  // side: 103 / 376 in their own order, 108 / 390 sorted; shuffled: 112 /
+  // 417 in their order, 110 / 380 sorted.)
+  const int runs_sorted = first_block_runs<R>(key, p.num_seqs, lane);
+  const bool keep = runs_batch == runs_sorted;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kWave + lane;
+    if (i < p.num_seqs) order[i] = keep ? i : (int)(key[r] & 0x7FFu);
+  }
+}
+
+__device__ void sort_batch(const DecodeParams& p, const int* len, int* order, int lane) {
+  if (p.num_seqs <= 64) sort_by_first_block<64>(p, len, order, lane);
+  else if (p.num_seqs <= 128) sort_by_first_block<128>(p, len, order, lane);
+  else if (p.num_seqs <= 256) sort_by_first_block<256>(p, len, order, lane);
+  else sort_by_first_block<kSortSeqs>(p, len, order, lane);
+}
+
 // Segment table of this launch's sequences, built in LDS by every thread of
-// the workgroup: len[s] = clamped context length, incl[s] = tiles of
-// sequences 0..s (blocks x head groups), summed.  Returns T = incl[S-1].
+// the workgroup: len[s] = clamped context length of sequence s, order[i] the
+// sequence at position i of the flattened order (when the batch is sorted;
+// else position i is sequence i), incl[i] = tiles of positions 0..i
+// (blocks x head groups), summed.  Returns T = incl[S-1].
 __device__ int build_segment_table(const DecodeParams& p, int head_groups, int* incl, int* len,
-                                   int* wsum, int lane, int w) {
+                                   int* order, int* wsum, int lane, int w) {
   const int S = p.num_seqs;
   const int max_tokens = p.max_blocks * kBlockSize;
-  const int per = (S + kThreads - 1) / kThreads;  // sequences per thread, contiguous
+  const int per = (S + kThreads - 1) / kThreads;  // positions per thread, contiguous
   const int s0 = threadIdx.x * per;
+  const bool sorted = sorts_batch(p);
   int sum = 0;
   for (int k = 0; k < per; ++k) {
     const int s = s0 + k;
@@ -276,6 +388,16 @@ __device__ int build_segment_table(const DecodeParams& p, int head_groups, int* 
       const int L = clamp_len(p.context_lens[s], max_tokens);
       len[s] = L;
       sum += blocks_of(L) * head_groups;
+    }
+  }
+  if (sorted) {
+    __syncthreads();
+    if (w == 0) sort_batch(p, len, order, lane);
+    __syncthreads();
+    sum = 0;
+    for (int k = 0; k < per; ++k) {
+      const int i = s0 + k;
+      if (i < S) sum += blocks_of(len[order[i]]) * head_groups;
     }
   }
   const int inc = wave_incl_scan_i(sum, lane);
@@ -290,18 +412,18 @@ __device__ int build_segment_table(const DecodeParams& p, int head_groups, int* 
     total += t;
   }
   for (int k = 0; k < per; ++k) {
-    const int s = s0 + k;
-    if (s < S) {
-      run += blocks_of(len[s]) * head_groups;
-      incl[s] = run;
+    const int i = s0 + k;
+    if (i < S) {
+      run += blocks_of(len[sorted ? order[i] : i]) * head_groups;
+      incl[i] = run;
     }
   }
   __syncthreads();
   return sread(total);
 }
 
-// Sequence whose tiles hold flattened position x < T: the first s with
-// incl[s] > x.
+// Position (in the flattened order) whose tiles hold flattened tile x < T:
+// the first i with incl[i] > x.
 __device__ __forceinline__ int seq_of(const int* incl, int S, int x) {
   int lo = 0, hi = S - 1;
   while (lo < hi) {
@@ -767,7 +889,8 @@ struct Window {
 // the block table).  The lane of the range's first tile also writes the
 // range's descriptor.
 __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const int* incl,
-                                 const int* len, int head_groups, int r, int xw, int lane) {
+                                 const int* len, const int* order, int head_groups, int r,
+                                 int xw, int lane) {
   Window wd;
   const int x0 = m.start(r);
   const int x1 = m.end(r);
@@ -780,28 +903,36 @@ __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const
   wd.info = 0;
   const int x = xw + lane;
   if (lane < wd.cnt) {
-    const int s = seq_of(incl, p.num_seqs, x);
-    const int excl = s > 0 ? incl[s - 1] : 0;
-    const int nb = (incl[s] - excl) / head_groups;
+    const int i = seq_of(incl, p.num_seqs, x);
+    const int s = sorts_batch(p) ? order[i] : i;
+    const int excl = i > 0 ? incl[i - 1] : 0;
+    const int nb = (incl[i] - excl) / head_groups;
     const int local = x - excl;
     const int hg = local / nb;
     const int n = local - hg * nb;
     const int64_t b_raw = p.block_tables[(int64_t)s * p.max_blocks + n];
+    const int64_t b = b_raw < 0 ? 0 : (b_raw >= p.num_blocks ? p.num_blocks - 1 : b_raw);
     // A tile is read by several waves in one call, and is worth keeping in
     // cache, when its kv head serves more than one head group (each group
-    // reads it), or when its block is shared: the sequences of one request
-    // (parallel samples, beams) sit side by side and share their prompt's
-    // blocks, so a block that the previous or the next sequence maps at the
-    // same index is taken as shared.  Every other tile is read once per
-    // call.  Both neighbours' entries are read on every path (clamped rows).
-    const int sp = s > 0 ? s - 1 : s;
-    const int sn = s + 1 < p.num_seqs ? s + 1 : s;
-    const int64_t b_prev = p.block_tables[(int64_t)sp * p.max_blocks + n];
-    const int64_t b_next = p.block_tables[(int64_t)sn * p.max_blocks + n];
-    const bool shared = head_groups > p.num_kv_heads ||
-                        (sp != s && n * kBlockSize < len[sp] && b_prev == b_raw) ||
-                        (sn != s && n * kBlockSize < len[sn] && b_next == b_raw);
-    const int64_t b = b_raw < 0 ? 0 : (b_raw >= p.num_blocks ? p.num_blocks - 1 : b_raw);
+    // reads it), or when its block is shared between sequences.  The
+    // caller's flags say which blocks are ([TEQ] "Paging's second gift":
+    // each block carries a reference count, kept by the runtime).  Without
+    // them, sequences of one request (parallel samples, beams) are taken to
+    // sit side by side: a block that the previous or the next sequence maps
+    // at the same index counts as shared (both neighbours' entries are read
+    // on every path, from rows clamped into the batch).  Every other tile
+    // is read once per call.
+    bool shared = head_groups > p.num_kv_heads;
+    if (p.block_shared != nullptr) {
+      shared = shared || p.block_shared[b] != 0;
+    } else {
+      const int sp = s > 0 ? s - 1 : s;
+      const int sn = s + 1 < p.num_seqs ? s + 1 : s;
+      const int64_t b_prev = p.block_tables[(int64_t)sp * p.max_blocks + n];
+      const int64_t b_next = p.block_tables[(int64_t)sn * p.max_blocks + n];
+      shared = shared || (sp != s && n * kBlockSize < len[sp] && b_prev == b_raw) ||
+               (sn != s && n * kBlockSize < len[sn] && b_next == b_raw);
+    }
     wd.id = (int)b;
     wd.s = s;
     int f = hg | (min(kBlockSize, len[s] - n * kBlockSize) << 16) | (shared ? kShared : 0);
@@ -838,6 +969,7 @@ paged_decode_kernel(const DecodeParams p) {
   float sm_stage[kWavesPerWG][C::kStageRecs > 0 ? C::kStageRecs * C::kPartStride : 4];
   __shared__ int sm_incl[kLdsSeqs];
   __shared__ int sm_len[kLdsSeqs];
+  __shared__ int sm_order[kSortSeqs];
   __shared__ int sm_wsum[kWavesPerWG];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -853,12 +985,12 @@ paged_decode_kernel(const DecodeParams p) {
   const int nwaves = nwg * kWavesPerWG;
 
   const int head_groups = p.num_kv_heads * p.hgk;
-  const int T = build_segment_table(p, head_groups, sm_incl, sm_len, sm_wsum, lane, w);
+  const int T = build_segment_table(p, head_groups, sm_incl, sm_len, sm_order, sm_wsum, lane, w);
 
   // sequences with no cached token: their output is zero
   for (int base = 0; base < p.num_seqs; base += kWave) {
     const int s = base + lane;
-    const bool empty = s < p.num_seqs && sm_incl[s] == (s > 0 ? sm_incl[s - 1] : 0);
+    const bool empty = s < p.num_seqs && sm_len[s] == 0;
     unsigned long long z = __ballot(empty && s % nwaves == v);
     while (z) {
       const int l = __ffsll((long long)z) - 1;
@@ -973,7 +1105,8 @@ paged_decode_kernel(const DecodeParams p) {
 
   // the wave's stream of tiles: windows cw (being computed) and nw (next)
   Window cw =
-      prepare_window(p, map, sm_incl, sm_len, head_groups, r_first, map.start(r_first), lane);
+      prepare_window(p, map, sm_incl, sm_len, sm_order, head_groups, r_first, map.start(r_first),
+                     lane);
   Window nw = cw;
   bool have_nw = false;
   bool no_more = false;  // no range after the current one
@@ -1036,7 +1169,7 @@ paged_decode_kernel(const DecodeParams p) {
     have_nw = r2 < r_end;
     no_more = r2 >= r_end;
     if (r2 < r_end)
-      nw = prepare_window(p, map, sm_incl, sm_len, head_groups, r2,
+      nw = prepare_window(p, map, sm_incl, sm_len, sm_order, head_groups, r2,
                           cw.ends_range ? map.start(r2) : cw.x + cw.cnt, lane);
   };
   auto step = [&](const Tile& tc, Tile& tn) __attribute__((always_inline)) {
@@ -1608,7 +1741,8 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
                        int block_size, int max_blocks_per_seq, int64_t num_blocks,
                        int partition_size, void* workspace, size_t workspace_bytes, int dtype,
                        int kv_dtype, void* stream, const void* new_key = nullptr,
-                       const void* new_value = nullptr, bool static_scratch = false) {
+                       const void* new_value = nullptr, bool static_scratch = false,
+                       const uint8_t* block_shared = nullptr) {
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if ((new_key == nullptr) != (new_value == nullptr)) return PKV_ERR_INVALID_ARG;
@@ -1677,6 +1811,7 @@ static int decode_impl(void* out, const void* query, const void* key_cache,
   a.vcache = (const char*)value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.block_shared = block_shared;
   // exp(x) = 2^(x log2 e); an E4M3 pool's key scale multiplies every logit
   a.scale_log2 = scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
@@ -1735,11 +1870,13 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
                                       int num_kv_heads, int num_seqs, int num_heads,
                                       int head_size, int block_size, int max_blocks_per_seq,
                                       int64_t num_blocks, int partition_size, void* workspace,
-                                      size_t workspace_bytes, int dtype, void* stream) {
+                                      size_t workspace_bytes, int dtype,
+                                      const uint8_t* block_shared, void* stream) {
   return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                           1.f, 1.f, num_kv_heads, num_seqs, num_heads, head_size, block_size,
                           max_blocks_per_seq, num_blocks, partition_size, workspace,
-                          workspace_bytes, dtype, dtype, stream);
+                          workspace_bytes, dtype, dtype, stream, nullptr, nullptr, false,
+                          block_shared);
 }
 
 extern "C" int paged_attention_decode_append(
@@ -1747,12 +1884,14 @@ extern "C" int paged_attention_decode_append(
     const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
     const void* new_value, float scale, int num_kv_heads, int num_seqs, int num_heads,
     int head_size, int block_size, int max_blocks_per_seq, int64_t num_blocks,
-    int partition_size, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    int partition_size, void* workspace, size_t workspace_bytes, int dtype,
+    const uint8_t* block_shared, void* stream) {
   if (!new_key || !new_value) return PKV_ERR_INVALID_ARG;
   return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                           1.f, 1.f, num_kv_heads, num_seqs, num_heads, head_size, block_size,
                           max_blocks_per_seq, num_blocks, partition_size, workspace,
-                          workspace_bytes, dtype, dtype, stream, new_key, new_value);
+                          workspace_bytes, dtype, dtype, stream, new_key, new_value, false,
+                          block_shared);
 }
 
 extern "C" int paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
@@ -1763,12 +1902,13 @@ extern "C" int paged_attention_decode_fp8(void* out, const void* query, const vo
                                           int block_size, int max_blocks_per_seq,
                                           int64_t num_blocks, int partition_size,
                                           void* workspace, size_t workspace_bytes, int dtype,
-                                          void* stream) {
+                                          const uint8_t* block_shared, void* stream) {
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   return pkv::decode_impl(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                           k_scale, v_scale, num_kv_heads, num_seqs, num_heads, head_size,
                           block_size, max_blocks_per_seq, num_blocks, partition_size, workspace,
-                          workspace_bytes, dtype, PKV_FP8_E4M3, stream);
+                          workspace_bytes, dtype, PKV_FP8_E4M3, stream, nullptr, nullptr, false,
+                          block_shared);
 }
 
 extern "C" int paged_attention_decode_noalloc(void* out, const void* query,

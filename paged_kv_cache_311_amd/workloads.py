@@ -29,6 +29,9 @@ sampling over a shared prompt, long contexts):
   opt13b_fp8,    the same shapes and lengths with pools of OCP E4M3 codes
   long_gqa_fp8   and one scale per pool (keys 1/64, values 3/128); queries,
                  outputs and new tokens stay fp16 / bf16.
+  sampling_cow_shuffled, beam_shuffled
+                 the same batches with the sequences in a random order, so
+                 the siblings of a request are no longer neighbours.
   beam           beam search: 16 requests x 4 beams, 40 heads of 128, fp16,
                  prompts U{256..1024} shared by their beams; 24 steps of
                  appends (copy-on-write of shared partial blocks) with beams
@@ -87,6 +90,8 @@ class Workload:
     kv_dtype: str = ""      # "" (pools in `dtype`) | "e4m3" (pools of E4M3 codes)
     k_scale: float = 1.0    # per-pool scales of an E4M3 pool
     v_scale: float = 1.0
+    shuffle: bool = False   # (cow / beam) sequences in a random order instead of
+                            # each request's siblings side by side
 
     @property
     def max_query_len(self):
@@ -151,6 +156,13 @@ WORKLOADS = {
                  ("factor", 1.25), "decode", 32768),
         Workload("beam", 11, 64, 40, 40, 128, "f16", ("beam", 256, 1024, 24),
                  ("factor", 1.25), "beam", 1056, prompts=16, samples=4),
+        # the same two batches with their sequences in a random order (the
+        # siblings of a request no longer side by side)
+        Workload("sampling_cow_shuffled", 4, 256, 40, 40, 128, "f16",
+                 ("cow", 64, 1024, 1, 64), ("factor", 1.25), "cow", 1088,
+                 prompts=32, samples=8, shuffle=True),
+        Workload("beam_shuffled", 11, 64, 40, 40, 128, "f16", ("beam", 256, 1024, 24),
+                 ("factor", 1.25), "beam", 1056, prompts=16, samples=4, shuffle=True),
         Workload("prefill_chunk", 8, 16, 40, 40, 128, "f16", ("prefill", 0, 1536, 512, 512),
                  ("factor", 1.25), "prefill", 2048),
         Workload("prefill_gqa", 9, 8, 32, 8, 128, "bf16", ("prefill", 0, 0, 2048, 2048),
@@ -377,8 +389,9 @@ def draw_metadata(w, seed):
         md["token_seq"] = np.asarray(token_seq, dtype=np.int64)
         md["cow_pairs"] = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
         md["shared_blocks"] = int((mgr.ref > 1).sum())
+        md["block_shared"] = (mgr.ref > 1).astype(np.uint8)
         md["prompt_lens"] = P.astype(np.int64)
-        return md
+        return _shuffled(md, seed) if w.shuffle else md
 
     if w.step == "beam":
         # beam search: each request's beams share its prompt; every step each
@@ -429,10 +442,30 @@ def draw_metadata(w, seed):
         md["token_seq"] = np.arange(len(beams), dtype=np.int64)
         md["cow_pairs"] = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
         md["shared_blocks"] = int((mgr.ref > 1).sum())
+        md["block_shared"] = (mgr.ref > 1).astype(np.uint8)
         md["prompt_lens"] = P.astype(np.int64)
         md["forks"] = forks
-        return md
+        return _shuffled(md, seed) if w.shuffle else md
     raise ValueError(w.step)
+
+
+def _shuffled(md, seed):
+    """The same batch with its sequences in a seeded random order: rows of
+    the tables and lengths permuted, each new token moved with its sequence
+    (tokens stay grouped by sequence, in the new order); blocks, slots and
+    copy pairs are unchanged."""
+    perm = np.random.default_rng(seed + 7777).permutation(len(md["context_lens"]))
+    new_of_old = np.empty_like(perm)
+    new_of_old[perm] = np.arange(len(perm))
+    md = dict(md)
+    md["context_lens"] = md["context_lens"][perm]
+    md["block_tables"] = md["block_tables"][perm]
+    ts = new_of_old[md["token_seq"]]
+    order = np.argsort(ts, kind="stable")
+    md["token_seq"] = ts[order].astype(np.int64)
+    md["slot_mapping"] = md["slot_mapping"][order]
+    md["sequence_order"] = perm.astype(np.int64)
+    return md
 
 
 _TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}

@@ -33,17 +33,23 @@ def dev_i64(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(DEV)
 
 
-def run_decode(b, partition_size=None, out=None):
+def run_decode(b, partition_size=None, out=None, flags="batch"):
+    """The decode call on a batch; `flags`: "batch" passes the batch's
+    block_shared flags when it has them, None passes none, or a tensor."""
     w = b["workload"]
     ps = w.partition_size if partition_size is None else partition_size
     out = torch.empty_like(b["query"]) if out is None else out
+    if isinstance(flags, str):
+        flags = (torch.from_numpy(b["block_shared"]).to(DEV) if "block_shared" in b
+                 else None)
     args = (out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
             dev_i32(b["context_lens"]), float(w.scale))
     if w.fp8:
         pkv.paged_attention_decode_fp8(*args, w.k_scale, w.v_scale, w.num_kv_heads,
-                                       partition_size=ps)
+                                       partition_size=ps, block_shared=flags)
     else:
-        pkv.paged_attention_decode(*args, w.num_kv_heads, partition_size=ps)
+        pkv.paged_attention_decode(*args, w.num_kv_heads, partition_size=ps,
+                                   block_shared=flags)
     torch.cuda.synchronize()
     return out
 

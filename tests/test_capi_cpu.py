@@ -67,7 +67,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 6
+    assert lib.pkv_abi_version() == 7
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -122,7 +122,7 @@ def decode(lib, **kw):
     return lib.paged_attention_decode(
         a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["hkv"],
         a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ps"], a["ws"], a["wsb"],
-        a["dtype"], a["stream"])
+        a["dtype"], None, a["stream"])
 
 
 def test_decode_argument_validation(lib):
@@ -205,7 +205,7 @@ def decode_fp8(lib, **kw):
     return lib.paged_attention_decode_fp8(
         a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["ks"], a["vs"],
         a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ps"], a["ws"],
-        a["wsb"], a["dtype"], a["stream"])
+        a["wsb"], a["dtype"], None, a["stream"])
 
 
 def test_fp8_argument_validation(lib):
@@ -307,7 +307,7 @@ def test_decode_append_argument_validation(lib):
         return lib.paged_attention_decode_append(
             a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["nk"], a["nv"],
             a["scale"], a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ps"],
-            a["ws"], a["wsb"], a["dtype"], a["stream"])
+            a["ws"], a["wsb"], a["dtype"], None, a["stream"])
     assert app() == WORKSPACE                      # valid up to the workspace
     assert app(nk=0) == INVALID
     assert app(nv=0) == INVALID

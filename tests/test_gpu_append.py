@@ -54,10 +54,11 @@ def run_append(b, nk, nv, partition_size=None, out=None):
     w = b["workload"]
     ps = w.partition_size if partition_size is None else partition_size
     out = torch.empty_like(b["query"]) if out is None else out
+    flags = torch.from_numpy(b["block_shared"]).to(DEV) if "block_shared" in b else None
     pkv.paged_attention_decode_append(out, b["query"], b["key_cache"], b["value_cache"],
                                       dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
                                       nk, nv, float(w.scale), w.num_kv_heads,
-                                      partition_size=ps, validate=True)
+                                      partition_size=ps, validate=True, block_shared=flags)
     torch.cuda.synchronize()
     return out
 

@@ -197,3 +197,31 @@ def test_beam_step_copies_shared_partial_blocks():
     # the first prompt block of a request is shared by all its beams
     first = bt[:, 0].reshape(w.prompts, w.samples)
     assert (first == first[:, :1]).all()
+
+
+@pytest.mark.parametrize("base", ["sampling_cow", "beam"])
+def test_shuffled_batches_are_the_same_batch_reordered(base):
+    """The shuffled sibling workloads hold the ordered batch's sequences in
+    another order: the same rows, every new token still in a block of its
+    own sequence's table at that sequence's next position, and the same
+    blocks flagged as shared (reference count above one)."""
+    w0 = wl.WORKLOADS[base]
+    w1 = wl.WORKLOADS[base + "_shuffled"]
+    a = wl.draw_metadata(w0, w0.default_seed)
+    b = wl.draw_metadata(w1, w1.default_seed)
+    perm = b["sequence_order"]
+    assert not np.array_equal(perm, np.arange(len(perm)))
+    assert np.array_equal(b["context_lens"], a["context_lens"][perm])
+    assert np.array_equal(b["block_tables"], a["block_tables"][perm])
+    assert np.array_equal(np.sort(b["slot_mapping"]), np.sort(a["slot_mapping"]))
+    assert (np.diff(b["token_seq"]) >= 0).all()
+    for slot, s in zip(b["slot_mapping"], b["token_seq"]):
+        assert slot // 16 in set(b["block_tables"][s].tolist())
+    assert np.array_equal(b["block_shared"], a["block_shared"])
+    assert np.array_equal(b["cow_pairs"], a["cow_pairs"])
+    # flags = blocks that more than one sequence's table maps
+    counts = np.zeros(a["num_blocks"], np.int64)
+    for s, L in enumerate(a["context_lens"]):
+        for x in a["block_tables"][s, :-(-int(L) // 16)]:
+            counts[x] += 1
+    assert np.array_equal(a["block_shared"], (counts > 1).astype(np.uint8))

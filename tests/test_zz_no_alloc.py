@@ -45,8 +45,8 @@ def c_workspace(lib, out, b, ps, bt, cl):
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     return lib.paged_attention_decode(
         p(out), p(b["query"]), p(b["key_cache"]), p(b["value_cache"]), p(bt), p(cl),
-        float(w.scale), w.num_kv_heads, S, Hq, D, 16, bt.shape[1], NB, ps, ctypes.c_void_p(ws.data_ptr()),
-        need, code, stream), ws
+        float(w.scale), w.num_kv_heads, S, Hq, D, 16, bt.shape[1], NB, ps,
+        ctypes.c_void_p(ws.data_ptr()), need, code, None, stream), ws
 
 
 def one_call(lib, b, ps, seqs):
