@@ -59,6 +59,11 @@ int32_t pkv_bm_num_free(const pkv_bm* bm);
 int32_t pkv_bm_num_sequences(const pkv_bm* bm);
 /* References to a block (0 = free); -1 for an id outside the pool. */
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
+/* flags[b] = 1 where block b has more than one reference, else 0, for every
+ * block of the pool (the block_shared argument of the decode calls of
+ * pagedkv.h, once copied to the device).  n is the capacity of flags (at
+ * least num_blocks).  Returns num_blocks, or PKV_BM_INVALID. */
+int32_t pkv_bm_shared_flags(const pkv_bm* bm, uint8_t* flags, int32_t n);
 
 /*
  * A new sequence seq_id holding num_tokens tokens (its prompt): takes

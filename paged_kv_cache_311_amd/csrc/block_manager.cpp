@@ -45,7 +45,7 @@ struct pkv_bm {
 
 extern "C" {
 
-int pkv_bm_abi_version(void) { return 1; }
+int pkv_bm_abi_version(void) { return 2; }
 
 pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size) {
   if (num_blocks <= 0 || block_size <= 0) return nullptr;
@@ -76,6 +76,12 @@ int32_t pkv_bm_num_sequences(const pkv_bm* bm) { return bm ? (int32_t)bm->seqs.s
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
   return bm->refcount[block];
+}
+
+int32_t pkv_bm_shared_flags(const pkv_bm* bm, uint8_t* flags, int32_t n) {
+  if (!bm || !flags || n < bm->num_blocks) return PKV_BM_INVALID;
+  for (int32_t b = 0; b < bm->num_blocks; ++b) flags[b] = bm->refcount[b] > 1 ? 1 : 0;
+  return bm->num_blocks;
 }
 
 int pkv_bm_add_sequence(pkv_bm* bm, int64_t seq_id, int64_t num_tokens) {

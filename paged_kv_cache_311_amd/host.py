@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB_PATH = os.path.join(HERE, "libpkvhost.so")
 
 OK, INVALID, NO_BLOCKS = 0, -1, -5
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 
@@ -64,6 +64,7 @@ def load_host_library(path=HOST_LIB_PATH):
         "pkv_bm_num_free": ([P], I32),
         "pkv_bm_num_sequences": ([P], I32),
         "pkv_bm_refcount": ([P, I32], I32),
+        "pkv_bm_shared_flags": ([P, P, I32], I32),
         "pkv_bm_add_sequence": ([P, I64, I64], ctypes.c_int),
         "pkv_bm_fork": ([P, I64, I64], ctypes.c_int),
         "pkv_bm_append_slot": ([P, I64, P, P, P], ctypes.c_int),
@@ -120,6 +121,15 @@ class BlockManager:
 
     def refcount(self, block):
         return self._lib.pkv_bm_refcount(self._h, int(block))
+
+    def shared_flags(self):
+        """uint8 [num_blocks]: 1 where a block has more than one reference
+        (the decode calls' block_shared flags)."""
+        out = np.zeros(self.num_blocks, dtype=np.uint8)
+        n = self._lib.pkv_bm_shared_flags(self._h, out.ctypes.data_as(ctypes.c_void_p),
+                                          len(out))
+        _check(n if n < 0 else 0)
+        return out
 
     def add_sequence(self, seq_id, num_tokens):
         _check(self._lib.pkv_bm_add_sequence(self._h, int(seq_id), int(num_tokens)))

@@ -51,6 +51,8 @@ def check_invariants(bm, seqs):
     counts = np.asarray([bm.refcount(b) for b in range(bm.num_blocks)])
     assert (counts == refs).all(), "reference counts differ from table references"
     assert bm.num_free == int((counts == 0).sum())
+    # the decode calls' sharing flags: blocks that more than one table maps
+    assert np.array_equal(bm.shared_flags(), (refs > 1).astype(np.uint8))
     assert bm.num_sequences == len(seqs)
 
 

@@ -78,8 +78,11 @@ def test_beam_decode_loop_driven_by_host_manager(gpu_lib, num_heads, num_kv_head
         tables, lens = bm.block_tables(live, W)
         q = randn(len(live), num_heads, D)
         out = torch.empty_like(q)
+        # the manager's reference counts above one as the cache-policy flags
+        flags = torch.from_numpy(bm.shared_flags()).to(DEV) if step % 2 else None
         pkv.paged_attention_decode(out, q, kc, vc, torch.from_numpy(tables).to(DEV),
-                                   torch.from_numpy(lens).to(DEV), scale, num_kv_heads)
+                                   torch.from_numpy(lens).to(DEV), scale, num_kv_heads,
+                                   block_shared=flags)
         torch.cuda.synchronize()
         assert wl.to_host(kc).view(np.uint16).tobytes() == kc_h.view(np.uint16).tobytes()
         assert wl.to_host(vc).view(np.uint16).tobytes() == vc_h.view(np.uint16).tobytes()
