@@ -184,10 +184,10 @@ class Step:
                       if pairs is not None and len(pairs) else None)
         self.new_tokens = len(slots)
         # one new token per sequence, token s of sequence s, at position L-1:
-        # the decode call caches it itself (16/32-bit pools)
+        # the decode call caches it itself
         one_each = ("slot_mapping" not in b
                     or np.array_equal(b.get("token_seq", []), np.arange(w.num_seqs)))
-        self.fused = bool(fuse and not w.fp8 and one_each and (lens >= 1).all())
+        self.fused = bool(fuse and one_each and (lens >= 1).all())
 
     def updates(self):
         b, w = self.b, self.w
@@ -217,7 +217,12 @@ class Step:
 
     def decode(self):
         b, w = self.b, self.w
-        if self.fused:
+        if self.fused and w.fp8:
+            self.pkv.paged_attention_decode_append_fp8(
+                self.out, b["query"], b["key_cache"], b["value_cache"], self.bt, self.cl,
+                self.key, self.value, float(w.scale), w.k_scale, w.v_scale, w.num_kv_heads,
+                partition_size=self.ps, workspace=self.ws, block_shared=self.flags)
+        elif self.fused:
             self.pkv.paged_attention_decode_append(
                 self.out, b["query"], b["key_cache"], b["value_cache"], self.bt, self.cl,
                 self.key, self.value, float(w.scale), w.num_kv_heads, partition_size=self.ps,
@@ -766,8 +771,10 @@ def emit(a, w, main_r, cpu, trans, others, prefill):
         "pct_of_hbm_peak": round(main_r["pct_of_hbm_peak"], 2),
         "decode_tokens_per_s": round(main_r["decode_tokens_per_s"], 1),
         "roofline": {
-            "kernel": (("paged_attention_decode_append" if main_r["append"].startswith("fused")
-                        else "paged_attention_decode") +
+            "kernel": ((("paged_attention_decode_append_fp8" if w.fp8 else
+                         "paged_attention_decode_append") if main_r["append"].startswith("fused")
+                        else ("paged_attention_decode_fp8" if w.fp8 else
+                              "paged_attention_decode")) +
                        " call (decode kernel + merge kernel)"),
             "timing": main_r["decode_call_timing"],
             "bound": "hbm",

@@ -80,7 +80,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 7 */
+int pkv_abi_version(void);  /* 8 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -297,8 +297,8 @@ int reshape_and_cache_fp8(const void* key, const void* value,
  * result equals reshape_and_cache of those rows to those slots followed by
  * paged_attention_decode (same arguments otherwise).  The block holding a
  * new token must not be shared (copy it first, as for reshape_and_cache).
- * Pools in `dtype` (not E4M3: UNSUPPORTED).  Sequences with L = 0 write
- * nothing.
+ * Pools in `dtype` (E4M3 pools: paged_attention_decode_append_fp8).
+ * Sequences with L = 0 write nothing.
  */
 int paged_attention_decode_append(void* out, const void* query, void* key_cache,
                                   void* value_cache, const int32_t* block_tables,
@@ -328,6 +328,34 @@ int paged_attention_decode_fp8(void* out, const void* query, const void* key_cac
                                int partition_size, void* workspace,
                                size_t workspace_bytes, int dtype,
                                const uint8_t* block_shared, void* stream);
+
+/*
+ * paged_attention_decode_append_fp8: the appending decode step over E4M3
+ * pools -- reshape_and_cache_fp8 of each sequence's newest token followed
+ * by paged_attention_decode_fp8, in one launch.  For every sequence s with
+ * L = context_lens[s] >= 1, token L - 1 is the new one: its key and value
+ * rows new_key[s], new_value[s] ([num_seqs][num_kv_heads][head_size],
+ * `dtype`, PKV_F16 or PKV_BF16) are encoded as reshape_and_cache_fp8
+ * encodes them (the code nearest to the float32 quotient by k_scale /
+ * v_scale, ties to even, saturating at +-448, NaN to 0x7F), the codes are
+ * written to the token's slot, block_tables[s][(L-1)/16] * 16 + (L-1) % 16
+ * ([TEQ] "The OS already solved this in the 1960s"), and the attention
+ * over tokens 0 .. L-1 uses them.  The result -- pools and outputs -- equals
+ * reshape_and_cache_fp8 of those rows to those slots followed by
+ * paged_attention_decode_fp8 with the same arguments.  The block holding a
+ * new token must not be shared.  Sequences with L = 0 write nothing.
+ * Other arguments, workspace and errors as for paged_attention_decode_fp8.
+ */
+int paged_attention_decode_append_fp8(void* out, const void* query, void* key_cache,
+                                      void* value_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const void* new_key,
+                                      const void* new_value, float scale, float k_scale,
+                                      float v_scale, int num_kv_heads, int num_seqs,
+                                      int num_heads, int head_size, int block_size,
+                                      int max_blocks_per_seq, int64_t num_blocks,
+                                      int partition_size, void* workspace,
+                                      size_t workspace_bytes, int dtype,
+                                      const uint8_t* block_shared, void* stream);
 
 /*
  * paged_attention_prefill

@@ -3,8 +3,9 @@
 The three operations -- paged_attention_decode, reshape_and_cache and
 copy_blocks -- the fp8 variants of the first two (pools of E4M3 codes with
 one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8),
-paged_attention_decode_append (a decode step that also caches each
-sequence's newest token) and paged_attention_prefill (causal attention of
+paged_attention_decode_append and paged_attention_decode_append_fp8 (a
+decode step that also caches each sequence's newest token), the
+allocation-free paged_attention_decode_noalloc, and paged_attention_prefill (causal attention of
 a chunk of new tokens) run entirely in the HIP kernels of libpagedkv.so
 (declared in include/pagedkv.h).  This module only marshals torch tensors (device
 memory and the current stream) into the C calls and raises on a nonzero
@@ -71,6 +72,10 @@ def _declare(lib):
     lib.paged_attention_decode_append.argtypes = [
         vp, vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
         c_i64, c_int, vp, c_sz, c_int, vp, vp]
+    lib.paged_attention_decode_append_fp8.restype = c_int
+    lib.paged_attention_decode_append_fp8.argtypes = [
+        vp, vp, vp, vp, vp, vp, vp, vp, c_f, c_f, c_f, c_int, c_int, c_int, c_int, c_int,
+        c_int, c_i64, c_int, vp, c_sz, c_int, vp, vp]
     lib.pkv_vpool_create.restype = c_int
     lib.pkv_vpool_create.argtypes = [c_i64, c_i64, ctypes.POINTER(vp)]
     lib.pkv_vpool_map.restype = c_int
@@ -220,14 +225,19 @@ def _decode(out, query, key_cache, value_cache, block_tables, context_lens, scal
     flags = _ptr(block_shared) if block_shared is not None else ctypes.c_void_p(0)
     tail = (int(num_kv_heads), S, Hq, D, bs, W, NB, int(partition_size), ws_ptr, ws_len, code,
             flags, _stream_of(query))
-    if fp8:
-        _check(lib.paged_attention_decode_fp8(*common, float(k_scale), float(v_scale), *tail))
-    elif new_key is not None:
+    if new_key is not None:
         _all_cuda_contiguous(new_key, new_value)
         _need(new_key.dtype == query.dtype and new_value.dtype == query.dtype,
               "new keys and values share the query's dtype")
         _need(tuple(new_key.shape) == (S, Hkv, D) and tuple(new_value.shape) == (S, Hkv, D),
               "new keys and values are [S, Hkv, D]")
+    if fp8 and new_key is not None:
+        _check(lib.paged_attention_decode_append_fp8(
+            *common[:6], _ptr(new_key), _ptr(new_value), common[6], float(k_scale),
+            float(v_scale), *tail))
+    elif fp8:
+        _check(lib.paged_attention_decode_fp8(*common, float(k_scale), float(v_scale), *tail))
+    elif new_key is not None:
         _check(lib.paged_attention_decode_append(*common[:6], _ptr(new_key), _ptr(new_value),
                                                  common[6], *tail))
     else:
@@ -245,7 +255,8 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
     `workspace` (uint8 device tensor) is allocated here if needed and None.
     `block_shared` (uint8 [num_blocks], optional): nonzero for blocks that
     more than one sequence maps (reference count above one); it chooses the
-    cache policy only, never the result.
+    cache policy (and, with up to 512 sequences, the order the batch is
+    worked through), never the result beyond rounding.
     """
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0,
@@ -304,6 +315,20 @@ def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, True, k_scale, v_scale,
                    block_shared=block_shared)
+
+
+def paged_attention_decode_append_fp8(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, new_key, new_value, scale, k_scale, v_scale,
+                                      num_kv_heads, partition_size=0, workspace=None,
+                                      validate=False, block_shared=None):
+    """reshape_and_cache_fp8 of each sequence's newest token followed by
+    paged_attention_decode_fp8, in one call: new_key / new_value [S, Hkv, D]
+    (the query's 16-bit type) are token L - 1 of each sequence; their E4M3
+    codes (of new_key / k_scale, new_value / v_scale) are written to that
+    token's slot and attended."""
+    return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                   num_kv_heads, partition_size, workspace, validate, True, k_scale, v_scale,
+                   new_key, new_value, block_shared)
 
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,

@@ -38,6 +38,7 @@ def test_header_declares_the_three_operations():
     for n in ("paged_attention_decode", "reshape_and_cache", "copy_blocks",
               "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
               "paged_attention_decode_append", "paged_attention_decode_noalloc",
+              "paged_attention_decode_append_fp8",
               "paged_attention_workspace_bytes", "pkv_status_string", "pkv_abi_version"):
         assert n in names
 
@@ -67,7 +68,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 7
+    assert lib.pkv_abi_version() == 8
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")

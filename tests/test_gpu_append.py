@@ -55,10 +55,15 @@ def run_append(b, nk, nv, partition_size=None, out=None):
     ps = w.partition_size if partition_size is None else partition_size
     out = torch.empty_like(b["query"]) if out is None else out
     flags = torch.from_numpy(b["block_shared"]).to(DEV) if "block_shared" in b else None
-    pkv.paged_attention_decode_append(out, b["query"], b["key_cache"], b["value_cache"],
-                                      dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
-                                      nk, nv, float(w.scale), w.num_kv_heads,
-                                      partition_size=ps, validate=True, block_shared=flags)
+    args = (out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
+            dev_i32(b["context_lens"]), nk, nv, float(w.scale))
+    if w.fp8:
+        pkv.paged_attention_decode_append_fp8(*args, w.k_scale, w.v_scale, w.num_kv_heads,
+                                              partition_size=ps, validate=True,
+                                              block_shared=flags)
+    else:
+        pkv.paged_attention_decode_append(*args, w.num_kv_heads, partition_size=ps,
+                                          validate=True, block_shared=flags)
     torch.cuda.synchronize()
     return out
 
@@ -101,8 +106,12 @@ def append_and_check(b, seqs=None, partition_size=None, seed=0, against_separate
             pkv.copy_blocks(kc1, vc1, dev_i64(pairs))
         if len(live):
             lt = torch.from_numpy(live).to(DEV)
-            pkv.reshape_and_cache(nk[lt].contiguous(), nv[lt].contiguous(), dev_i64(slots),
-                                  kc1, vc1)
+            if w.fp8:
+                pkv.reshape_and_cache_fp8(nk[lt].contiguous(), nv[lt].contiguous(),
+                                          dev_i64(slots), kc1, vc1, w.k_scale, w.v_scale)
+            else:
+                pkv.reshape_and_cache(nk[lt].contiguous(), nv[lt].contiguous(), dev_i64(slots),
+                                      kc1, vc1)
         sep = run_decode(dict(b, key_cache=kc1, value_cache=vc1), partition_size=partition_size)
         assert torch.equal(bits(kc1), bits(b["key_cache"]))
         assert torch.equal(bits(vc1), bits(b["value_cache"]))
