@@ -391,7 +391,16 @@ int paged_attention_decode_append_fp8(void* out, const void* query, void* key_ca
  * (new token, query head of the group) pairs; keys are walked 32 at a
  * time through LDS and both products run on MFMA with float32
  * accumulation.  The probabilities enter the second product rounded to
- * `dtype`.  No workspace.  Errors: INVALID_ARG for null pointers, sizes
+ * `dtype`.  No workspace.
+ *
+ * Masking: keys past a row's position get probability 0 by selection, and
+ * tokens past the context are read as zeros, so whatever the pools hold
+ * there never reaches a result.  In the 32-key steps that mask keys for
+ * some rows of a workgroup, the values of the keys past its earliest row
+ * are made finite before the second product (an infinity or NaN becomes
+ * the largest finite value of its sign, NaN: +): rows that do not see such
+ * a key are exact, rows that do see a non-finite value there get that
+ * largest value in its place rather than an infinity or NaN.  Errors: INVALID_ARG for null pointers, sizes
  * out of range, Hq % Hkv != 0 or misalignment; UNSUPPORTED for other
  * dtypes, block_size != 16 or head_size not 64/128.  Device-side contents
  * (tables, lengths, query_start_loc) are not validated; every read stays

@@ -109,6 +109,20 @@ struct Params {
 
 
 
+// The two 16-bit values of a word, each made finite where asked: an
+// infinity or NaN (exponent all ones) becomes the largest finite value of
+// its sign (a NaN's sign bit is ignored: +).
+template <int DT>
+__device__ __forceinline__ uint32_t finite_pair(uint32_t w, bool lo, bool hi) {
+  constexpr uint32_t kExp = DT == PKV_BF16 ? 0x7F80u : 0x7C00u;
+  constexpr uint32_t kMax = DT == PKV_BF16 ? 0x7F7Fu : 0x7BFFu;  // largest finite
+  const uint32_t a = w & 0xFFFFu, b = w >> 16;
+  const bool nan_a = (a & 0x7FFFu) > kExp, nan_b = (b & 0x7FFFu) > kExp;
+  const uint32_t fa = (a & kExp) == kExp ? ((nan_a ? 0u : (a & 0x8000u)) | kMax) : a;
+  const uint32_t fb = (b & kExp) == kExp ? ((nan_b ? 0u : (b & 0x8000u)) | kMax) : b;
+  return (lo ? fa : a) | ((hi ? fb : b) << 16);
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params p) {
   using LD = Lds<D>;
@@ -197,10 +211,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     in_blk[u] = (uint32_t)(head_bytes + (tk_u[u] % kBlockSize) * D * 2 + (c - tk_u[u] * CPR) * 16);
   }
   // Tokens past the context are read from the sequence's first block
-  // instead (same row): from the second step on, the context holds more
-  // than 32 tokens, so that block is full of cached tokens, whose values
-  // the zero probabilities of masked tokens then multiply.  The first step
-  // is stored with explicit zeros past the context.
+  // instead (same row, a slot of the context, so the load is in bounds and
+  // uniform) and stored to LDS as zeros.
   int32_t ids[NCH], ids_next[NCH];
   auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
 #pragma unroll
@@ -222,24 +234,37 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       st.v[u] = load16(p.vcache + off);
     }
   };
-  auto lstore = [&](const Stage& st, int buf) {
+  // Stored to LDS as rows.  A masked probability is an exact zero, but the
+  // second product still meets the value it multiplies (0 x inf = NaN), so
+  // on the steps that mask keys for some row of the workgroup (or reach
+  // past the context) the values are made safe first: tokens past the
+  // context become zeros, whatever the slot read in their place holds, and
+  // the non-finite values of keys past the workgroup's earliest row become
+  // the largest finite value of their sign (NaN: +).  Rows that do not see
+  // such a key are then exact; rows that see a non-finite value there get
+  // that largest value in its place.  Other steps are stored as read.
+  const int wg_pos0 = base + R0 / G;  // position of the workgroup's earliest row
+  auto lstore = [&](const Stage& st, int buf, int step) {
     char* kb = lds + buf * LD::kKBuf;
     char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
+    const bool edge = step * kKeys + kKeys - 1 > wg_pos0;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + u * kThreads;
       const int tk = c / CPR;
-      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, st.k[u]);
-      store16(vb + tk * LD::kVS + (c - tk * CPR) * 16, st.v[u]);
-    }
-  };
-  auto zero_tail = [&](Stage& st) {  // first step: tokens past the context
+      u32x4 kv = st.k[u], vv = st.v[u];
+      if (edge) {
+        const int t = step * kKeys + tk_u[u];
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+        if (t > wg_pos0) {
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      if (tk_u[u] >= Lc) {
-        st.k[u] = u32x4{0u, 0u, 0u, 0u};
-        st.v[u] = u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < 4; ++i) vv[i] = finite_pair<DT>(vv[i], true, true);
+        }
+        kv = t >= Lc ? zero : kv;
+        vv = t >= Lc ? zero : vv;
       }
+      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kv);
+      store16(vb + tk * LD::kVS + (c - tk * CPR) * 16, vv);
     }
   };
 
@@ -355,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
     }
 
-    if (step + 1 < nsteps) lstore(ready, buf ^ 1);
+    if (step + 1 < nsteps) lstore(ready, buf ^ 1, step + 1);
 #pragma unroll
     for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
     __syncthreads();
@@ -367,8 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     read_ids(1, ids);
     gload(sb, ids);
     read_ids(2, ids);
-    zero_tail(sa);
-    lstore(sa, 0);
+    lstore(sa, 0, 0);
   }
   __syncthreads();
   for (int step = 0; step < nsteps; step += 2) {

@@ -203,3 +203,45 @@ def test_prefill_of_a_long_prompt_in_chunks_matches_whole(gpu_lib):
     diff = (torch.cat(parts).float() - whole.float()).abs().max().item()
     say(f"    chunked vs whole prompt: max diff {diff:.2e}")
     assert diff <= 2e-3
+
+
+@pytest.mark.parametrize("bad", [float("inf"), float("-inf"), float("nan")])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_nonfinite_value_stays_with_rows_that_see_it(gpu_lib, dtype, bad):
+    """A cached value that is not finite, at a token of the chunk that
+    earlier rows of the same 32-key step do not see: every row that does
+    not see that token matches the oracle (the value never meets its zero
+    probability), and every row that sees it carries, in that dimension, a
+    result that is infinite, NaN or at least a millionth of the largest
+    finite value (the kernel's stand-in for it in steps that mask keys)."""
+    # prefixes of 5 and 40 tokens, chunks of 27 and 50: the planted tokens
+    # sit inside 32-key steps that also hold earlier rows
+    w = wl.custom_prefill([5, 40], [27, 50], 8, 2, 128, dtype)
+    b = wl.make_batch(w, 19, DEV)
+    run_pool_updates(b)
+    kc0, vc0 = clone_pools(b)   # the written pools: the step only reads them now
+    planted = []                # (sequence, token position, kv head, dim)
+    for s, t, g, d in ((0, 17, 1, 5), (1, 58, 0, 100)):
+        blk = int(b["block_tables"][s, t // 16])
+        vc0[blk, g, t % 16, d] = bad
+        planted.append((s, t, g, d))
+    b["value_cache"] = vc0.clone()
+    out = run_prefill(b)
+    nb = dict(b)
+    nb.pop("slot_mapping")     # the oracle reads the pools as they are now
+    qsl, lens = b["query_start_loc"], b["context_lens"]
+    group = 8 // 2
+    for s, t, g, d in planted:
+        rows, ref = oracle_prefill_subset(nb, kc0, vc0, [s])
+        n = int(qsl[s + 1] - qsl[s])
+        pos = int(lens[s]) - n + np.arange(n)          # position of each chunk row
+        blind = np.flatnonzero(pos < t)
+        sees = np.flatnonzero(pos >= t)
+        assert len(blind) and len(sees)
+        got = out[torch.from_numpy(rows).to(DEV)]
+        assert_close(got[torch.from_numpy(blind).to(DEV)], ref[blind], dtype,
+                     f"rows not seeing the {bad} at token {t}")
+        heads = range(g * group, (g + 1) * group)
+        seen = got[torch.from_numpy(sees).to(DEV)][:, list(heads), d].float()
+        big = 6.0e4 if dtype == "f16" else 3.0e38
+        assert bool(((~torch.isfinite(seen)) | (seen.abs() >= big / 1e6)).all())
