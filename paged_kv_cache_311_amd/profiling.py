@@ -46,9 +46,9 @@ def short_name(name):
 def kernel_durations(trace_dir):
     """{(kernel, grid): [duration_us, ...]} for this library's kernels."""
     out = collections.defaultdict(list)
-    for r in _csv(trace_dir, "kernel_trace.csv"):
-        if "pkv::" not in r["Kernel_Name"]:
-            continue
+    rows = [r for r in _csv(trace_dir, "kernel_trace.csv") if "pkv::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))  # in launch order
+    for r in rows:
         grid = r.get("Grid_Size_X") or r.get("Grid_Size")
         key = (short_name(r["Kernel_Name"]), int(grid))
         out[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
@@ -74,11 +74,12 @@ def source_sha256(path=KERNEL_SOURCE):
 def cmd_trace(args):
     d = kernel_durations(args.trace_dir)
     lines = [f"# Kernel trace: {args.title}", "", "Command:", "", "```", args.cmd, "```", "",
-             "| kernel | grid (threads) | calls | avg us | min us | max us |",
-             "|---|---|---|---|---|---|"]
+             f"| kernel | grid (threads) | calls | avg us | avg us, last {args.last} calls | "
+             "min us | max us |",
+             "|---|---|---|---|---|---|---|"]
     for (k, g), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{k}` | {g} | {len(v)} | {statistics.mean(v):.1f} | "
-                     f"{min(v):.1f} | {max(v):.1f} |")
+                     f"{statistics.mean(v[-args.last:]):.1f} | {min(v):.1f} | {max(v):.1f} |")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -142,6 +143,8 @@ def main():
     t.add_argument("out")
     t.add_argument("cmd")
     t.add_argument("--title", default="bench.py")
+    t.add_argument("--last", type=int, default=20,
+                   help="also average the last N calls of each kernel (launch order)")
     t.set_defaults(fn=cmd_trace)
     c = sub.add_parser("traffic")
     c.add_argument("out_json")
