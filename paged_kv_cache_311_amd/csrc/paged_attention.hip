@@ -102,9 +102,9 @@ constexpr int kMergeRounds = 8;                 // merge grid: at most this x th
 // with one head per group the matrix-core path is 4% slower).
 constexpr int kPvMfmaMinGc = 4;
 constexpr int kPvMfmaMinGcFp8 = 4;              // ... with E4M3 pools
-// Matrix-core path: a head's running max is raised only when a tile's max
-// exceeds it by more than this (log2 units), so the accumulator is rescaled
-// rarely; probabilities then stay below 2^kPvSlack.
+// A head's running max is raised only when a tile's max exceeds it by more
+// than this (log2 units), so the accumulator is rescaled rarely;
+// probabilities then stay below 2^kPvSlack.
 constexpr float kPvSlack = 8.f;
 // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -118,8 +118,9 @@ constexpr int kLdsSeqs = 2048;
 constexpr int kSortSeqs = 512;
 
 // DT: query / output element; KT: pool element (DT itself, or E4M3 codes
-// with 16-bit queries).
-template <int DT, int KT, int D, int GC>
+// with 16-bit queries); AP: the call also appends each sequence's newest
+// token (its rows come in beside the pools).
+template <int DT, int KT, int D, int GC, bool AP = true>
 struct DecodeCfg {
   static constexpr bool kFp8 = KT == PKV_FP8_E4M3;
   static_assert(KT == DT || (kFp8 && (DT == PKV_F16 || DT == PKV_BF16)), "pool format");
@@ -168,7 +169,7 @@ struct DecodeCfg {
   // slower with bfloat16 pools).
   static constexpr bool kOverlapNext = kFp8;
   // Appending: new-token rows a wave holds in LDS before writing them
-  static constexpr int kNewRecs = kPvMfma ? 4 : 8;
+  static constexpr int kNewRecs = !AP ? 0 : kPvMfma ? 4 : 8;
   // E4M3 appending: new-row elements each lane encodes, and their bytes
   static constexpr int kEncPerLane = D / kWave;
   static constexpr int kEncBytes = kEncPerLane * kEszQ;
@@ -187,7 +188,8 @@ struct DecodeCfg {
   static constexpr int kPartFloats = GC * D + 2 * GC;
   static constexpr int kPartStride = (kPartFloats + 3) / 4 * 4;
   static constexpr int kLdsFixed =
-      kLdsSeqs * 8 + kSortSeqs * 4 + kWavesPerWG * ((kFp8 ? 2 * D : 16) + kNewRecs * 2 * kRowB) +
+      kLdsSeqs * 8 + kSortSeqs * 4 +
+      kWavesPerWG * ((kFp8 && AP ? 2 * D : 16) + (kNewRecs > 0 ? kNewRecs * 2 * kRowB : 16)) +
       kWavesPerWG * (kPvMfma ? kBlockSize * kVS + 4 : kBlockSize * GC * 4 + 16) + 64;
   static constexpr int kLdsPerWg = 160 * 1024 / kGridWaves - 1024;
   static constexpr int kStageFit = (kLdsPerWg - kLdsFixed) / kWavesPerWG / (kPartStride * 4);
@@ -977,10 +979,10 @@ __device__ Window prepare_window(const DecodeParams& p, const RangeMap& m, const
   return wd;
 }
 
-template <int DT, int KT, int D, int GC>
-__global__ __launch_bounds__(kThreads, (DecodeCfg<DT, KT, D, GC>::kMinWaves)) void
+template <int DT, int KT, int D, int GC, bool AP>
+__global__ __launch_bounds__(kThreads, (DecodeCfg<DT, KT, D, GC, AP>::kMinWaves)) void
 paged_decode_kernel(const DecodeParams p) {
-  using C = DecodeCfg<DT, KT, D, GC>;
+  using C = DecodeCfg<DT, KT, D, GC, AP>;
   constexpr int NLD = C::kNld;
   constexpr int EPC = C::kEpc;
 
@@ -993,9 +995,10 @@ paged_decode_kernel(const DecodeParams p) {
   __shared__ int sm_len[kLdsSeqs];
   __shared__ int sm_order[kSortSeqs];
   // E4M3 appending: each wave's encoded new key and value rows
-  __shared__ __attribute__((aligned(16))) uint8_t sm_new[kWavesPerWG][C::kFp8 ? 2 * D : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sm_new[kWavesPerWG][C::kFp8 && AP ? 2 * D : 16];
   // appending: each wave's new-token rows waiting to be written
-  __shared__ __attribute__((aligned(16))) char sm_newrec[kWavesPerWG][C::kNewRecs * 2 * C::kRowB];
+  __shared__ __attribute__((aligned(16)))
+  char sm_newrec[kWavesPerWG][C::kNewRecs > 0 ? C::kNewRecs * 2 * C::kRowB : 16];
   __shared__ int sm_wsum[kWavesPerWG];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -1053,7 +1056,7 @@ paged_decode_kernel(const DecodeParams p) {
   uint32_t new_kw = 0u, new_vw = 0u;
   auto load_q = [&](QRegs& q, int s, int hg) {
     if constexpr (C::kFp8) {
-      if (p.new_k != nullptr) {
+      if constexpr (AP) {
         const int64_t nrow = ((int64_t)s * p.num_kv_heads + kv_head_of(p, hg)) * C::kRowQ;
         new_kw = load_lane_bytes<C::kEncBytes>(p.new_k + nrow + lane * C::kEncBytes);
         new_vw = load_lane_bytes<C::kEncBytes>(p.new_v + nrow + lane * C::kEncBytes);
@@ -1086,7 +1089,7 @@ paged_decode_kernel(const DecodeParams p) {
     const int64_t off = (int64_t)id * block_stride + (int64_t)g * C::kTileB;
     const char* kb = p.kcache + off;
     const char* vb = p.vcache + off;
-    if (!C::kFp8 && p.new_k != nullptr && (info_t & kSegEnd)) {
+    if (!C::kFp8 && AP && (info_t & kSegEnd)) {
       // the sequence's last block: the lanes of its newest token (row
       // valid - 1) read that token's rows from the new keys and values
       const int nt = ((info_t >> 16) & 31) - 1;
@@ -1312,7 +1315,7 @@ paged_decode_kernel(const DecodeParams p) {
 
     // 3. compute the current tile
     if constexpr (C::kFp8) {
-      if (p.new_k != nullptr && (info & kSegEnd)) substitute_new_token(tc, valid - 1);
+      if (AP && (info & kSegEnd)) substitute_new_token(tc, valid - 1);
     }
     if (info & kPieceFirst) {
       if constexpr (C::kPvMfma) {
@@ -1338,7 +1341,7 @@ paged_decode_kernel(const DecodeParams p) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = 4 * jg + i < valid ? rr[i] * p.scale_log2 : -INFINITY;
-      if (p.new_k != nullptr && (info & kSegEnd))
+      if (AP && (info & kSegEnd))
         store_new_token(tc, __builtin_amdgcn_readlane(cw.id, ci), hg, info);
       // the value tile into the wave's LDS rows as 16-bit elements (E4M3
       // codes widened exactly), rows past the context zeroed
@@ -1397,13 +1400,17 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < GC; ++g) sc[g] = -INFINITY;
       }
-      if (p.new_k != nullptr && (info & kSegEnd))
+      if (AP && (info & kSegEnd))
         store_new_token(tc, __builtin_amdgcn_readlane(cw.id, ci), hg, info);
+      // The running max is raised (to the tile's max, and the state
+      // rescaled) only when a logit exceeds it by more than kPvSlack, so
+      // most tiles need no reduction over the lanes; probabilities then
+      // stay below 2^kPvSlack.
       float pr[GC];
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
-        const float tmax = uniform(row_max16(sc[g]));
-        if (tmax > m_run[g]) {
+        if (__builtin_amdgcn_ballot_w64(sc[g] > m_run[g] + kPvSlack)) {
+          const float tmax = uniform(row_max16(sc[g]));
           const float alpha = __builtin_amdgcn_exp2f(m_run[g] - tmax);
           l_run[g] *= alpha;
 #pragma unroll
@@ -1417,6 +1424,14 @@ paged_decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < GC; ++g) pw[lane * GC + g] = pr[g];
       }
+      // value rows past the context zeroed (only a sequence's last block
+      // has them)
+      if (valid < kBlockSize) {
+#pragma unroll
+        for (int ld = 0; ld < NLD; ++ld) {
+          if (ld * C::kTpl + lane / C::kNch >= valid) tc.v[ld] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
@@ -1424,10 +1439,8 @@ paged_decode_kernel(const DecodeParams p) {
         float pv[GC];
 #pragma unroll
         for (int g = 0; g < GC; ++g) pv[g] = pw[tok * GC + g];
-        u32x4 vv = tc.v[ld];
-        if (valid < kBlockSize && tok >= valid) vv = u32x4{0u, 0u, 0u, 0u};
         float fv[EPC];
-        widen_chunk<KT>(vv, fv);
+        widen_chunk<KT>(tc.v[ld], fv);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
 #pragma unroll
@@ -1575,7 +1588,7 @@ paged_decode_kernel(const DecodeParams p) {
     if (done) break;
   }
   if constexpr (C::kStageRecs > 0) flush_stage();
-  if (p.new_k != nullptr) write_new_tokens();
+  if constexpr (AP) write_new_tokens();
 }
 
 // ----------------------------------------------------------- merge kernel --
@@ -1692,7 +1705,10 @@ static int resident_workgroups(const void* kernel, int waves_per_simd) {
 template <int DT, int KT, int D, int GC>
 static hipError_t launch_decode(DecodeParams a, hipStream_t st) {
   if (!FoldState<D, GC>::kSliced) a.desc_first = nullptr;  // no merges in slices
-  const void* k = reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC>);
+  // the appending kernel where the call carries new rows
+  const bool ap = a.new_k != nullptr;
+  const void* k = ap ? reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC, true>)
+                     : reinterpret_cast<const void*>(&paged_decode_kernel<DT, KT, D, GC, false>);
   const int nwg = resident_workgroups(k, DecodeCfg<DT, KT, D, GC>::kGridWaves);
   if (nwg <= 0) return hipErrorInvalidDevice;
   // The merge kernel takes a range per wave per round.  Without a cap there
@@ -1707,8 +1723,12 @@ static hipError_t launch_decode(DecodeParams a, hipStream_t st) {
   }
   int64_t mwg = (ranges + kWavesPerWG - 1) / kWavesPerWG;
   mwg = mwg < (int64_t)nwg * kMergeRounds ? mwg : (int64_t)nwg * kMergeRounds;
-  hipLaunchKernelGGL((paged_decode_kernel<DT, KT, D, GC>), dim3(nwg), dim3(kThreads), 0, st,
-                     a);
+  if (ap)
+    hipLaunchKernelGGL((paged_decode_kernel<DT, KT, D, GC, true>), dim3(nwg), dim3(kThreads), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((paged_decode_kernel<DT, KT, D, GC, false>), dim3(nwg), dim3(kThreads), 0,
+                       st, a);
   hipLaunchKernelGGL((paged_decode_merge_kernel<DT, D, GC>), dim3((unsigned)mwg),
                      dim3(kThreads), 0, st, a);
   return hipGetLastError();

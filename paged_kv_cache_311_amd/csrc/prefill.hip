@@ -191,47 +191,55 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   }
 
   // cooperative tile loads: chunk c = tid + 256u is 16 B of token c / CPR
-  // of the step (a row's chunks on consecutive lanes).  The block ids a
-  // step needs are read from the table one step before its tiles are
-  // loaded, so the two reads never follow one another.
-  const int64_t blk_bytes = (int64_t)p.num_kv_heads * kBlockSize * D * 2;
-  const int64_t head_bytes = (int64_t)g * kBlockSize * D * 2;
+  // of the step (a row's chunks on consecutive lanes).  All 64 chunks of a
+  // wave's load u lie in one pool block (16 tokens of D * 2 bytes make 16
+  // KiB and more per block, 1 KiB per wave load), so the block id and the
+  // tile's base address are wave-uniform (scalar registers) and each lane
+  // adds only its fixed offset inside the tile.  The block ids a step needs
+  // are read from the table one step before its tiles are loaded, so the
+  // two reads never follow one another.
+  constexpr int kTileBytes = kBlockSize * D * 2;
+  const int64_t blk_bytes = (int64_t)p.num_kv_heads * kTileBytes;
+  const int64_t head_bytes = (int64_t)g * kTileBytes;
   const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
   struct Stage {
     u32x4 k[NCH], v[NCH];
   };
-  // per chunk: its token within a step and the byte offset, inside a
-  // block, of this kv head's row chunk (both fixed for the thread)
-  int tk_u[NCH];
-  uint32_t in_blk[NCH];
+  // per chunk: its token within a step, and its byte offset inside the
+  // kv head's tile (both fixed for the thread); the step's block holding
+  // load u of this wave (0 or 1, uniform)
+  int tk_u[NCH], half_u[NCH];
+  uint32_t in_tile[NCH];
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const int c = tid + u * kThreads;
     tk_u[u] = c / CPR;
-    in_blk[u] = (uint32_t)(head_bytes + (tk_u[u] % kBlockSize) * D * 2 + (c - tk_u[u] * CPR) * 16);
+    in_tile[u] = (uint32_t)((tk_u[u] % kBlockSize) * D * 2 + (c - tk_u[u] * CPR) * 16);
+    half_u[u] = ((w * kWave + u * kThreads) / CPR) / kBlockSize;
   }
-  // Tokens past the context are read from the sequence's first block
-  // instead (same row, a slot of the context, so the load is in bounds and
-  // uniform) and stored to LDS as zeros.
+  // Blocks past the context read the sequence's first block instead (a
+  // table entry of the context, so the load is in bounds); their tokens,
+  // and those past the context in its last block, are stored to LDS as
+  // zeros.
+  const int nblk = (Lc + kBlockSize - 1) / kBlockSize;
   int32_t ids[NCH], ids_next[NCH];
   auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int t = step * kKeys + tk_u[u];
-      dst[u] = table[t < Lc ? t / kBlockSize : 0];  // always a table entry of the context
+      const int bi = step * (kKeys / kBlockSize) + half_u[u];
+      dst[u] = __builtin_amdgcn_readfirstlane(table[bi < nblk ? bi : 0]);
     }
   };
   // Loads are issued for every step, also past the last one, so the
   // compiler's count of loads in flight is the same on every path.
   const int max_blk = (int)(p.num_blocks - 1);
-  const uint32_t blk_bytes32 = (uint32_t)blk_bytes;  // below 2^32 (checked at launch)
   auto gload = [&](Stage& st, const int32_t (&id)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const uint32_t b = (uint32_t)min(max(id[u], 0), max_blk);  // clamped into the pool
-      const uint64_t off = (uint64_t)b * blk_bytes32 + in_blk[u];
-      st.k[u] = load16(p.kcache + off);
-      st.v[u] = load16(p.vcache + off);
+      const int64_t b = min(max(id[u], 0), max_blk);  // clamped into the pool
+      const int64_t off = b * blk_bytes + head_bytes;
+      st.k[u] = load16_buffer<kCacheDefault>(buffer_rsrc(p.kcache + off, kTileBytes), in_tile[u]);
+      st.v[u] = load16_buffer<kCacheDefault>(buffer_rsrc(p.vcache + off, kTileBytes), in_tile[u]);
     }
   };
   // Stored to LDS as rows.  A masked probability is an exact zero, but the
