@@ -14,7 +14,10 @@
  *                           in which every sequence appends one token; and
  *   paged_attention_prefill causal attention of a chunk of new tokens per
  *                           sequence (a whole prompt, or the next part of
- *                           one) over the cached tokens, on the same pools.
+ *                           one) over the cached tokens, on the same pools;
+ *   paged_attention_decode_shared_prefix  decode for batches whose
+ *                           sequences share leading blocks (samples, beams
+ *                           of one prompt), each shared block read once.
  *
  * Sources (titles of the pages this library follows):
  *   [TEQ]  "Your GPU was mostly empty: how PagedAttention turned KV-cache
@@ -80,7 +83,7 @@ enum pkv_status {
 };
 
 /* ABI version of this header (bumped on any signature change). */
-int pkv_abi_version(void);  /* 8 */
+int pkv_abi_version(void);  /* 9 */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int status);
@@ -400,7 +403,9 @@ int paged_attention_decode_append_fp8(void* out, const void* query, void* key_ca
  * are made finite before the second product (an infinity or NaN becomes
  * the largest finite value of its sign, NaN: +): rows that do not see such
  * a key are exact, rows that do see a non-finite value there get that
- * largest value in its place rather than an infinity or NaN.  Errors: INVALID_ARG for null pointers, sizes
+ * largest value in its place rather than an infinity or NaN.
+ *
+ * Errors: INVALID_ARG for null pointers, sizes
  * out of range, Hq % Hkv != 0 or misalignment; UNSUPPORTED for other
  * dtypes, block_size != 16 or head_size not 64/128.  Device-side contents
  * (tables, lengths, query_start_loc) are not validated; every read stays
@@ -414,6 +419,68 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
                             int head_size, int block_size, int max_blocks_per_seq,
                             int64_t num_blocks, int max_query_len, int dtype,
                             void* stream);
+
+/*
+ * paged_attention_decode_shared_prefix -- paged_attention_decode for a
+ * batch whose sequences share leading blocks, reading each shared block
+ * once for all the sequences that map it.
+ *
+ * Sequences forked from one prompt (parallel samples, beams) map the
+ * prompt's blocks to the same physical blocks, each block counting its
+ * sharers, until one of them writes into a block and gets a private copy
+ * ([TEQ] "Paging's second gift: copy-on-write"; [AITJ] "A request
+ * lifecycle: allocation, growth, sharing and release").  The caller, which
+ * keeps those reference counts, names the groups:
+ *
+ *   group_start    int32 [num_groups + 1], device: group j is sequences
+ *                  group_start[j] .. group_start[j+1] - 1; increasing from
+ *                  0 to num_seqs (so every sequence is in one group; a
+ *                  sequence that shares nothing is a group of its own)
+ *   prefix_blocks  int32 [num_groups], device: every member of group j
+ *                  holds the same block ids in its first prefix_blocks[j]
+ *                  table entries.  The library uses at most the full
+ *                  blocks of the group's shortest member (so a shared
+ *                  block holds 16 cached tokens of every member)
+ *   num_groups     0 .. num_seqs; 0: nothing is shared (both pointers may
+ *                  be NULL)
+ *
+ * The other arguments are as for paged_attention_decode; the result is
+ * the same attention, merged exactly in float32 from pieces of at most 256
+ * tokens.  Each (shared block, kv head) is read once for the query rows
+ * of every member of its group (up to 16 rows per read, member-major);
+ * each sequence's blocks after its group's shared ones are read for it
+ * alone.  A first kernel leaves a float32 state (max, sum, unnormalized
+ * output) per (sequence, head, piece) in the workspace, a second merges
+ * each row's pieces into `out`.
+ *
+ *   dtype        PKV_F16 or PKV_BF16 (pools in `dtype`)
+ *   num_seqs     at most 2048
+ *   workspace    at least paged_attention_shared_prefix_workspace_bytes()
+ *                bytes, 16-byte aligned, caller-owned, contents need no
+ *                initialization; calls that use one workspace must not
+ *                overlap
+ *
+ * Errors: INVALID_ARG for null pointers (group pointers only when
+ * num_groups > 0), sizes out of range, Hq % Hkv != 0 or misalignment;
+ * UNSUPPORTED for other dtypes, block_size != 16, head_size not 64/128,
+ * more than 2048 sequences or more groups than sequences; WORKSPACE when
+ * the workspace is missing or too small.  Device-side contents are not
+ * validated: group starts are clamped into [0, num_seqs], shared counts
+ * into [0, max_blocks_per_seq] and block ids into the pool, so a wrong
+ * description gives wrong numbers, never an access outside the buffers.
+ */
+int paged_attention_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
+    const int32_t* prefix_blocks, int num_groups, float scale, int num_kv_heads, int num_seqs,
+    int num_heads, int head_size, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+    void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/* Workspace bytes paged_attention_decode_shared_prefix needs for these
+ * sizes (0 when they are out of range: num_seqs outside 1..2048 or a size
+ * <= 0).  No device access. */
+size_t paged_attention_shared_prefix_workspace_bytes(int num_seqs, int num_heads,
+                                                     int head_size, int max_blocks_per_seq);
 
 #ifdef __cplusplus
 }

@@ -5,8 +5,10 @@ copy_blocks -- the fp8 variants of the first two (pools of E4M3 codes with
 one scale per pool: paged_attention_decode_fp8, reshape_and_cache_fp8),
 paged_attention_decode_append and paged_attention_decode_append_fp8 (a
 decode step that also caches each sequence's newest token), the
-allocation-free paged_attention_decode_noalloc, and paged_attention_prefill (causal attention of
-a chunk of new tokens) run entirely in the HIP kernels of libpagedkv.so
+allocation-free paged_attention_decode_noalloc,
+paged_attention_decode_shared_prefix (decode that reads blocks shared by a
+group of sequences once for the group), and paged_attention_prefill (causal
+attention of a chunk of new tokens) run entirely in the HIP kernels of libpagedkv.so
 (declared in include/pagedkv.h).  This module only marshals torch tensors (device
 memory and the current stream) into the C calls and raises on a nonzero
 status.  There is no fallback: if the library is missing or was not built,
@@ -92,6 +94,12 @@ def _declare(lib):
     lib.pkv_vpool_mapped_bytes.argtypes = [vp]
     lib.pkv_vpool_destroy.restype = None
     lib.pkv_vpool_destroy.argtypes = [vp]
+    lib.paged_attention_decode_shared_prefix.restype = c_int
+    lib.paged_attention_decode_shared_prefix.argtypes = [
+        vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
+        c_i64, vp, c_sz, c_int, vp]
+    lib.paged_attention_shared_prefix_workspace_bytes.restype = c_sz
+    lib.paged_attention_shared_prefix_workspace_bytes.argtypes = [c_int] * 4
     lib.paged_attention_prefill.restype = c_int
     lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_f, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_i64, c_int, c_int, vp]
@@ -261,6 +269,93 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables,
     return _decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                    num_kv_heads, partition_size, workspace, validate, False, 1.0, 1.0,
                    block_shared=block_shared)
+
+
+def shared_prefix_workspace_bytes(num_seqs, num_heads, head_size, max_blocks_per_seq):
+    """Workspace bytes paged_attention_decode_shared_prefix needs (0: sizes
+    out of range)."""
+    return int(load_library().paged_attention_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, head_size, max_blocks_per_seq))
+
+
+def shared_prefix_groups(block_tables, context_lens):
+    """The group description paged_attention_decode_shared_prefix takes,
+    from host copies of the tables: (group_start int32 [G + 1],
+    prefix_blocks int32 [G]).
+
+    Runs of consecutive sequences whose tables begin with the same block
+    form a group, sharing their longest common run of leading block ids
+    that are full blocks of every member; every other sequence is a group
+    of its own with no shared blocks.  Sequences forked from one prompt
+    (samples, beams) must therefore sit side by side to be found."""
+    bt = np.asarray(block_tables)
+    lens = np.asarray(context_lens).astype(np.int64)
+    S = len(lens)
+    starts, shared = [0], []
+    s = 0
+    while s < S:
+        e = s + 1
+        if lens[s] >= BLOCK_SIZE:
+            while e < S and lens[e] >= BLOCK_SIZE and bt[e, 0] == bt[s, 0]:
+                e += 1
+        pb = 0
+        if e - s >= 2:
+            full = int(lens[s:e].min()) // BLOCK_SIZE
+            same = (bt[s:e, :full] == bt[s, :full]).all(axis=0)
+            pb = full if bool(same.all()) else int(np.argmin(same))
+        shared.append(pb)
+        starts.append(e)
+        s = e
+    return np.asarray(starts, np.int32), np.asarray(shared, np.int32)
+
+
+def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, block_tables,
+                                         context_lens, group_start, prefix_blocks, scale,
+                                         num_kv_heads, workspace=None, validate=False):
+    """paged_attention_decode for a batch whose sequences share leading
+    blocks (samples or beams of one prompt): group j is sequences
+    group_start[j] .. group_start[j + 1] - 1, whose tables hold the same
+    first prefix_blocks[j] block ids (int32 device tensors, see
+    shared_prefix_groups).  Each shared block is read once for the whole
+    group.  16-bit pools only; at most 2048 sequences."""
+    import torch
+    lib = load_library()
+    _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens,
+                         group_start, prefix_blocks)
+    for t in (out, key_cache, value_cache):
+        _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
+    for t in (block_tables, context_lens, group_start, prefix_blocks):
+        _need(t.dtype == torch.int32, "tables, lengths and the group description are int32")
+    S, Hq, D = query.shape
+    NB, Hkv, bs, D2 = key_cache.shape
+    _need(tuple(out.shape) == (S, Hq, D), "out must match query")
+    _need(tuple(value_cache.shape) == tuple(key_cache.shape), "pools must match")
+    _need(D2 == D and Hkv == num_kv_heads, "pool shape does not match query")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables [S, W]")
+    _need(tuple(context_lens.shape) == (S,), "context_lens [S]")
+    G = prefix_blocks.numel()
+    _need(tuple(group_start.shape) == (G + 1,), "group_start [G + 1], prefix_blocks [G]")
+    W = block_tables.shape[1]
+    if validate:
+        _validate_tables(block_tables, context_lens, NB)
+        gs, pb = group_start.cpu().numpy(), prefix_blocks.cpu().numpy()
+        _need(G == 0 or (gs[0] == 0 and gs[-1] == S and (np.diff(gs) > 0).all()),
+              "group_start must run from 0 to num_seqs, increasing")
+        bt = block_tables.cpu().numpy()
+        for j in range(G):
+            rows = bt[gs[j]:gs[j + 1], :pb[j]]
+            _need((rows == rows[:1]).all(), f"group {j} does not share its first {pb[j]} blocks")
+    need = shared_prefix_workspace_bytes(S, Hq, D, W)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.paged_attention_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(group_start), _ptr(prefix_blocks), G, float(scale),
+        int(num_kv_heads), S, Hq, D, bs, W, NB, ws_ptr, ws_len, _dtype_code(query),
+        _stream_of(query)))
+    return out
 
 
 def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,

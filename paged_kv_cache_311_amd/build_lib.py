@@ -21,7 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(CSRC, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["paged_attention.hip", "cache_ops.hip", "prefill.hip", "vpool.hip"]
+SOURCES = ["paged_attention.hip", "cache_ops.hip", "prefill.hip", "vpool.hip",
+           "shared_prefix.hip"]
 HOST_LIB_PATH = os.path.join(HERE, "libpkvhost.so")
 HOST_SOURCES = ["block_manager.cpp"]
 CXX = os.environ.get("CXX", "g++")

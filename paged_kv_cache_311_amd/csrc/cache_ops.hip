@@ -241,7 +241,7 @@ extern "C" int reshape_and_cache_fp8(const void* key, const void* value,
 #define PKV_BUILD_ID "unstamped"
 #endif
 
-extern "C" int pkv_abi_version(void) { return 8; }
+extern "C" int pkv_abi_version(void) { return 9; }
 
 extern "C" const char* pkv_build_id(void) { return PKV_BUILD_ID; }
 

@@ -290,4 +290,35 @@ __device__ __forceinline__ floatx4 mfma32(const u32x4& a, const u32x4& b, const 
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Four probabilities as eight k slots of a 16-bit MFMA operand: each
+// rounded to the 16-bit type, then the remainder of that rounding (exact
+// in float32), also rounded.  With the values repeated in both halves the
+// product carries p to about 2^-16 of itself (float16: 2^-22), as a
+// float32 product would; one rounding alone would leave 2^-9 (bfloat16).
+template <int DT>
+__device__ __forceinline__ u32x4 split_probs(const float (&pe)[4]) {
+  float hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == PKV_F16) hi[i] = (float)(_Float16)pe[i];
+    else hi[i] = (float)(__bf16)pe[i];
+    lo[i] = pe[i] - hi[i];
+  }
+  return u32x4{pack2<DT>(pe[0], pe[1]), pack2<DT>(pe[2], pe[3]), pack2<DT>(lo[0], lo[1]),
+               pack2<DT>(lo[2], lo[3])};
+}
+
+// Four floats stored as the output type (8 bytes for 16-bit types).
+template <int DT>
+__device__ __forceinline__ void store4(char* dst, const floatx4& v) {
+  if constexpr (DT == PKV_F32) {
+    store16(dst, u32x4{bits_of(v[0]), bits_of(v[1]), bits_of(v[2]), bits_of(v[3])});
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{float_to_bits<DT>(v[0]) | (float_to_bits<DT>(v[1]) << 16),
+              float_to_bits<DT>(v[2]) | (float_to_bits<DT>(v[3]) << 16)};
+  }
+}
+
 }  // namespace pkv

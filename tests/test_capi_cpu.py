@@ -68,7 +68,7 @@ def test_host_library_exports_every_declared_symbol():
 
 
 def test_status_strings(lib):
-    assert lib.pkv_abi_version() == 8
+    assert lib.pkv_abi_version() == 9
     assert lib.pkv_status_string(OK) == b"ok"
     for st in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.pkv_status_string(st) not in (b"ok", b"unknown status")
@@ -342,3 +342,57 @@ def test_vpool_argument_validation(lib):
     assert lib.pkv_vpool_covers(None, 0, 1) == 0
     assert lib.pkv_vpool_keys(None) is None and lib.pkv_vpool_mapped_bytes(None) == 0
     lib.pkv_vpool_destroy(None)                                      # a no-op
+
+
+def shared_prefix(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, gs=FAKE, pb=FAKE, G=1,
+             scale=0.1, hkv=4, S=2, Hq=8, D=128, bs=16, W=4, NB=64, ws=FAKE, wsb=1 << 30,
+             dtype=1)
+    a.update(kw)
+    return lib.paged_attention_decode_shared_prefix(
+        a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["gs"], a["pb"], a["G"],
+        a["scale"], a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ws"],
+        a["wsb"], a["dtype"], None)
+
+
+def test_shared_prefix_validation(lib):
+    """paged_attention_decode_shared_prefix rejects bad scalar arguments
+    before any device work; its workspace size follows the documented
+    layout (per sequence two ints, then per (sequence, head, piece) a
+    (max, sum) pair and a head_size accumulator, pieces = ceil(W / 16) + 1,
+    each part rounded up to 256 bytes)."""
+    up = lambda x: (x + 255) // 256 * 256
+    f = lib.paged_attention_shared_prefix_workspace_bytes
+    rows = 256 * 40 * (-(-68 // 16) + 1)
+    assert f(256, 40, 128, 68) == up(256 * 8) + up(rows * 8) + up(rows * 128 * 4)
+    assert f(0, 40, 128, 68) == 0 and f(2049, 40, 128, 68) == 0 and f(4, 8, 128, 0) == 0
+    assert shared_prefix(lib, out=None) == INVALID
+    assert shared_prefix(lib, gs=None) == INVALID            # groups named, no pointer
+    assert shared_prefix(lib, G=-1) == INVALID
+    assert shared_prefix(lib, Hq=6) == INVALID               # 6 query heads over 4 kv heads
+    assert shared_prefix(lib, out=FAKE + 8) == INVALID        # rows are 16-byte aligned
+    assert shared_prefix(lib, dtype=0) == UNSUPPORTED        # float32 pools
+    assert shared_prefix(lib, dtype=3) == UNSUPPORTED
+    assert shared_prefix(lib, bs=8) == UNSUPPORTED
+    assert shared_prefix(lib, D=96) == UNSUPPORTED
+    assert shared_prefix(lib, S=2049, G=1) == UNSUPPORTED     # more than 2048 sequences
+    assert shared_prefix(lib, S=2, G=3) == UNSUPPORTED        # more groups than sequences
+    assert shared_prefix(lib, ws=None) == WORKSPACE
+    assert shared_prefix(lib, wsb=f(2, 8, 128, 4) - 1) == WORKSPACE
+    assert shared_prefix(lib, S=0, G=0, ws=None) == OK         # nothing to do
+
+
+def test_shared_prefix_groups_from_tables():
+    """The host helper finds runs of sequences that begin with the same
+    block and the common full blocks of each run."""
+    import numpy as np
+    import paged_kv_cache_311_amd as pkv
+    bt = np.array([[5, 6, 7, 9], [5, 6, 7, 10], [5, 6, 8, 11],   # share 2 blocks
+                   [1, 2, 3, 4],                                  # alone
+                   [20, 21, -1, -1], [20, 21, 22, -1],            # share 1 full block
+                   [30, -1, -1, -1], [30, 31, -1, -1]],           # first one too short
+                  np.int32)
+    lens = np.array([64, 60, 50, 64, 20, 40, 10, 30], np.int32)
+    gs, pb = pkv.shared_prefix_groups(bt, lens)
+    assert gs.tolist() == [0, 3, 4, 6, 7, 8]
+    assert pb.tolist() == [2, 0, 1, 0, 0]
