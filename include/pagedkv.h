@@ -445,7 +445,7 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
  *                  be NULL)
  *
  * The other arguments are as for paged_attention_decode; the result is
- * the same attention, merged exactly in float32 from pieces of at most 256
+ * the same attention, merged exactly in float32 from pieces of at most 128
  * tokens.  Each (shared block, kv head) is read once for the query rows
  * of every member of its group (up to 16 rows per read, member-major);
  * each sequence's blocks after its group's shared ones are read for it

@@ -50,7 +50,7 @@ namespace shared_prefix {
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxSeqs = 2048;            // sequences (and groups) per call
-constexpr int kChunk = 16;                // tiles per work item
+constexpr int kChunk = 8;                 // tiles per work item
 constexpr int kRowsPerItem = 16;          // query rows per item (MFMA columns)
 constexpr int kWavesPerSimd = 2;
 constexpr float kSlack = 8.f;             // running max raised past this (log2 units)

@@ -359,11 +359,11 @@ def test_shared_prefix_validation(lib):
     """paged_attention_decode_shared_prefix rejects bad scalar arguments
     before any device work; its workspace size follows the documented
     layout (per sequence two ints, then per (sequence, head, piece) a
-    (max, sum) pair and a head_size accumulator, pieces = ceil(W / 16) + 1,
+    (max, sum) pair and a head_size accumulator, pieces = ceil(W / 8) + 1,
     each part rounded up to 256 bytes)."""
     up = lambda x: (x + 255) // 256 * 256
     f = lib.paged_attention_shared_prefix_workspace_bytes
-    rows = 256 * 40 * (-(-68 // 16) + 1)
+    rows = 256 * 40 * (-(-68 // 8) + 1)
     assert f(256, 40, 128, 68) == up(256 * 8) + up(rows * 8) + up(rows * 128 * 4)
     assert f(0, 40, 128, 68) == 0 and f(2049, 40, 128, 68) == 0 and f(4, 8, 128, 0) == 0
     assert shared_prefix(lib, out=None) == INVALID
