@@ -145,7 +145,7 @@ def decode_algorithmic_bytes(w, lens):
 class Step:
     """Device-resident batch and the calls of one step (no allocation inside)."""
 
-    def __init__(self, w, seed, ps, fuse=True):
+    def __init__(self, w, seed, ps, fuse=True, shared=False):
         import torch
         import paged_kv_cache_311_amd as pkv
         from paged_kv_cache_311_amd import workloads as wl
@@ -188,6 +188,20 @@ class Step:
         one_each = ("slot_mapping" not in b
                     or np.array_equal(b.get("token_seq", []), np.arange(w.num_seqs)))
         self.fused = bool(fuse and one_each and (lens >= 1).all())
+        # the shared-prefix call: groups of sequences that begin with the same
+        # blocks (samples, beams of one prompt), found from the tables; it
+        # does not append, so the step caches its tokens first
+        self.shared = shared
+        if shared:
+            self.fused = False
+            order, gs, pb = pkv.shared_prefix_groups(b["block_tables"], lens)
+            self.order = torch.from_numpy(order).to(dev)
+            self.group_start = torch.from_numpy(gs).to(dev)
+            self.prefix_blocks = torch.from_numpy(pb).to(dev)
+            self.shared_groups = int((pb > 0).sum())
+            self.sws = torch.zeros(max(pkv.shared_prefix_workspace_bytes(
+                w.num_seqs, w.num_heads, w.head_size, b["block_tables"].shape[1]), 1),
+                dtype=torch.uint8, device=dev)
 
     def updates(self):
         b, w = self.b, self.w
@@ -217,7 +231,12 @@ class Step:
 
     def decode(self):
         b, w = self.b, self.w
-        if self.fused and w.fp8:
+        if self.shared:
+            self.pkv.paged_attention_decode_shared_prefix(
+                self.out, b["query"], b["key_cache"], b["value_cache"], self.bt, self.cl,
+                self.order, self.group_start, self.prefix_blocks, float(w.scale),
+                w.num_kv_heads, workspace=self.sws)
+        elif self.fused and w.fp8:
             self.pkv.paged_attention_decode_append_fp8(
                 self.out, b["query"], b["key_cache"], b["value_cache"], self.bt, self.cl,
                 self.key, self.value, float(w.scale), w.k_scale, w.v_scale, w.num_kv_heads,
@@ -354,8 +373,8 @@ def measure_prefill(w, seed, steps, warmup):
     }
 
 
-def measure(w, seed, steps, warmup, ps, fuse=True):
-    st = Step(w, seed, ps, fuse)
+def measure(w, seed, steps, warmup, ps, fuse=True, shared=None):
+    st = Step(w, seed, ps, fuse, shared=bool(shared))
     step_ms, dec_ms, wall = st.run(steps, warmup)
     kvb = kv_bytes(w, st.lens)
     algo = decode_algorithmic_bytes(w, st.lens)
@@ -392,7 +411,43 @@ def measure(w, seed, steps, warmup, ps, fuse=True):
         r["kv_shared_fraction"] = 1.0 - uniq / kvb
         r["kv_unique_GBps"] = uniq / (step_ms * 1e-3) / 1e9
         r["decode_unique_GBps"] = (algo - kvb + uniq) / (dec_avg * 1e-3) / 1e9
+        if shared is None and not w.fp8:
+            r["shared_prefix"] = measure_shared(w, seed, steps, warmup, ps, st)
     return r, st
+
+
+def measure_shared(w, seed, steps, warmup, ps, plain):
+    """The same steps with paged_attention_decode_shared_prefix (blocks a
+    group of sequences shares read once for the group), beside the plain
+    call's numbers; outputs compared with the plain call's on the same
+    pools."""
+    torch = plain.torch
+    r, st = measure(w, seed, steps, warmup, ps, fuse=False, shared=True)
+    # same pools as `plain` after its steps: recompute both on st's pools
+    plain_out = torch.empty_like(st.out)
+    st.decode_into(plain_out, st.b["key_cache"], st.b["value_cache"], st.bt, st.flags)
+    st.decode()
+    torch.cuda.synchronize()
+    diff = (plain_out.float() - st.out.float()).abs().max().item()
+    uniq = kv_unique_bytes(w, st.b["block_tables"], st.lens)
+    out = {
+        "call": "paged_attention_decode_shared_prefix",
+        "groups_sharing": st.shared_groups,
+        "ms_per_step": r["ms_per_step"],
+        "decode_call_ms_avg": r["decode_call_ms_avg"],
+        "decode_tokens_per_s": r["decode_tokens_per_s"],
+        "decode_logical_GBps": r["decode_GBps"],
+        "decode_unique_GBps": (r["decode_algorithmic_bytes"] - r["kv_bytes_per_step"] + uniq)
+                              / (r["decode_call_ms_avg"] * 1e-3) / 1e9,
+        "decode_unique_pct_of_hbm_peak": 100.0 * (r["decode_algorithmic_bytes"]
+                                                  - r["kv_bytes_per_step"] + uniq)
+                                         / (r["decode_call_ms_avg"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBPS,
+        "max_abs_diff_vs_plain_call": diff,
+    }
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 def contiguous_layout(st):

@@ -432,9 +432,14 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
  * lifecycle: allocation, growth, sharing and release").  The caller, which
  * keeps those reference counts, names the groups:
  *
- *   group_start    int32 [num_groups + 1], device: group j is sequences
- *                  group_start[j] .. group_start[j+1] - 1; increasing from
- *                  0 to num_seqs (so every sequence is in one group; a
+ *   order          int32 [num_seqs], device, or NULL (the identity): a
+ *                  permutation of the sequences; groups are runs of
+ *                  consecutive positions in it, so the members of a group
+ *                  need not sit side by side in the batch
+ *   group_start    int32 [num_groups + 1], device: group j is the
+ *                  sequences at positions group_start[j] ..
+ *                  group_start[j+1] - 1 of `order`; increasing from 0 to
+ *                  num_seqs (so every sequence is in one group; a
  *                  sequence that shares nothing is a group of its own)
  *   prefix_blocks  int32 [num_groups], device: every member of group j
  *                  holds the same block ids in its first prefix_blocks[j]
@@ -465,16 +470,18 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
  * UNSUPPORTED for other dtypes, block_size != 16, head_size not 64/128,
  * more than 2048 sequences or more groups than sequences; WORKSPACE when
  * the workspace is missing or too small.  Device-side contents are not
- * validated: group starts are clamped into [0, num_seqs], shared counts
- * into [0, max_blocks_per_seq] and block ids into the pool, so a wrong
- * description gives wrong numbers, never an access outside the buffers.
+ * validated: order entries are clamped into [0, num_seqs), group starts
+ * into [0, num_seqs], shared counts into [0, max_blocks_per_seq] and block
+ * ids into the pool, so a wrong description (or an order that is not a
+ * permutation) gives wrong numbers, never an access outside the buffers.
  */
 int paged_attention_decode_shared_prefix(
     void* out, const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
-    const int32_t* prefix_blocks, int num_groups, float scale, int num_kv_heads, int num_seqs,
-    int num_heads, int head_size, int block_size, int max_blocks_per_seq, int64_t num_blocks,
-    void* workspace, size_t workspace_bytes, int dtype, void* stream);
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* order,
+    const int32_t* group_start, const int32_t* prefix_blocks, int num_groups, float scale,
+    int num_kv_heads, int num_seqs, int num_heads, int head_size, int block_size,
+    int max_blocks_per_seq, int64_t num_blocks, void* workspace, size_t workspace_bytes,
+    int dtype, void* stream);
 
 /* Workspace bytes paged_attention_decode_shared_prefix needs for these
  * sizes (0 when they are out of range: num_seqs outside 1..2048 or a size

@@ -96,8 +96,8 @@ def _declare(lib):
     lib.pkv_vpool_destroy.argtypes = [vp]
     lib.paged_attention_decode_shared_prefix.restype = c_int
     lib.paged_attention_decode_shared_prefix.argtypes = [
-        vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_f, c_int, c_int, c_int, c_int, c_int, c_int,
-        c_i64, vp, c_sz, c_int, vp]
+        vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int, c_f, c_int, c_int, c_int, c_int, c_int,
+        c_int, c_i64, vp, c_sz, c_int, vp]
     lib.paged_attention_shared_prefix_workspace_bytes.restype = c_sz
     lib.paged_attention_shared_prefix_workspace_bytes.argtypes = [c_int] * 4
     lib.paged_attention_prefill.restype = c_int
@@ -280,51 +280,61 @@ def shared_prefix_workspace_bytes(num_seqs, num_heads, head_size, max_blocks_per
 
 def shared_prefix_groups(block_tables, context_lens):
     """The group description paged_attention_decode_shared_prefix takes,
-    from host copies of the tables: (group_start int32 [G + 1],
-    prefix_blocks int32 [G]).
+    from host copies of the tables: (order int32 [S], group_start int32
+    [G + 1], prefix_blocks int32 [G]).
 
-    Runs of consecutive sequences whose tables begin with the same block
-    form a group, sharing their longest common run of leading block ids
-    that are full blocks of every member; every other sequence is a group
-    of its own with no shared blocks.  Sequences forked from one prompt
-    (samples, beams) must therefore sit side by side to be found."""
+    Sequences whose tables begin with the same block form a group (in
+    `order` they sit side by side, wherever they are in the batch), sharing
+    their longest common run of leading block ids that are full blocks of
+    every member; every other sequence is a group of its own with no shared
+    blocks."""
     bt = np.asarray(block_tables)
     lens = np.asarray(context_lens).astype(np.int64)
     S = len(lens)
+    if S == 0:
+        return np.zeros(0, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32)
+    first = np.where(lens >= BLOCK_SIZE, bt[:, 0].astype(np.int64), -1)
+    # sequences holding a full first block, by that block (stable), then the rest
+    key = np.where(first >= 0, first, np.iinfo(np.int64).max)
+    order = np.argsort(key, kind="stable").astype(np.int32)
     starts, shared = [0], []
-    s = 0
-    while s < S:
-        e = s + 1
-        if lens[s] >= BLOCK_SIZE:
-            while e < S and lens[e] >= BLOCK_SIZE and bt[e, 0] == bt[s, 0]:
+    i = 0
+    while i < S:
+        e = i + 1
+        if first[order[i]] >= 0:
+            while e < S and first[order[e]] == first[order[i]]:
                 e += 1
         pb = 0
-        if e - s >= 2:
-            full = int(lens[s:e].min()) // BLOCK_SIZE
-            same = (bt[s:e, :full] == bt[s, :full]).all(axis=0)
+        if e - i >= 2:
+            members = order[i:e]
+            full = int(lens[members].min()) // BLOCK_SIZE
+            rows = bt[members, :full]
+            same = (rows == rows[:1]).all(axis=0)
             pb = full if bool(same.all()) else int(np.argmin(same))
         shared.append(pb)
         starts.append(e)
-        s = e
-    return np.asarray(starts, np.int32), np.asarray(shared, np.int32)
+        i = e
+    return order, np.asarray(starts, np.int32), np.asarray(shared, np.int32)
 
 
 def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, block_tables,
-                                         context_lens, group_start, prefix_blocks, scale,
-                                         num_kv_heads, workspace=None, validate=False):
+                                         context_lens, order, group_start, prefix_blocks,
+                                         scale, num_kv_heads, workspace=None,
+                                         validate=False):
     """paged_attention_decode for a batch whose sequences share leading
-    blocks (samples or beams of one prompt): group j is sequences
-    group_start[j] .. group_start[j + 1] - 1, whose tables hold the same
-    first prefix_blocks[j] block ids (int32 device tensors, see
+    blocks (samples or beams of one prompt): group j is the sequences at
+    positions group_start[j] .. group_start[j + 1] - 1 of `order` (a
+    permutation; None: the batch order), whose tables hold the same first
+    prefix_blocks[j] block ids (int32 device tensors, see
     shared_prefix_groups).  Each shared block is read once for the whole
     group.  16-bit pools only; at most 2048 sequences."""
     import torch
     lib = load_library()
-    _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens,
-                         group_start, prefix_blocks)
+    idx = [group_start, prefix_blocks] + ([order] if order is not None else [])
+    _all_cuda_contiguous(out, query, key_cache, value_cache, block_tables, context_lens, *idx)
     for t in (out, key_cache, value_cache):
         _need(t.dtype == query.dtype, "query, out and pools must share a dtype")
-    for t in (block_tables, context_lens, group_start, prefix_blocks):
+    for t in [block_tables, context_lens] + idx:
         _need(t.dtype == torch.int32, "tables, lengths and the group description are int32")
     S, Hq, D = query.shape
     NB, Hkv, bs, D2 = key_cache.shape
@@ -335,15 +345,18 @@ def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, blo
     _need(tuple(context_lens.shape) == (S,), "context_lens [S]")
     G = prefix_blocks.numel()
     _need(tuple(group_start.shape) == (G + 1,), "group_start [G + 1], prefix_blocks [G]")
+    _need(order is None or tuple(order.shape) == (S,), "order [S]")
     W = block_tables.shape[1]
     if validate:
         _validate_tables(block_tables, context_lens, NB)
         gs, pb = group_start.cpu().numpy(), prefix_blocks.cpu().numpy()
+        perm = np.arange(S) if order is None else order.cpu().numpy()
+        _need(np.array_equal(np.sort(perm), np.arange(S)), "order must be a permutation")
         _need(G == 0 or (gs[0] == 0 and gs[-1] == S and (np.diff(gs) > 0).all()),
               "group_start must run from 0 to num_seqs, increasing")
         bt = block_tables.cpu().numpy()
         for j in range(G):
-            rows = bt[gs[j]:gs[j + 1], :pb[j]]
+            rows = bt[perm[gs[j]:gs[j + 1]], :pb[j]]
             _need((rows == rows[:1]).all(), f"group {j} does not share its first {pb[j]} blocks")
     need = shared_prefix_workspace_bytes(S, Hq, D, W)
     if workspace is None and need:
@@ -352,7 +365,8 @@ def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, blo
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.paged_attention_decode_shared_prefix(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), _ptr(group_start), _ptr(prefix_blocks), G, float(scale),
+        _ptr(context_lens), _ptr(order) if order is not None else ctypes.c_void_p(0),
+        _ptr(group_start), _ptr(prefix_blocks), G, float(scale),
         int(num_kv_heads), S, Hq, D, bs, W, NB, ws_ptr, ws_len, _dtype_code(query),
         _stream_of(query)))
     return out

@@ -62,6 +62,7 @@ struct Params {
   const char* vcache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* order;          // position -> sequence (NULL: the identity)
   const int32_t* group_start;
   const int32_t* prefix_blocks;
   int2* pieces;        // per sequence: (prefix pieces, suffix pieces)
@@ -80,9 +81,10 @@ struct Plan {
   int gs[kMaxSeqs + 1];   // group starts, clamped into [0, num_seqs]
   int pb[kMaxSeqs];       // shared blocks per group (clamped)
   int gincl[kMaxSeqs];    // prefix items, inclusive running sum over groups
-  int len[kMaxSeqs];      // context lengths, clamped
-  int grp[kMaxSeqs];      // group of each sequence, or -1
-  int sincl[kMaxSeqs];    // suffix items, inclusive running sum over sequences
+  int seq[kMaxSeqs];      // sequence at each position (the order, clamped)
+  int len[kMaxSeqs];      // context lengths by position, clamped
+  int grp[kMaxSeqs];      // group of each position, or -1
+  int sincl[kMaxSeqs];    // suffix items, inclusive running sum over positions
   int scan[kThreads];
 };
 
@@ -127,7 +129,10 @@ __device__ void build_plan(const Params& p, Plan& pl) {
   const int ns = p.num_seqs, ng = p.num_groups;
   const int max_tokens = p.max_blocks * kBlockSize;
   for (int s = tid; s < ns; s += kThreads) {
-    const int L = p.context_lens[s];
+    int q = p.order != nullptr ? p.order[s] : s;
+    q = q < 0 ? 0 : (q >= ns ? ns - 1 : q);
+    pl.seq[s] = q;
+    const int L = p.context_lens[q];
     pl.len[s] = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
   }
   for (int j = tid; j <= ng; j += kThreads) {
@@ -168,7 +173,7 @@ __device__ void build_plan(const Params& p, Plan& pl) {
     const int pb = j >= 0 ? pl.pb[j] : 0;
     const int suf = ceil_div(pl.len[s], kBlockSize) - pb;
     pl.sincl[s] = hkv * ceil_div(G, kRowsPerItem) * ceil_div(suf, kChunk);
-    if (blockIdx.x == 0) p.pieces[s] = int2{ceil_div(pb, kChunk), ceil_div(suf, kChunk)};
+    if (blockIdx.x == 0) p.pieces[pl.seq[s]] = int2{ceil_div(pb, kChunk), ceil_div(suf, kChunk)};
   }
   __syncthreads();
   if (ng > 0) block_scan(pl.gincl, ng, pl.scan);
@@ -201,22 +206,23 @@ __device__ __forceinline__ Item item_of(const Params& p, const Plan& pl, int x, 
     const int rem = local - it.g * rsets * chunks;
     const int rs = rem / chunks;
     const int c = rem - rs * chunks;
-    it.tseq = pl.gs[j];
+    it.tseq = pl.seq[pl.gs[j]];
     it.n0 = c * kChunk;
     it.n1 = min(it.n0 + kChunk, pl.pb[j]);
     it.last_valid = kBlockSize;
     it.piece = c;
     it.nrows = min(kRowsPerItem, rows - rs * kRowsPerItem);
     r = rs * kRowsPerItem + (col < it.nrows ? col : 0);
-    it.seq_r = pl.gs[j] + r / G;
+    it.seq_r = pl.seq[pl.gs[j] + r / G];
     it.head_r = it.g * G + r % G;
   } else {
     const int y = x - P;
-    const int s = search(pl.sincl, p.num_seqs, y);
-    const int local = y - (s > 0 ? pl.sincl[s - 1] : 0);
-    const int j = pl.grp[s];
+    const int pos = search(pl.sincl, p.num_seqs, y);
+    const int s = pl.seq[pos];
+    const int local = y - (pos > 0 ? pl.sincl[pos - 1] : 0);
+    const int j = pl.grp[pos];
     const int pb = j >= 0 ? pl.pb[j] : 0;
-    const int nb = ceil_div(pl.len[s], kBlockSize);
+    const int nb = ceil_div(pl.len[pos], kBlockSize);
     const int rsets = ceil_div(G, kRowsPerItem);
     const int chunks = ceil_div(nb - pb, kChunk);
     it.g = local / (rsets * chunks);
@@ -226,7 +232,7 @@ __device__ __forceinline__ Item item_of(const Params& p, const Plan& pl, int x, 
     it.tseq = s;
     it.n0 = pb + c * kChunk;
     it.n1 = min(it.n0 + kChunk, nb);
-    it.last_valid = it.n1 == nb ? pl.len[s] - (nb - 1) * kBlockSize : kBlockSize;
+    it.last_valid = it.n1 == nb ? pl.len[pos] - (nb - 1) * kBlockSize : kBlockSize;
     it.piece = ceil_div(pb, kChunk) + c;
     it.nrows = min(kRowsPerItem, G - rs * kRowsPerItem);
     r = rs * kRowsPerItem + (col < it.nrows ? col : 0);
@@ -494,10 +500,11 @@ extern "C" size_t paged_attention_shared_prefix_workspace_bytes(int num_seqs, in
 
 extern "C" int paged_attention_decode_shared_prefix(
     void* out, const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
-    const int32_t* prefix_blocks, int num_groups, float scale, int num_kv_heads, int num_seqs,
-    int num_heads, int head_size, int block_size, int max_blocks_per_seq, int64_t num_blocks,
-    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* order,
+    const int32_t* group_start, const int32_t* prefix_blocks, int num_groups, float scale,
+    int num_kv_heads, int num_seqs, int num_heads, int head_size, int block_size,
+    int max_blocks_per_seq, int64_t num_blocks, void* workspace, size_t workspace_bytes,
+    int dtype, void* stream) {
   using namespace pkv;
   using namespace pkv::shared_prefix;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
@@ -533,6 +540,7 @@ extern "C" int paged_attention_decode_shared_prefix(
   a.context_lens = context_lens;
   // no groups: every sequence is a suffix of its own (the pointers are
   // never read)
+  a.order = order;
   a.group_start = num_groups > 0 ? group_start : context_lens;
   a.prefix_blocks = num_groups > 0 ? prefix_blocks : context_lens;
   a.pieces = (int2*)((char*)workspace + l.pieces);

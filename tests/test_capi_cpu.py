@@ -345,12 +345,14 @@ def test_vpool_argument_validation(lib):
 
 
 def shared_prefix(lib, **kw):
-    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, gs=FAKE, pb=FAKE, G=1,
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, order=None, gs=FAKE,
+             pb=FAKE, G=1,
              scale=0.1, hkv=4, S=2, Hq=8, D=128, bs=16, W=4, NB=64, ws=FAKE, wsb=1 << 30,
              dtype=1)
     a.update(kw)
     return lib.paged_attention_decode_shared_prefix(
-        a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["gs"], a["pb"], a["G"],
+        a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["order"], a["gs"], a["pb"],
+        a["G"],
         a["scale"], a["hkv"], a["S"], a["Hq"], a["D"], a["bs"], a["W"], a["NB"], a["ws"],
         a["wsb"], a["dtype"], None)
 
@@ -383,8 +385,9 @@ def test_shared_prefix_validation(lib):
 
 
 def test_shared_prefix_groups_from_tables():
-    """The host helper finds runs of sequences that begin with the same
-    block and the common full blocks of each run."""
+    """The host helper groups the sequences that begin with the same full
+    block, wherever they sit in the batch (an order that puts them side by
+    side, stable), and finds the common full blocks of each group."""
     import numpy as np
     import paged_kv_cache_311_amd as pkv
     bt = np.array([[5, 6, 7, 9], [5, 6, 7, 10], [5, 6, 8, 11],   # share 2 blocks
@@ -393,6 +396,15 @@ def test_shared_prefix_groups_from_tables():
                    [30, -1, -1, -1], [30, 31, -1, -1]],           # first one too short
                   np.int32)
     lens = np.array([64, 60, 50, 64, 20, 40, 10, 30], np.int32)
-    gs, pb = pkv.shared_prefix_groups(bt, lens)
-    assert gs.tolist() == [0, 3, 4, 6, 7, 8]
-    assert pb.tolist() == [2, 0, 1, 0, 0]
+    order, gs, pb = pkv.shared_prefix_groups(bt, lens)
+    assert order.tolist() == [3, 0, 1, 2, 4, 5, 7, 6]  # by first block; too short last
+    assert gs.tolist() == [0, 1, 4, 6, 7, 8]
+    assert pb.tolist() == [0, 2, 1, 0, 0]
+    # the same batch shuffled: the same groups, found by their first blocks
+    perm = np.array([6, 2, 4, 0, 7, 3, 5, 1])
+    order2, gs2, pb2 = pkv.shared_prefix_groups(bt[perm], lens[perm])
+    assert gs2.tolist() == gs.tolist() and pb2.tolist() == pb.tolist()
+    assert [sorted(perm[order2[gs2[j]:gs2[j + 1]]].tolist()) for j in range(len(pb2))] == \
+        [[3], [0, 1, 2], [4, 5], [7], [6]]
+    empty = pkv.shared_prefix_groups(np.zeros((0, 4), np.int32), np.zeros(0, np.int32))
+    assert [x.tolist() for x in empty] == [[], [0], []]

@@ -24,17 +24,18 @@ W = wl.WORKLOADS
 
 
 def run_shared(b, groups=None, workspace=None):
-    """The shared-prefix call on batch b; groups = (group_start, prefix_blocks)
-    host arrays (default: found from the batch's tables)."""
+    """The shared-prefix call on batch b; groups = (order or None,
+    group_start, prefix_blocks) host arrays (default: found from the
+    batch's tables)."""
     w = b["workload"]
     if groups is None:
         groups = pkv.shared_prefix_groups(b["block_tables"], b["context_lens"])
-    gs, pb = groups
+    order, gs, pb = groups
     out = torch.full_like(b["query"], float("nan"))
     pkv.paged_attention_decode_shared_prefix(
         out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
-        dev_i32(b["context_lens"]), dev_i32(gs), dev_i32(pb), float(w.scale), w.num_kv_heads,
-        workspace=workspace)
+        dev_i32(b["context_lens"]), None if order is None else dev_i32(order), dev_i32(gs),
+        dev_i32(pb), float(w.scale), w.num_kv_heads, workspace=workspace)
     torch.cuda.synchronize()
     return out
 
@@ -60,27 +61,31 @@ def share(b, groups):
     for s in range(covered, S):
         starts.append(s + 1)
         shared.append(0)
-    return np.asarray(starts, np.int32), np.asarray(shared, np.int32)
+    return None, np.asarray(starts, np.int32), np.asarray(shared, np.int32)
 
 
-@pytest.mark.parametrize("key", ["sampling_cow", "beam"])
+@pytest.mark.parametrize("key", ["sampling_cow", "beam", "sampling_cow_shuffled",
+                                 "beam_shuffled"])
 def test_shared_prefix_sampling_and_beam(gpu_lib, key):
-    """The sampling and beam-search batches at their configured sizes, after
-    the step's copy-on-write and appends: sampled sequences against the
-    oracle, every sequence against the plain decode call."""
+    """The sampling and beam-search batches at their configured sizes (also
+    with their sequences in a random order, the groups then found through
+    the order), after the step's copy-on-write and appends: sampled
+    sequences against the oracle, every sequence against the plain decode
+    call."""
     w = W[key]
     b = wl.make_batch(w, w.default_seed, DEV)
     kc0, vc0 = clone_pools(b)
     run_pool_updates(b)
-    gs, pb = pkv.shared_prefix_groups(b["block_tables"], b["context_lens"])
+    order, gs, pb = pkv.shared_prefix_groups(b["block_tables"], b["context_lens"])
     shared_groups = int((pb > 0).sum())
     say(f"    {key}: {len(pb)} groups, {shared_groups} sharing "
         f"{int(pb.sum())} blocks (mean {pb[pb > 0].mean():.1f})")
     assert shared_groups == w.prompts  # every prompt's samples / beams found
-    out = run_shared(b, (gs, pb))
+    out = run_shared(b, (order, gs, pb))
     seqs = sample_seqs(b["context_lens"], k=6)
-    # a whole group too: its first and last members
-    seqs = sorted(set(seqs) | {int(gs[1]) - 1, int(gs[1]) - 2, 0})
+    # a whole group too
+    j = int(np.argmax(pb > 0))
+    seqs = sorted(set(seqs) | {int(x) for x in order[gs[j]:gs[j + 1]]})
     ref = oracle_decode_subset(b, kc0, vc0, seqs)
     assert_close(out[seqs], ref, w.dtype, f"{key} sampled seqs")
     plain = run_decode(b)
@@ -106,7 +111,7 @@ def test_shared_prefix_custom_groups(gpu_lib, case):
     """Hand-made groups: members with and without private blocks (a member
     whose whole context is the shared part), grouped-query heads with more
     than 16 rows per group or per kv head, 64- and 128-wide heads, long
-    contexts (several 256-token pieces per row), a member with no cached
+    contexts (several 128-token pieces per row), a member with no cached
     token (its group then shares nothing), and singletons; every output
     against the oracle."""
     lens, hq, hkv, d, dt, groups = CASES[case]
@@ -130,18 +135,21 @@ def test_shared_prefix_overstated_and_no_groups(gpu_lib):
     lens = [100, 45, 160, 160]
     w = wl.custom(lens, 8, 8, 128, "f16")
     b = wl.make_batch(w, 311600, DEV)
-    gs, pb = share(b, [(0, 4, 2)])  # members 0..3 share blocks 0, 1
+    _, gs, pb = share(b, [(0, 4, 2)])  # members 0..3 share blocks 0, 1
     kc0, vc0 = clone_pools(b)
     ref = oracle_decode_subset(b, kc0, vc0, list(range(4)))
     over = pb.copy()
     over[0] = 5  # member 1 holds 2 full blocks only
-    assert_close(run_shared(b, (gs, over)), ref, "f16", "overstated shared count")
+    assert_close(run_shared(b, (None, gs, over)), ref, "f16", "overstated shared count")
+    # the same group named through an order that lists it backwards
+    rev = np.array([3, 2, 1, 0], np.int32)
+    assert_close(run_shared(b, (rev, gs, pb)), ref, "f16", "group through an order")
     empty = (np.zeros(1, np.int32), np.zeros(0, np.int32))
     out = torch.full_like(b["query"], float("nan"))
     pkv.paged_attention_decode_shared_prefix(
         out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
-        dev_i32(b["context_lens"]), dev_i32(empty[0]), dev_i32(empty[1]), float(w.scale),
-        w.num_kv_heads)
+        dev_i32(b["context_lens"]), None, dev_i32(empty[0]), dev_i32(empty[1]),
+        float(w.scale), w.num_kv_heads)
     torch.cuda.synchronize()
     assert_close(out, ref, "f16", "no groups")
 
