@@ -66,6 +66,23 @@ int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 int32_t pkv_bm_shared_flags(const pkv_bm* bm, uint8_t* flags, int32_t n);
 
 /*
+ * The group description of paged_attention_decode_shared_prefix (pagedkv.h)
+ * for a batch of n sequences (positions 0..n-1 = seq_ids[0..n-1]):
+ * sequences whose first block is a full block held by more than one
+ * reference, and the same for all of them, form a group; order[0..n) is a
+ * stable permutation of the positions putting each group's members side
+ * by side (ordered by that first block, sequences without one last), group
+ * j is positions group_start[j] .. group_start[j+1] - 1 of order, and
+ * prefix_blocks[j] is the number of leading blocks every member holds in
+ * common, full blocks only (0 for a group of one).  order and
+ * prefix_blocks need room for n entries, group_start for n + 1;
+ * *num_groups receives the count.  PKV_BM_INVALID for null pointers or an
+ * unknown sequence (nothing written).
+ */
+int pkv_bm_prefix_groups(const pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* order,
+                         int32_t* group_start, int32_t* prefix_blocks, int32_t* num_groups);
+
+/*
  * A new sequence seq_id holding num_tokens tokens (its prompt): takes
  * ceil(num_tokens / block_size) blocks.  PKV_BM_INVALID if seq_id exists or
  * num_tokens < 0; PKV_BM_NO_BLOCKS if the pool has too few free blocks.

@@ -45,7 +45,7 @@ struct pkv_bm {
 
 extern "C" {
 
-int pkv_bm_abi_version(void) { return 2; }
+int pkv_bm_abi_version(void) { return 3; }
 
 pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size) {
   if (num_blocks <= 0 || block_size <= 0) return nullptr;
@@ -82,6 +82,55 @@ int32_t pkv_bm_shared_flags(const pkv_bm* bm, uint8_t* flags, int32_t n) {
   if (!bm || !flags || n < bm->num_blocks) return PKV_BM_INVALID;
   for (int32_t b = 0; b < bm->num_blocks; ++b) flags[b] = bm->refcount[b] > 1 ? 1 : 0;
   return bm->num_blocks;
+}
+
+int pkv_bm_prefix_groups(const pkv_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* order,
+                         int32_t* group_start, int32_t* prefix_blocks, int32_t* num_groups) {
+  if (!bm || n < 0 || !group_start || !num_groups ||
+      (n > 0 && (!seq_ids || !order || !prefix_blocks)))
+    return PKV_BM_INVALID;
+  std::vector<const pkv_bm::Seq*> q(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PKV_BM_INVALID;
+    q[i] = &it->second;
+  }
+  // a sequence's key: its first block when that block is full and shared
+  const int64_t kNone = INT64_MAX;
+  std::vector<int64_t> key(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq& s = *q[i];
+    key[i] = s.len >= bm->block_size && bm->refcount[s.blocks[0]] > 1 ? s.blocks[0] : kNone;
+  }
+  std::vector<int32_t> ord(n);
+  for (int32_t i = 0; i < n; ++i) ord[i] = i;
+  std::stable_sort(ord.begin(), ord.end(),
+                   [&](int32_t a, int32_t b) { return key[a] < key[b]; });
+  int32_t g = 0;
+  group_start[0] = 0;
+  for (int32_t i = 0; i < n;) {
+    int32_t e = i + 1;
+    if (key[ord[i]] != kNone)
+      while (e < n && key[ord[e]] == key[ord[i]]) ++e;
+    int32_t pb = 0;
+    if (e - i >= 2) {
+      int64_t full = INT64_MAX;
+      for (int32_t k = i; k < e; ++k) full = std::min(full, q[ord[k]]->len / bm->block_size);
+      const std::vector<int32_t>& lead = q[ord[i]]->blocks;
+      while (pb < full) {
+        bool same = true;
+        for (int32_t k = i + 1; k < e && same; ++k) same = q[ord[k]]->blocks[pb] == lead[pb];
+        if (!same) break;
+        ++pb;
+      }
+    }
+    prefix_blocks[g] = pb;
+    group_start[++g] = e;
+    i = e;
+  }
+  for (int32_t i = 0; i < n; ++i) order[i] = ord[i];
+  *num_groups = g;
+  return PKV_BM_OK;
 }
 
 int pkv_bm_add_sequence(pkv_bm* bm, int64_t seq_id, int64_t num_tokens) {

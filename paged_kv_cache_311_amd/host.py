@@ -5,6 +5,7 @@
     bm.add_sequence(seq_id, prompt_tokens)
     bm.fork(parent, child)
     slots, pairs = bm.append_slots([seq ids])     # one new token each
+    order, starts, shared = bm.prefix_groups([seq ids])  # shared-prefix decode
     tables, lens = bm.block_tables([seq ids], width)
     bm.free_sequence(seq_id)
 
@@ -23,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB_PATH = os.path.join(HERE, "libpkvhost.so")
 
 OK, INVALID, NO_BLOCKS = 0, -1, -5
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -65,6 +66,7 @@ def load_host_library(path=HOST_LIB_PATH):
         "pkv_bm_num_sequences": ([P], I32),
         "pkv_bm_refcount": ([P, I32], I32),
         "pkv_bm_shared_flags": ([P, P, I32], I32),
+        "pkv_bm_prefix_groups": ([P, P, I32, P, P, P, P], ctypes.c_int),
         "pkv_bm_add_sequence": ([P, I64, I64], ctypes.c_int),
         "pkv_bm_fork": ([P, I64, I64], ctypes.c_int),
         "pkv_bm_append_slot": ([P, I64, P, P, P], ctypes.c_int),
@@ -130,6 +132,22 @@ class BlockManager:
                                           len(out))
         _check(n if n < 0 else 0)
         return out
+
+    def prefix_groups(self, seq_ids):
+        """(order int32 [n], group_start int32 [G + 1], prefix_blocks int32
+        [G]) for a batch of these sequences: the group description of
+        paged_attention_decode_shared_prefix, from the tables and reference
+        counts (sequences sharing a full first block grouped, with their
+        common full leading blocks)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        order = np.empty(n, np.int32)
+        starts = np.empty(n + 1, np.int32)
+        shared = np.empty(max(n, 1), np.int32)
+        g = ctypes.c_int32()
+        _check(self._lib.pkv_bm_prefix_groups(self._h, _ptr(ids), n, _ptr(order),
+                                               _ptr(starts), _ptr(shared), ctypes.byref(g)))
+        return order, starts[:g.value + 1].copy(), shared[:g.value].copy()
 
     def add_sequence(self, seq_id, num_tokens):
         _check(self._lib.pkv_bm_add_sequence(self._h, int(seq_id), int(num_tokens)))

@@ -4,7 +4,9 @@ decode loop (marked gpu).
 Prompts are cached with reshape_and_cache, beams fork from them (shared
 blocks, reference counts), and every step takes one new token for each live
 beam from the manager: its copy-on-write pairs go to copy_blocks, its slots
-to reshape_and_cache, its block tables and lengths to paged_attention_decode.
+to reshape_and_cache, its block tables and lengths to paged_attention_decode,
+and its group description (from the reference counts) to
+paged_attention_decode_shared_prefix.
 Beams are killed and forked along the way, so blocks are released and
 reused.  After every step the pools must equal the oracle's replay of the
 same updates bit for bit, and the attention output must match the oracle's
@@ -62,7 +64,7 @@ def test_beam_decode_loop_driven_by_host_manager(gpu_lib, num_heads, num_kv_head
             live.append(next_id)
             next_id += 1
     scale = 1.0 / math.sqrt(D)
-    copies = 0
+    copies = shared_total = 0
     for step in range(24):
         if step % 6 == 5:                                # a beam dies, another splits
             bm.free_sequence(live.pop(int(rng.integers(len(live)))))
@@ -89,8 +91,18 @@ def test_beam_decode_loop_driven_by_host_manager(gpu_lib, num_heads, num_kv_head
         ref = oracle.decode_attention(wl.to_host(q), kc_h, vc_h, tables, lens, scale,
                                       num_kv_heads, dtype)
         assert_close(out, ref, dtype, f"step {step}")
-    say(f"    {copies} copy-on-write pairs, {bm.num_free} blocks free at the end")
-    assert copies > 0
+        # the shared-prefix call with the manager's groups (reference counts)
+        order, starts, shared = bm.prefix_groups(live)
+        sp = torch.full_like(q, float("nan"))
+        d = lambda a: torch.from_numpy(a).to(DEV)
+        pkv.paged_attention_decode_shared_prefix(sp, q, kc, vc, d(tables), d(lens), d(order),
+                                                 d(starts), d(shared), scale, num_kv_heads)
+        torch.cuda.synchronize()
+        shared_total += int(shared.sum())
+        assert_close(sp, ref, dtype, f"step {step}, shared prefixes {shared.tolist()}")
+    say(f"    {copies} copy-on-write pairs, {bm.num_free} blocks free at the end, "
+        f"{shared_total} shared blocks read once per group over the steps")
+    assert copies > 0 and shared_total > 0
     for s in live:
         bm.free_sequence(s)
     assert bm.num_free == NB
