@@ -45,14 +45,19 @@
 //                lane and 16-dim block.
 //                Lane l holds output dims 16j + 4(l/16) .. +3 of row
 //                l % 16, so the rescale by the row's running max and the
-//                final 1/sum are lane-local.
+//                final 1/sum are lane-local.  One more product per row
+//                block, of a block of ones with P^T, gives every lane its
+//                row's sum of the probabilities (no VALU sums).
 //   Masking selects only on the steps that reach past a wave's earliest
 //   row.  A row's max is raised only when a step's exceeds it by 2^8 (so
-//   probabilities stay below 256) and the rescale then runs for the wave.
+//   probabilities stay below 256) and the rescale then runs for the wave;
+//   each lane tests its own 8 scores first, so the maximum across a row's
+//   lanes is taken only on the steps that raise some row's max.
 //
 // Precision: products accumulate in float32; the probabilities enter the
-// second product rounded to the input type (as the values are); the row
-// sums are float32.
+// second product rounded to the input type (as the values are), and the
+// row sums add those same rounded probabilities (in float32), so the
+// weights of a row's values sum to one.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -221,13 +226,20 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   // table entry of the context, so the load is in bounds); their tokens,
   // and those past the context in its last block, are stored to LDS as
   // zeros.
+  // The entries are read with vector loads: a scalar load would share its
+  // wait counter with the LDS reads, and those are waited for in full at
+  // every step (scalar loads return out of order), so every step would wait
+  // out a table round trip.  A vector load is waited for only where its id
+  // is used, one step after it was issued.
   const int nblk = (Lc + kBlockSize - 1) / kBlockSize;
+  const __amdgpu_buffer_rsrc_t table_rs = buffer_rsrc(table, (uint32_t)p.max_blocks * 4u);
   int32_t ids[NCH], ids_next[NCH];
   auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int bi = step * (kKeys / kBlockSize) + half_u[u];
-      dst[u] = __builtin_amdgcn_readfirstlane(table[bi < nblk ? bi : 0]);
+      dst[u] = __builtin_amdgcn_raw_buffer_load_b32(table_rs, (bi < nblk ? bi : 0) * 4, 0,
+                                                    kCacheDefault);
     }
   };
   // Loads are issued for every step, also past the last one, so the
@@ -236,7 +248,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   auto gload = [&](Stage& st, const int32_t (&id)[NCH]) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int64_t b = min(max(id[u], 0), max_blk);  // clamped into the pool
+      const int idu = __builtin_amdgcn_readfirstlane(id[u]);
+      const int64_t b = min(max(idu, 0), max_blk);  // clamped into the pool
       const int64_t off = b * blk_bytes + head_bytes;
       st.k[u] = load16_buffer<kCacheDefault>(buffer_rsrc(p.kcache + off, kTileBytes), in_tile[u]);
       st.v[u] = load16_buffer<kCacheDefault>(buffer_rsrc(p.vcache + off, kTileBytes), in_tile[u]);
@@ -278,14 +291,17 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 
   // running max in log2 units, floored at -1e30 so that a row with nothing
   // visible yet keeps alpha = 1 and p = 0 (no infinity minus infinity)
-  float m_run[kRB], l_run[kRB];
+  float m_run[kRB];
   floatx4 acc[kRB][NDB];
+  floatx4 lacc[kRB];  // row sums: the product of a block of ones with P^T
+  constexpr uint32_t kOnes = DT == PKV_F16 ? 0x3C003C00u : 0x3F803F80u;
+  const u32x4 ones = u32x4{kOnes, kOnes, kOnes, kOnes};
   const float c2 = p.scale_log2;
   const int wave_pos0 = base + min(R0 + w * kRB * 16, rows - 1) / G;  // earliest row of the wave
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     m_run[rb] = -1e30f;
-    l_run[rb] = 0.f;
+    lacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -356,27 +372,25 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
           x[e] = t <= pos[rb] ? x[e] : -INFINITY;
         }
       }
+      // The lane's own maximum decides whether its row's max may need
+      // raising (the row's running max is the same in its four lanes); only
+      // then is the row's maximum taken across them.
       float mt = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      const float m_tile = max4rows(mt) * c2;
-      const bool grow = m_tile > m_run[rb] + kSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // some row of the wave: rescale it
+      if (__builtin_amdgcn_ballot_w64(mt * c2 > m_run[rb] + kSlack)) {  // rescale some rows
+        const float m_tile = max4rows(mt) * c2;
+        const bool grow = m_tile > m_run[rb] + kSlack;
         const float m_new = grow ? m_tile : m_run[rb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         m_run[rb] = m_new;
-        l_run[rb] *= alpha;
+        lacc[rb] *= alpha;
 #pragma unroll
         for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
       }
       float pe[8];
-      float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_run[rb]));
-        psum += pe[e];
-      }
-      l_run[rb] += psum;
+      for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_run[rb]));
 #pragma unroll
       for (int e = 0; e < 4; ++e) pb[rb][e] = pack2<DT>(pe[2 * e], pe[2 * e + 1]);
     }
@@ -387,6 +401,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
     }
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) lacc[rb] = mfma32<DT>(ones, pb[rb], lacc[rb]);
 
     if (step + 1 < nsteps) lstore(ready, buf ^ 1, step + 1);
 #pragma unroll
@@ -395,11 +411,16 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   };
 
   if (nsteps > 0) {
+    // issued in the order the loop keeps (a step's table entries, then the
+    // tiles of the step before them), so that the loads in flight at the
+    // loop's head are the same on entry as on every later pass
     read_ids(0, ids);
     gload(sa, ids);
     read_ids(1, ids);
+    read_ids(2, ids_next);
     gload(sb, ids);
-    read_ids(2, ids);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
     lstore(sa, 0, 0);
   }
   __syncthreads();
@@ -411,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   // normalize and store: lane l holds dims 16j + 4(l/16) .. +3 of its row
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const float l = sum4rows(l_run[rb]);
+    const float l = lacc[rb][0];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (row_ok[rb]) {
       char* dst = (char*)p.out + (row_off[rb] + 4 * grp) * 2;
