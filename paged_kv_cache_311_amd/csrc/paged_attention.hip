@@ -160,14 +160,25 @@ struct DecodeCfg {
   static constexpr int kMinWaves =
       kPvMfma ? (kFp8 ? 3 : 2)
               : (kNarrow && (GC == 1 || (GC == 2 && D == 64)) ? 3 : (kNarrow && GC <= 4 ? 2 : 1));
-  static constexpr int kGridWaves = kFp8 ? kWavesPerSimdFp8 : kWavesPerSimd;
+  // Sixteen heads per group (16-bit pools): one wave per SIMD, with the
+  // next tile in flight during the compute (below).  A tile's products and
+  // softmax for 16 heads take long enough that a wave which waits for its
+  // next tile before computing leaves the stream idle meanwhile, and half
+  // the waves make half the split pieces (measured on one MI355X, 32 query
+  // / 2 kv heads over 16 x 32K bfloat16 tokens, decode call: 100 us at two
+  // waves per SIMD, 106 with the next tile in flight there, 95 at one wave
+  // with it, 114 at one wave without it; with 4 or 8 heads per group one
+  // wave per SIMD is within 1% of two).
+  static constexpr bool kWide = kPvMfma && !kFp8 && GC == 16;
+  static constexpr int kGridWaves = kFp8 ? kWavesPerSimdFp8 : (kWide ? 1 : kWavesPerSimd);
   // E4M3 tiles: the next tile's loads stay in flight while the current
-  // tile is computed.  16-bit tiles: the wave waits for them as well before
+  // tile is computed (also 16-bit tiles with sixteen heads per group, see
+  // kWide).  Other 16-bit tiles: the wave waits for them as well before
   // computing; their stream is at the HBM ceiling already and more loads
   // in flight only add contention (measured on one MI355X: overlapping is
   // 15% faster on the 32K-token grouped workload with E4M3 pools, 3.7%
   // slower with bfloat16 pools).
-  static constexpr bool kOverlapNext = kFp8;
+  static constexpr bool kOverlapNext = kFp8 || kWide;
   // Appending: new-token rows a wave holds in LDS before writing them
   static constexpr int kNewRecs = !AP ? 0 : kPvMfma ? 4 : 8;
   // E4M3 appending: new-row elements each lane encodes, and their bytes
