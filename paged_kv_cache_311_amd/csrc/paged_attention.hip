@@ -803,37 +803,31 @@ __device__ void merge_by_workgroup(const DecodeParams& p, const Split& sp, int l
 // is merged by the waves of the ranges it spans.  With n ranges whose first
 // tile lies in the segment (at most one per 8 chunks), the k-th of them
 // takes the k-th of n contiguous runs of the [GC][D] accumulator's 16-B
-// chunks.  Its lanes are 8 chunk
-// lanes x 8 piece lanes: lane (c, i) folds chunk c of pieces i, i + 8, ...
-// (8 pieces' loads go out together; 8 chunk lanes read 128 contiguous bytes
-// of a piece), then the 8 piece lanes of each chunk are combined.
-constexpr int kSliceChunkLanes = 8;
-constexpr int kSlicePieceLanes = kWave / kSliceChunkLanes;
+// chunks.  Its lanes are CL chunk lanes x 64 / CL piece lanes: lane (c, i)
+// folds chunk c of pieces i, i + 64 / CL, ... (kSliceUnroll pieces' loads
+// go out together; the chunk lanes read contiguous bytes of a piece), then
+// the piece lanes of each chunk are combined.  Runs of up to 8 chunks take
+// 8 chunk lanes; wider runs (few pieces, so few ranges) take 16, so that a
+// run still costs one round trip per batch of pieces.
 constexpr int kSliceUnroll = 8;
 
-template <int DT, int D, int GC>
-__device__ void merge_slice(const DecodeParams& p, const Split& sp, int r, int lane) {
-  constexpr int kChunks = GC * D / 4;
-  const int first = sp.rf + (sp.rf_tail ? 1 : 0);  // range rf starts in another segment
-  // slices of at least kSliceChunkLanes chunks: a wave's round trip then
-  // brings a full row of chunk lanes (narrow states use the first few ranges)
-  const int n = min(sp.rf + sp.np - first, FoldState<D, GC>::kMaxSlices);
-  const int cpp = (kChunks + n - 1) / n;
-  const int cbeg = (r - first) * cpp;
-  const int cend = min(cbeg + cpp, kChunks);
-  const int cl = lane % kSliceChunkLanes;
-  const int pl = lane / kSliceChunkLanes;
-  for (int c0 = cbeg; c0 < cend; c0 += kSliceChunkLanes) {
+template <int DT, int D, int GC, int CL>
+__device__ void merge_slice_run(const DecodeParams& p, const Split& sp, int cbeg, int cend,
+                                int lane) {
+  constexpr int PL = kWave / CL;
+  const int cl = lane % CL;
+  const int pl = lane / CL;
+  for (int c0 = cbeg; c0 < cend; c0 += CL) {
     const int c = min(c0 + cl, cend - 1);
     const int g = c * 4 / D;
     float M = -INFINITY, S = 0.f;
     floatx4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < sp.np; i0 += kSlicePieceLanes * kSliceUnroll) {
+    for (int i0 = 0; i0 < sp.np; i0 += PL * kSliceUnroll) {
       float mm[kSliceUnroll], ll[kSliceUnroll];
       u32x4 aa[kSliceUnroll];
 #pragma unroll
       for (int u = 0; u < kSliceUnroll; ++u) {
-        const int i = min(i0 + pl + u * kSlicePieceLanes, sp.np - 1);
+        const int i = min(i0 + pl + u * PL, sp.np - 1);
         const int64_t sl = piece_slot(sp, i);
         mm[u] = p.part_ml[(sl * GC + g) * 2 + 0];
         ll[u] = p.part_ml[(sl * GC + g) * 2 + 1];
@@ -846,7 +840,7 @@ __device__ void merge_slice(const DecodeParams& p, const Split& sp, int r, int l
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kSliceUnroll; ++u) {
-        const bool ok = i0 + pl + u * kSlicePieceLanes < sp.np;
+        const bool ok = i0 + pl + u * PL < sp.np;
         const float Mn = ok ? fmaxf(M, mm[u]) : M;  // every piece's max is finite
         const float a = ok ? __builtin_amdgcn_exp2f(M - Mn) : 1.f;
         const float b = ok ? __builtin_amdgcn_exp2f(mm[u] - Mn) : 0.f;
@@ -857,14 +851,30 @@ __device__ void merge_slice(const DecodeParams& p, const Split& sp, int r, int l
       }
     }
     // lanes without a piece hold max -inf and weigh 0
-    const float Mw = max_over_lane_groups<kSliceChunkLanes>(M);
+    const float Mw = max_over_lane_groups<CL>(M);
     const float wt = __builtin_amdgcn_exp2f(M - Mw);
-    const float Sw = sum_over_lane_groups<kSliceChunkLanes>(S * wt);
+    const float Sw = sum_over_lane_groups<CL>(S * wt);
     floatx4 Ow;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Ow[e] = sum_over_lane_groups<kSliceChunkLanes>(O[e] * wt);
+    for (int e = 0; e < 4; ++e) Ow[e] = sum_over_lane_groups<CL>(O[e] * wt);
     if (pl == 0 && c0 + cl < cend) store_merged<DT, D, GC>(p, sp, c0 + cl, Ow, 1.f / Sw);
   }
+}
+
+template <int DT, int D, int GC>
+__device__ void merge_slice(const DecodeParams& p, const Split& sp, int r, int lane) {
+  constexpr int kChunks = GC * D / 4;
+  const int first = sp.rf + (sp.rf_tail ? 1 : 0);  // range rf starts in another segment
+  // slices of at least 8 chunks: a wave's round trip then brings a full row
+  // of chunk lanes (narrow states use the first few ranges)
+  const int n = min(sp.rf + sp.np - first, FoldState<D, GC>::kMaxSlices);
+  const int cpp = (kChunks + n - 1) / n;
+  const int cbeg = (r - first) * cpp;
+  const int cend = min(cbeg + cpp, kChunks);
+  if (cpp > 8)
+    merge_slice_run<DT, D, GC, 16>(p, sp, cbeg, cend, lane);
+  else
+    merge_slice_run<DT, D, GC, 8>(p, sp, cbeg, cend, lane);
 }
 
 // ------------------------------------------------------------ main kernel --
