@@ -138,7 +138,8 @@ def test_append_reduced_workload_every_output(gpu_lib, key):
     append_and_check(wl.make_batch(w, w.default_seed + 3, DEV), seed=3)
 
 
-@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "beam"])
+@pytest.mark.parametrize("key", ["opt13b", "llama13b_conv", "beam", "long_gqa_p512", "gqa8_long",
+                                 "gqa16_long"])
 def test_append_full_size_sampled(gpu_lib, key):
     """Full workload in the benchmark's launch configuration; the oracle on
     a sample of sequences, the separate calls on all of them."""
