@@ -26,11 +26,11 @@
 //               of 16 rows.  It walks the keys 32 at a time (two pool
 //               blocks), from token 0 to the last position its rows see.
 //   per step  = the 256 threads load the two blocks' K and V tiles
-//               (16-B chunks, a row's chunks on consecutive lanes) into
-//               registers, then into one of two LDS buffers;
-//               the step after computes from that buffer while the next
-//               step's loads are in flight.  The table entries a step needs
-//               are read one step earlier than its tiles.
+//               straight from the pool into one of three LDS buffers (16 B
+//               per lane, no register stage): step s computes from its
+//               buffer while step s + 1's tiles land in the next and step
+//               s + 2's are issued into the third.  The table entries a step
+//               needs are read (scalar loads) one step before its tiles.
 //
 // Per step and wave (transposed products, so no operand needs a shuffle):
 //   S^T = K Q^T  MFMA 16x16x32: A = key rows from LDS as stored, B = the
@@ -85,16 +85,20 @@ constexpr int kMinBundle = 4;
 // accumulator is rescaled rarely.
 constexpr float kSlack = 8.f;
 
-// LDS: two buffers of K [32 tokens][D] and V [32 tokens][D], rows padded
-// so that the 16 lanes of a 16-B key read, and the four rows of a
-// transposing value read, fall on distinct banks.
+// LDS: three buffers of K [32 tokens][D] and V [32 tokens][D], rows
+// unpadded.  Within a row, the pool row's 16-B chunk c sits at chunk
+// c ^ kswz(row) (keys) or c ^ vswz(row) (values), so that the 16 rows of a
+// key read, and the 4 rows of a transposing value read, fall on distinct
+// banks.
 template <int D>
 struct Lds {
-  static constexpr int kKS = D * 2 + 16;      // key row stride (bytes), 16-B aligned
-  static constexpr int kVS = D * 2 + 32;      // value row stride: 4 rows on distinct banks
-  static constexpr int kKBuf = kKeys * kKS;
-  static constexpr int kVBuf = kKeys * kVS;
-  static constexpr int kBytes = 2 * kKBuf + 2 * kVBuf;
+  static constexpr int kRowB = D * 2;
+  static constexpr int kCpr = kRowB / 16;                // 16-B chunks per row
+  static constexpr int kRowsPer256 = 256 / kRowB;        // rows per 256 B (64 banks)
+  static constexpr int kBuf = kKeys * kRowB;             // one tensor of one step
+  static constexpr int kBytes = 6 * kBuf;                // K, V x 3 buffers
+  static __device__ __forceinline__ int kswz(int row) { return (row / kRowsPer256) % kCpr; }
+  static __device__ __forceinline__ int vswz(int row) { return 2 * ((row % 4) / kRowsPer256); }
 };
 
 struct Params {
@@ -128,14 +132,18 @@ __device__ __forceinline__ uint32_t finite_pair(uint32_t w, bool lo, bool hi) {
   return (lo ? fa : a) | ((hi ? fb : b) << 16);
 }
 
+// a buffer index as a type (for the unrolled copies of a step)
+template <int P>
+struct Phase {
+  static constexpr int value = P;
+};
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params p) {
   using LD = Lds<D>;
   constexpr int NKS = D / 32;                    // QK k-steps of 32 dims
   constexpr int NDB = D / 16;                    // output blocks of 16 dims
   constexpr int CPR = D / 8;                     // 16-B chunks per token row
-  constexpr int NCH = kKeys * CPR / kThreads;    // chunks per thread per tensor
-  static_assert(NCH * kThreads == kKeys * CPR, "whole chunks per thread");
   __shared__ __attribute__((aligned(16))) char lds[LD::kBytes];
 
   // workgroup -> (sequence, kv head, row tile).  Workgroups are dealt to
@@ -195,98 +203,113 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
                             : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // cooperative tile loads: chunk c = tid + 256u is 16 B of token c / CPR
-  // of the step (a row's chunks on consecutive lanes).  All 64 chunks of a
-  // wave's load u lie in one pool block (16 tokens of D * 2 bytes make 16
-  // KiB and more per block, 1 KiB per wave load), so the block id and the
-  // tile's base address are wave-uniform (scalar registers) and each lane
-  // adds only its fixed offset inside the tile.  The block ids a step needs
-  // are read from the table one step before its tiles are loaded, so the
-  // two reads never follow one another.
+  // Tiles go from the pool straight into LDS (global_load_lds, 16 B per
+  // lane): each wave instruction fills 1 KiB of one buffer, whole token
+  // rows of one pool block, lane l taking the LDS slot l (row l / CPR of the
+  // KiB, chunk l % CPR) and reading the pool chunk the swizzle puts there.
+  // A wave's KiBs of a step lie in one pool block, so it needs one block id
+  // per step (read from the table with a vector load a step before use).
   constexpr int kTileBytes = kBlockSize * D * 2;
+  constexpr int kRowsPerKiB = 1024 / LD::kRowB;
+  constexpr int kDma = kKeys * LD::kRowB / 1024 / kWaves;  // KiBs per wave per tensor
+  static_assert(kDma * kWaves * 1024 == kKeys * LD::kRowB, "whole KiBs per wave");
+  static_assert(kDma * kRowsPerKiB <= kBlockSize, "a wave's rows in one pool block");
   const int64_t blk_bytes = (int64_t)p.num_kv_heads * kTileBytes;
   const int64_t head_bytes = (int64_t)g * kTileBytes;
   const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
-  struct Stage {
-    u32x4 k[NCH], v[NCH];
-  };
-  // per chunk: its token within a step, and its byte offset inside the
-  // kv head's tile (both fixed for the thread); the step's block holding
-  // load u of this wave (0 or 1, uniform)
-  int tk_u[NCH], half_u[NCH];
-  uint32_t in_tile[NCH];
+  const int row_w0 = w * kDma * kRowsPerKiB;      // the wave's first row of a step
+  const int dma_half = row_w0 / kBlockSize;       // its pool block of the step's two
+  uint32_t ksrc[kDma], vsrc[kDma];                // pool byte offsets inside the tile
 #pragma unroll
-  for (int u = 0; u < NCH; ++u) {
-    const int c = tid + u * kThreads;
-    tk_u[u] = c / CPR;
-    in_tile[u] = (uint32_t)((tk_u[u] % kBlockSize) * D * 2 + (c - tk_u[u] * CPR) * 16);
-    half_u[u] = ((w * kWave + u * kThreads) / CPR) / kBlockSize;
+  for (int u = 0; u < kDma; ++u) {
+    const int row = row_w0 + u * kRowsPerKiB + lane / CPR;
+    const int ch = lane % CPR;
+    ksrc[u] = (uint32_t)((row % kBlockSize) * LD::kRowB + (ch ^ LD::kswz(row)) * 16);
+    vsrc[u] = (uint32_t)((row % kBlockSize) * LD::kRowB + (ch ^ LD::vswz(row)) * 16);
   }
-  // Blocks past the context read the sequence's first block instead (a
-  // table entry of the context, so the load is in bounds); their tokens,
-  // and those past the context in its last block, are stored to LDS as
-  // zeros.
-  // The entries are read with vector loads: a scalar load would share its
-  // wait counter with the LDS reads, and those are waited for in full at
-  // every step (scalar loads return out of order), so every step would wait
-  // out a table round trip.  A vector load is waited for only where its id
-  // is used, one step after it was issued.
   const int nblk = (Lc + kBlockSize - 1) / kBlockSize;
-  const __amdgpu_buffer_rsrc_t table_rs = buffer_rsrc(table, (uint32_t)p.max_blocks * 4u);
-  int32_t ids[NCH], ids_next[NCH];
-  auto read_ids = [&](int step, int32_t (&dst)[NCH]) {
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int bi = step * (kKeys / kBlockSize) + half_u[u];
-      dst[u] = __builtin_amdgcn_raw_buffer_load_b32(table_rs, (bi < nblk ? bi : 0) * 4, 0,
-                                                    kCacheDefault);
-    }
+  // The table is read with scalar loads (the address is the same for the
+  // whole wave); their waits share the LDS counter, and each falls at the
+  // head of a step, where no LDS operation is in flight.
+  const __attribute__((address_space(4))) int32_t* ctab =
+      (const __attribute__((address_space(4))) int32_t*)table;
+  // the block id of the wave's rows of a step (blocks past the context:
+  // the sequence's first block, a table entry of the context)
+  auto read_id = [&](int step) __attribute__((always_inline)) -> int {
+    const int bi = step * (kKeys / kBlockSize) + dma_half;
+    return ctab[bi < nblk ? bi : 0];
   };
-  // Loads are issued for every step, also past the last one, so the
-  // compiler's count of loads in flight is the same on every path.
   const int max_blk = (int)(p.num_blocks - 1);
-  auto gload = [&](Stage& st, const int32_t (&id)[NCH]) {
+  char* const lds_k = lds;
+  char* const lds_v = lds + 3 * LD::kBuf;
+  const uint32_t lds_k_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_k;
+  const uint32_t lds_v_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_v;
+  // The wave's KiBs of a step into buffer buf.  The loads are written out
+  // (M0 = the KiB's LDS address, one wait state after writing it), so that
+  // the compiler counts no LDS write in them: it would otherwise hold every
+  // transposing LDS read until all such loads in flight had landed, the
+  // next steps' too.  The waits that order them are the explicit ones below.
+  auto dma = [&](int id, int buf) __attribute__((always_inline)) {
+    const int64_t b = min(max(id, 0), max_blk);  // clamped into the pool
+    const char* kt = p.kcache + b * blk_bytes + head_bytes;
+    const char* vt = p.vcache + b * blk_bytes + head_bytes;
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int idu = __builtin_amdgcn_readfirstlane(id[u]);
-      const int64_t b = min(max(idu, 0), max_blk);  // clamped into the pool
-      const int64_t off = b * blk_bytes + head_bytes;
-      st.k[u] = load16_buffer<kCacheDefault>(buffer_rsrc(p.kcache + off, kTileBytes), in_tile[u]);
-      st.v[u] = load16_buffer<kCacheDefault>(buffer_rsrc(p.vcache + off, kTileBytes), in_tile[u]);
+    for (int u = 0; u < kDma; ++u) {
+      const uint32_t kib = (uint32_t)((w * kDma + u) * 1024 + buf * LD::kBuf);
+      asm volatile(
+          "s_mov_b32 m0, %2\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %0, %1\n\t"
+          "s_mov_b32 m0, %5\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %3, %4"
+          :
+          : "v"(ksrc[u]), "s"(kt), "s"(lds_k_addr + kib), "v"(vsrc[u]), "s"(vt),
+            "s"(lds_v_addr + kib)
+          : "memory", "m0");
     }
   };
-  // Stored to LDS as rows.  A masked probability is an exact zero, but the
-  // second product still meets the value it multiplies (0 x inf = NaN), so
-  // on the steps that mask keys for some row of the workgroup (or reach
-  // past the context) the values are made safe first: tokens past the
-  // context become zeros, whatever the slot read in their place holds, and
-  // the non-finite values of keys past the workgroup's earliest row become
-  // the largest finite value of their sign (NaN: +).  Rows that do not see
-  // such a key are then exact; rows that see a non-finite value there get
-  // that largest value in its place.  Other steps are stored as read.
+  // Once a step's tiles have landed: on the steps that mask keys for some
+  // row of the workgroup (or reach past the context), each lane makes its
+  // own slots safe.  A masked probability is an exact zero, but the second
+  // product still meets the value it multiplies (0 x inf = NaN): tokens past
+  // the context become zeros, whatever the slot read in their place holds,
+  // and the non-finite values of keys past the workgroup's earliest row
+  // become the largest finite value of their sign (NaN: +).  Rows that do
+  // not see such a key are then exact; rows that see a non-finite value
+  // there get that largest value in its place.
   const int wg_pos0 = base + R0 / G;  // position of the workgroup's earliest row
-  auto lstore = [&](const Stage& st, int buf, int step) {
-    char* kb = lds + buf * LD::kKBuf;
-    char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
-    const bool edge = step * kKeys + kKeys - 1 > wg_pos0;
+  auto fixup = [&](int buf, int step) __attribute__((always_inline)) {
+    if (step * kKeys + kKeys - 1 <= wg_pos0) return;
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int c = tid + u * kThreads;
-      const int tk = c / CPR;
-      u32x4 kv = st.k[u], vv = st.v[u];
-      if (edge) {
-        const int t = step * kKeys + tk_u[u];
-        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-        if (t > wg_pos0) {
+    for (int u = 0; u < kDma; ++u) {
+      const int kib = w * kDma + u;
+      const int t = step * kKeys + row_w0 + u * kRowsPerKiB + lane / CPR;
+      char* ks = lds_k + buf * LD::kBuf + kib * 1024 + lane * 16;
+      char* vs = lds_v + buf * LD::kBuf + kib * 1024 + lane * 16;
+      u32x4 kv = *reinterpret_cast<const u32x4*>(ks);
+      u32x4 vv = *reinterpret_cast<const u32x4*>(vs);
+      if (t > wg_pos0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vv[i] = finite_pair<DT>(vv[i], true, true);
-        }
-        kv = t >= Lc ? zero : kv;
-        vv = t >= Lc ? zero : vv;
+        for (int i = 0; i < 4; ++i) vv[i] = finite_pair<DT>(vv[i], true, true);
       }
-      store16(kb + tk * LD::kKS + (c - tk * CPR) * 16, kv);
-      store16(vb + tk * LD::kVS + (c - tk * CPR) * 16, vv);
+      const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+      kv = t >= Lc ? zero : kv;
+      vv = t >= Lc ? zero : vv;
+      *reinterpret_cast<u32x4*>(ks) = kv;
+      *reinterpret_cast<u32x4*>(vs) = vv;
     }
+  };
+  // Waits written out, so that no memory access moves across them: a
+  // step's tiles have landed while the 2 kDma loads of the next step's
+  // (issued after them) stay in flight.  A step's LDS writes are then
+  // published by a barrier (lgkmcnt(0) first: this wave's LDS operations
+  // done).
+  auto wait_tiles = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDma) : "memory");
+  };
+  auto publish = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   // running max in log2 units, floored at -1e30 so that a row with nothing
@@ -306,26 +329,30 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     for (int j = 0; j < NDB; ++j) acc[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Three steps in flight: while step s is computed from LDS buffer s % 2,
-  // the tiles of step s + 1 sit in one register stage (stored to the other
-  // buffer after the compute) and those of step s + 2 arrive in the other
-  // stage.  The body is written once and run with the two stages swapped.
-  Stage sa, sb;
-  auto body = [&](int step, Stage& fill, const Stage& ready) __attribute__((always_inline)) {
-    const int buf = step & 1;
-    read_ids(step + 3, ids_next);
-    gload(fill, ids);
-    const char* kb = lds + buf * LD::kKBuf;
-    const char* vb = lds + 2 * LD::kKBuf + buf * LD::kVBuf;
+  // Three steps in flight, in three buffers: step s is computed from buffer
+  // s % 3 while step s + 1's tiles land in the next and step s + 2's are
+  // issued into the third (the one step s - 1 was computed from).
+  int id_n = 0;  // block id of step s + 2, read during step s - 1
+  // The loop is unrolled by the three buffers, so that each copy's buffer
+  // offsets are constants (folded into the LDS instructions' offsets).
+  auto body = [&](int step, auto phase) __attribute__((always_inline)) {
+    constexpr int bcur = decltype(phase)::value;
+    constexpr int bnxt = (bcur + 1) % 3;
+    constexpr int bfar = (bcur + 2) % 3;
+    const int id_nn = read_id(step + 3);
+    dma(id_n, bfar);
+    const char* kb = lds_k + bcur * LD::kBuf;
+    const char* vb = lds_v + bcur * LD::kBuf;
 
     // S^T for both key blocks and both row blocks: all key operands are
     // read from LDS first, so their latencies overlap
     u32x4 ka[2][NKS];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const int r = h * 16 + col;
 #pragma unroll
       for (int m = 0; m < NKS; ++m)
-        ka[h][m] = load16(kb + (h * 16 + col) * LD::kKS + (32 * m + 8 * grp) * 2);
+        ka[h][m] = load16(kb + r * LD::kRowB + ((4 * m + grp) ^ LD::kswz(r)) * 16);
     }
     __builtin_amdgcn_sched_barrier(0);
     floatx4 sc[kRB][2];
@@ -344,12 +371,22 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     // runs: lane l gets dim 16j + l % 16 of tokens 4(l/16) + 0..3 of each
     // block (the probabilities' k order)
     u32x4 va[NDB];
-    const char* vsrc = vb + (4 * grp + (col >> 2)) * LD::kVS + (col & 3) * 8;
+    {
+      // dim block j = jl + kT jh sits at chunk 2 (jl ^ t) + 2 kT jh (+1 for
+      // the lane's upper 8 dims): kT lane addresses, the rest offsets; the
+      // second block's rows (16 on) have the same swizzle
+      constexpr int kT = 4 / LD::kRowsPer256;  // distinct swizzles of the rows
+      static_assert(NDB % kT == 0, "dim blocks in whole swizzle periods");
+      const int r0 = 4 * grp + (col >> 2);
+      const int t = LD::vswz(r0) / 2;
+      const char* vrow = vb + r0 * LD::kRowB + (col & 1) * 8 + ((col & 3) >> 1) * 16;
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) {
-      const uint2 lo = read_tr16(vsrc + 32 * j);
-      const uint2 hi = read_tr16(vsrc + 16 * LD::kVS + 32 * j);
-      va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      for (int j = 0; j < NDB; ++j) {
+        const char* a = vrow + 32 * ((j % kT) ^ t) + 32 * kT * (j / kT);
+        const uint2 lo = read_tr16(a);
+        const uint2 hi = read_tr16(a + 16 * LD::kRowB);
+        va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -404,30 +441,37 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) lacc[rb] = mfma32<DT>(ones, pb[rb], lacc[rb]);
 
-    if (step + 1 < nsteps) lstore(ready, buf ^ 1, step + 1);
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
-    __syncthreads();
+    // step + 1's tiles have landed (step + 2's, issued after them, stay in
+    // flight); made safe where needed, then published
+    __builtin_amdgcn_sched_barrier(0);
+    wait_tiles();
+    fixup(bnxt, step + 1);
+    id_n = id_nn;
+    publish();
   };
 
   if (nsteps > 0) {
-    // issued in the order the loop keeps (a step's table entries, then the
-    // tiles of the step before them), so that the loads in flight at the
-    // loop's head are the same on entry as on every later pass
-    read_ids(0, ids);
-    gload(sa, ids);
-    read_ids(1, ids);
-    read_ids(2, ids_next);
-    gload(sb, ids);
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) ids[u] = ids_next[u];
-    lstore(sa, 0, 0);
+    // steps 0 and 1 issued as the loop would, step 0's waited for
+    const int id0 = read_id(0);
+    const int id1 = read_id(1);
+    dma(id0, 0);
+    id_n = read_id(2);
+    dma(id1, 1);
+    wait_tiles();
+    fixup(0, 0);
   }
-  __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    body(step, sa, sb);
-    if (step + 1 < nsteps) body(step + 1, sb, sa);
+  // the queries have arrived (a wait the compiler sees, on either path, so
+  // that it adds none for them inside the loop)
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  publish();
+  int step = 0;
+  for (; step + 3 <= nsteps; step += 3) {
+    body(step, Phase<0>{});
+    body(step + 1, Phase<1>{});
+    body(step + 2, Phase<2>{});
   }
+  if (step < nsteps) body(step, Phase<0>{});
+  if (step + 1 < nsteps) body(step + 1, Phase<1>{});
 
   // normalize and store: lane l holds dims 16j + 4(l/16) .. +3 of its row
 #pragma unroll
