@@ -405,9 +405,14 @@ int paged_attention_decode_append_fp8(void* out, const void* query, void* key_ca
  * a key are exact, rows that do see a non-finite value there get that
  * largest value in its place rather than an infinity or NaN.
  *
+ * The scale may be any finite float: a negative one is applied by
+ * flipping the queries' signs, and zero weighs the visible tokens equally
+ * (it is taken as 1e-30 / log2 e, equal weights to float32 precision).
+ *
  * Errors: INVALID_ARG for null pointers, sizes
- * out of range, Hq % Hkv != 0 or misalignment; UNSUPPORTED for other
- * dtypes, block_size != 16 or head_size not 64/128.  Device-side contents
+ * out of range, Hq % Hkv != 0, misalignment or a non-finite scale;
+ * UNSUPPORTED for other dtypes, block_size != 16 or head_size not 64/128.
+ * Device-side contents
  * (tables, lengths, query_start_loc) are not validated; every read stays
  * inside the buffers whatever they hold, provided query_start_loc
  * describes rows of `query`.

@@ -109,7 +109,7 @@ struct Params {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start_loc;
-  float scale_log2;  // softmax scale x log2 e
+  float scale_log2;  // |softmax scale| x log2 e, at least 1e-30
   int num_seqs, num_heads, num_kv_heads, max_blocks;
   int64_t num_blocks;
   int row_tiles;     // 128-row tiles per (sequence, kv head) the grid covers
@@ -138,7 +138,7 @@ struct Phase {
   static constexpr int value = P;
 };
 
-template <int DT, int D>
+template <int DT, int D, bool kNeg>
 __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params p) {
   using LD = Lds<D>;
   constexpr int NKS = D / 32;                    // QK k-steps of 32 dims
@@ -184,7 +184,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  // this lane's rows (one per 16-row block) and their query operands
+  // this lane's rows (one per 16-row block) and their query operands.  A
+  // negative scale is carried by the queries (kNeg: their signs flipped),
+  // so that the softmax works with a positive one and a row's largest score
+  // is its largest scaled logit.
+  constexpr uint32_t qsign = kNeg ? 0x80008000u : 0u;
   u32x4 q[kRB][NKS];
   int pos[kRB];
   int64_t row_off[kRB];  // element offset of the row in query / out
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     row_off[rb] = ((int64_t)(q0 + i) * p.num_heads + g * G + (rc - i * G)) * D;
 #pragma unroll
     for (int m = 0; m < NKS; ++m)
-      q[rb][m] = row_ok[rb] ? load16(p.query + (row_off[rb] + 32 * m + 8 * grp) * 2)
+      q[rb][m] = row_ok[rb] ? load16(p.query + (row_off[rb] + 32 * m + 8 * grp) * 2) ^ qsign
                             : u32x4{0u, 0u, 0u, 0u};
   }
 
@@ -256,17 +260,14 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 #pragma unroll
     for (int u = 0; u < kDma; ++u) {
       const uint32_t kib = (uint32_t)((w * kDma + u) * 1024 + buf * LD::kBuf);
-      asm volatile(
-          "s_mov_b32 m0, %2\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %0, %1\n\t"
-          "s_mov_b32 m0, %5\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %3, %4"
-          :
-          : "v"(ksrc[u]), "s"(kt), "s"(lds_k_addr + kib), "v"(vsrc[u]), "s"(vt),
-            "s"(lds_v_addr + kib)
-          : "memory", "m0");
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :
+                   : "v"(ksrc[u]), "s"(kt), "{m0}"(lds_k_addr + kib)
+                   : "memory");
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :
+                   : "v"(vsrc[u]), "s"(vt), "{m0}"(lds_v_addr + kib)
+                   : "memory");
     }
   };
   // Once a step's tiles have landed: on the steps that mask keys for some
@@ -315,6 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
   // running max in log2 units, floored at -1e30 so that a row with nothing
   // visible yet keeps alpha = 1 and p = 0 (no infinity minus infinity)
   float m_run[kRB];
+  float m_thr[kRB];  // m_run + kSlack
   floatx4 acc[kRB][NDB];
   floatx4 lacc[kRB];  // row sums: the product of a block of ones with P^T
   constexpr uint32_t kOnes = DT == PKV_F16 ? 0x3C003C00u : 0x3F803F80u;
@@ -324,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     m_run[rb] = -1e30f;
+    m_thr[rb] = m_run[rb] + kSlack;
     lacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -403,11 +406,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
         for (int i = 0; i < 4; ++i) x[h * 4 + i] = sc[rb][h][i];
       }
       if (masked) {
+        // key e of the lane is token step kKeys + 4 grp + (e / 4) 16 + e % 4
+        const int d = pos[rb] - 4 * grp - step * kKeys;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = step * kKeys + (e >> 2) * 16 + 4 * grp + (e & 3);
-          x[e] = t <= pos[rb] ? x[e] : -INFINITY;
-        }
+        for (int e = 0; e < 8; ++e) x[e] = (e >> 2) * 16 + (e & 3) <= d ? x[e] : -INFINITY;
       }
       // The lane's own maximum decides whether its row's max may need
       // raising (the row's running max is the same in its four lanes); only
@@ -415,12 +417,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
       float mt = x[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      if (__builtin_amdgcn_ballot_w64(mt * c2 > m_run[rb] + kSlack)) {  // rescale some rows
+      if (__builtin_amdgcn_ballot_w64(mt * c2 > m_thr[rb])) {  // rescale some rows
         const float m_tile = max4rows(mt) * c2;
-        const bool grow = m_tile > m_run[rb] + kSlack;
+        const bool grow = m_tile > m_thr[rb];
         const float m_new = grow ? m_tile : m_run[rb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         m_run[rb] = m_new;
+        m_thr[rb] = m_new + kSlack;
         lacc[rb] *= alpha;
 #pragma unroll
         for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
@@ -492,8 +495,12 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
 }
 
 template <int DT, int D>
-static hipError_t launch(const Params& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((paged_prefill_kernel<DT, D>), dim3(grid), dim3(kThreads), 0, st, a);
+static hipError_t launch(const Params& a, bool neg, unsigned grid, hipStream_t st) {
+  if (neg)
+    hipLaunchKernelGGL((paged_prefill_kernel<DT, D, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((paged_prefill_kernel<DT, D, false>), dim3(grid), dim3(kThreads), 0, st,
+                       a);
   return hipGetLastError();
 }
 
@@ -517,6 +524,7 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
       num_blocks <= 0 || num_blocks > INT32_MAX || max_query_len < 0)
     return PKV_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!(fabsf(scale) <= 3.402823466e38f)) return PKV_ERR_INVALID_ARG;  // NaN, +-inf
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   if (head_size != 64 && head_size != 128) return PKV_ERR_UNSUPPORTED;
@@ -544,7 +552,13 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // exp(x) = 2^(x log2 e).  The kernel takes the scale's magnitude and its
+  // sign apart (a negative scale flips the queries' signs); a zero scale is
+  // taken as 1e-30, which weighs the visible tokens equally to float32
+  // precision as zero does, while a masked score, -inf, still scales to -inf.
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const bool neg = scale_log2 < 0.f;
+  a.scale_log2 = fmaxf(fabsf(scale_log2), 1e-30f);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -556,10 +570,10 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dtype == PKV_F16)
-    e = head_size == 64 ? launch<PKV_F16, 64>(a, (unsigned)grid, st)
-                        : launch<PKV_F16, 128>(a, (unsigned)grid, st);
+    e = head_size == 64 ? launch<PKV_F16, 64>(a, neg, (unsigned)grid, st)
+                        : launch<PKV_F16, 128>(a, neg, (unsigned)grid, st);
   else
-    e = head_size == 64 ? launch<PKV_BF16, 64>(a, (unsigned)grid, st)
-                        : launch<PKV_BF16, 128>(a, (unsigned)grid, st);
+    e = head_size == 64 ? launch<PKV_BF16, 64>(a, neg, (unsigned)grid, st)
+                        : launch<PKV_BF16, 128>(a, neg, (unsigned)grid, st);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -224,21 +224,23 @@ def sample_seqs(lens, k=3, seed=7):
     return sorted(pick)
 
 
-def run_prefill(b, out=None):
+def run_prefill(b, out=None, scale=None):
     w = b["workload"]
     out = torch.empty_like(b["query"]) if out is None else out
+    scale = float(w.scale) if scale is None else float(scale)
     pkv.paged_attention_prefill(out, b["query"], b["key_cache"], b["value_cache"],
                                 dev_i32(b["block_tables"]), dev_i32(b["context_lens"]),
-                                dev_i32(b["query_start_loc"]), float(w.scale), w.num_kv_heads,
+                                dev_i32(b["query_start_loc"]), scale, w.num_kv_heads,
                                 w.max_query_len, validate=True)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_prefill_subset(b, kc_before, vc_before, seqs):
+def oracle_prefill_subset(b, kc_before, vc_before, seqs, scale=None):
     """Oracle rows of the chosen sequences (their chunks, packed in order),
     after replaying the step's cache writes on host copies of the pools."""
     w = b["workload"]
+    scale = w.scale if scale is None else np.float32(scale)
     ids = blocks_read_by(b, seqs)
     if len(ids) == 0:
         ids = np.zeros(1, np.int64)
@@ -252,6 +254,6 @@ def oracle_prefill_subset(b, kc_before, vc_before, seqs):
     rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs]).astype(np.int64)
     sub_qsl = np.concatenate([[0], np.cumsum([qsl[s + 1] - qsl[s] for s in seqs])])
     q = wl.to_host(b["query"])[rows]
-    ref = oracle.prefill_attention(q, kc, vc, tables, lens, sub_qsl, w.scale, w.num_kv_heads,
+    ref = oracle.prefill_attention(q, kc, vc, tables, lens, sub_qsl, scale, w.num_kv_heads,
                                    w.dtype)
     return rows, ref

@@ -295,6 +295,8 @@ def test_prefill_argument_validation(lib):
     assert prefill(lib, D=96) == UNSUPPORTED
     assert prefill(lib, query=FAKE + 8) == INVALID        # 16-byte loads
     assert prefill(lib, out=FAKE + 4) == INVALID          # 8-byte stores
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert prefill(lib, scale=bad) == INVALID         # the scale must be finite
     assert prefill(lib, S=0) == OK                        # nothing to do: no launch
     assert prefill(lib, mq=0) == OK
 

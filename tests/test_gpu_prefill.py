@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 W = wl.WORKLOADS
 
 
-def prefill_step_and_check(b, seqs=None):
+def prefill_step_and_check(b, seqs=None, scale=None):
     w = b["workload"]
     kc0, vc0 = clone_pools(b)
     run_pool_updates(b)
@@ -37,9 +37,9 @@ def prefill_step_and_check(b, seqs=None):
         ek, ev, _ = oracle_pool(b, kc0, vc0, touched)
         assert gather_blocks(b["key_cache"], touched).tobytes() == ek.tobytes()
         assert gather_blocks(b["value_cache"], touched).tobytes() == ev.tobytes()
-    out = run_prefill(b)
+    out = run_prefill(b, scale=scale)
     seqs = list(range(w.num_seqs)) if seqs is None else seqs
-    rows, ref = oracle_prefill_subset(b, kc0, vc0, seqs)
+    rows, ref = oracle_prefill_subset(b, kc0, vc0, seqs, scale=scale)
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, w.dtype,
                  f"prefill {w.key} seqs={len(seqs)} rows={len(rows)}")
     return out
@@ -85,6 +85,17 @@ def test_prefill_head_grouping_and_types(gpu_lib, dtype, d, hq, hkv):
     w = wl.custom_prefill(prefixes, chunks, hq, hkv, d, dtype)
     b = wl.make_batch(w, int(rng.integers(1 << 30)), DEV)
     prefill_step_and_check(b)
+
+
+@pytest.mark.parametrize("scale", [-0.125, -0.0883883, 0.0])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_any_softmax_scale(gpu_lib, dtype, scale):
+    """The softmax scale is any float: a negative one turns each row's
+    largest logit into its smallest score (the kernel carries the sign in
+    the queries), and zero weighs the visible tokens equally."""
+    w = wl.custom_prefill([0, 37, 130], [45, 20, 70], 8, 2, 128, dtype)
+    b = wl.make_batch(w, 5, DEV)
+    prefill_step_and_check(b, scale=scale)
 
 
 def test_prefill_edge_cases(gpu_lib):
