@@ -84,6 +84,10 @@ constexpr int kMinBundle = 4;
 // than this (log2 units); probabilities then stay below 2^kSlack and the
 // accumulator is rescaled rarely.
 constexpr float kSlack = 8.f;
+// Waves per SIMD: three workgroups per CU (168 VGPRs; 3 x 48 KiB of LDS at
+// D = 128).  Measured on one MI355X: 3-5% faster than two, with the value
+// reads split in halves to fit.
+constexpr int kWavesPerSimd = 3;
 
 // LDS: three buffers of K [32 tokens][D] and V [32 tokens][D], rows
 // unpadded.  Within a row, the pool row's 16-B chunk c sits at chunk
@@ -139,7 +143,7 @@ struct Phase {
 };
 
 template <int DT, int D, bool kNeg>
-__global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(const Params p) {
   using LD = Lds<D>;
   constexpr int NKS = D / 32;                    // QK k-steps of 32 dims
   constexpr int NDB = D / 16;                    // output blocks of 16 dims
@@ -347,50 +351,48 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     const char* kb = lds_k + bcur * LD::kBuf;
     const char* vb = lds_v + bcur * LD::kBuf;
 
-    // S^T for both key blocks and both row blocks: all key operands are
-    // read from LDS first, so their latencies overlap
-    u32x4 ka[2][NKS];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = h * 16 + col;
-#pragma unroll
-      for (int m = 0; m < NKS; ++m)
-        ka[h][m] = load16(kb + r * LD::kRowB + ((4 * m + grp) ^ LD::kswz(r)) * 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // S^T for both key blocks and both row blocks, one key block's
+    // operands (read from LDS together) at a time
     floatx4 sc[kRB][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      u32x4 ka[NKS];
+      const int r = h * 16 + col;
+#pragma unroll
+      for (int m = 0; m < NKS; ++m)
+        ka[m] = load16(kb + r * LD::kRowB + ((4 * m + grp) ^ LD::kswz(r)) * 16);
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < NKS; ++m) {
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = mfma32<DT>(ka[h][m], q[rb][m], sc[rb][h]);
+        for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = mfma32<DT>(ka[m], q[rb][m], sc[rb][h]);
       }
     }
 
-    // the value operands of this step, read transposed while the softmax
-    // runs: lane l gets dim 16j + l % 16 of tokens 4(l/16) + 0..3 of each
-    // block (the probabilities' k order)
+    // The value operands, read transposed: lane l gets dim 16j + l % 16 of
+    // tokens 4(l/16) + 0..3 of each block (the probabilities' k order).
+    // Dim block j = jl + kT jh sits at chunk 2 (jl ^ t) + 2 kT jh (+1 for
+    // the lane's upper 8 dims): kT lane addresses, the rest offsets; the
+    // second block's rows (16 on) have the same swizzle.  The first half is
+    // read while the softmax runs, the second after the first half's
+    // products (the registers of both halves at once would not leave room
+    // for three waves per SIMD).
     u32x4 va[NDB];
-    {
-      // dim block j = jl + kT jh sits at chunk 2 (jl ^ t) + 2 kT jh (+1 for
-      // the lane's upper 8 dims): kT lane addresses, the rest offsets; the
-      // second block's rows (16 on) have the same swizzle
-      constexpr int kT = 4 / LD::kRowsPer256;  // distinct swizzles of the rows
-      static_assert(NDB % kT == 0, "dim blocks in whole swizzle periods");
-      const int r0 = 4 * grp + (col >> 2);
-      const int t = LD::vswz(r0) / 2;
-      const char* vrow = vb + r0 * LD::kRowB + (col & 1) * 8 + ((col & 3) >> 1) * 16;
+    constexpr int kT = 4 / LD::kRowsPer256;  // distinct swizzles of the rows
+    static_assert(NDB % kT == 0 && NDB % 2 == 0, "dim blocks in whole swizzle periods");
+    const int r0 = 4 * grp + (col >> 2);
+    const char* vrow =
+        vb + r0 * LD::kRowB + (col & 1) * 8 + ((col & 3) >> 1) * 16;
+    const int vt = LD::vswz(r0) / 2;
+    auto read_v = [&](int j) __attribute__((always_inline)) {
+      const char* a = vrow + 32 * ((j % kT) ^ vt) + 32 * kT * (j / kT);
+      const uint2 lo = read_tr16(a);
+      const uint2 hi = read_tr16(a + 16 * LD::kRowB);
+      va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
 #pragma unroll
-      for (int j = 0; j < NDB; ++j) {
-        const char* a = vrow + 32 * ((j % kT) ^ t) + 32 * kT * (j / kT);
-        const uint2 lo = read_tr16(a);
-        const uint2 hi = read_tr16(a + 16 * LD::kRowB);
-        va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-    }
+    for (int j = 0; j < NDB / 2; ++j) read_v(j);
     __builtin_amdgcn_sched_barrier(0);
 
     // online softmax per row; probabilities packed as the B operand of PV.
@@ -438,6 +440,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(const Params
     // O^T += V^T P^T, one 16-dim block at a time
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
+      if (j == NDB / 2) {
+#pragma unroll
+        for (int jj = NDB / 2; jj < NDB; ++jj) read_v(jj);
+      }
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
     }
