@@ -142,6 +142,19 @@ struct Phase {
   static constexpr int value = P;
 };
 
+// Whether any of the eight 16-bit values of a 16-B chunk is an infinity or
+// NaN: a value's exponent field plus its lowest bit carries into the
+// value's top bit exactly when the field is all ones.
+template <int DT>
+__device__ __forceinline__ bool nonfinite_any(u32x4 v) {
+  constexpr uint32_t kExp = DT == PKV_BF16 ? 0x7F807F80u : 0x7C007C00u;
+  constexpr uint32_t kLow = DT == PKV_BF16 ? 0x00800080u : 0x04000400u;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c |= (v[i] & kExp) + kLow;
+  return (c & 0x80008000u) != 0;
+}
+
 template <int DT, int D, bool kNeg>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(const Params p) {
   using LD = Lds<D>;
@@ -284,25 +297,34 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   // not see such a key are then exact; rows that see a non-finite value
   // there get that largest value in its place.
   const int wg_pos0 = base + R0 / G;  // position of the workgroup's earliest row
+  // The test for a non-finite value comes first (a few instructions); the
+  // clamp and its write run only where one was found.
   auto fixup = [&](int buf, int step) __attribute__((always_inline)) {
-    if (step * kKeys + kKeys - 1 <= wg_pos0) return;
+    const bool edge = step * kKeys + kKeys - 1 > wg_pos0;  // uniform
+    const bool tail = step * kKeys + kKeys > Lc;           // uniform
+    if (!edge && !tail) return;
 #pragma unroll
     for (int u = 0; u < kDma; ++u) {
       const int kib = w * kDma + u;
       const int t = step * kKeys + row_w0 + u * kRowsPerKiB + lane / CPR;
       char* ks = lds_k + buf * LD::kBuf + kib * 1024 + lane * 16;
       char* vs = lds_v + buf * LD::kBuf + kib * 1024 + lane * 16;
-      u32x4 kv = *reinterpret_cast<const u32x4*>(ks);
-      u32x4 vv = *reinterpret_cast<const u32x4*>(vs);
-      if (t > wg_pos0) {
+      if (edge) {
+        u32x4 vv = *reinterpret_cast<const u32x4*>(vs);
+        const bool bad = nonfinite_any<DT>(vv) && t > wg_pos0;
+        if (__builtin_amdgcn_ballot_w64(bad)) {
+          if (bad) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = finite_pair<DT>(vv[i], true, true);
+            for (int i = 0; i < 4; ++i) vv[i] = finite_pair<DT>(vv[i], true, true);
+            *reinterpret_cast<u32x4*>(vs) = vv;
+          }
+        }
       }
-      const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-      kv = t >= Lc ? zero : kv;
-      vv = t >= Lc ? zero : vv;
-      *reinterpret_cast<u32x4*>(ks) = kv;
-      *reinterpret_cast<u32x4*>(vs) = vv;
+      if (tail && t >= Lc) {
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(ks) = zero;
+        *reinterpret_cast<u32x4*>(vs) = zero;
+      }
     }
   };
   // Waits written out, so that no memory access moves across them: a
