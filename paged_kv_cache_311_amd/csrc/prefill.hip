@@ -349,6 +349,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   const u32x4 ones = u32x4{kOnes, kOnes, kOnes, kOnes};
   const float c2 = p.scale_log2;
   const int wave_pos0 = base + min(R0 + w * kRB * 16, rows - 1) / G;  // earliest row of the wave
+  // the wave's latest row: steps that start past it are masked for all its
+  // rows, and the wave only takes its part in their loads
+  const int wave_pos1 = base + min(R0 + (w + 1) * kRB * 16 - 1, rows - 1) / G;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     m_run[rb] = -1e30f;
@@ -370,107 +373,109 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     constexpr int bfar = (bcur + 2) % 3;
     const int id_nn = read_id(step + 3);
     dma(id_n, bfar);
-    const char* kb = lds_k + bcur * LD::kBuf;
-    const char* vb = lds_v + bcur * LD::kBuf;
+    if (step * kKeys <= wave_pos1) {
+      const char* kb = lds_k + bcur * LD::kBuf;
+      const char* vb = lds_v + bcur * LD::kBuf;
 
-    // S^T for both key blocks and both row blocks, one key block's
-    // operands (read from LDS together) at a time
-    floatx4 sc[kRB][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 ka[NKS];
-      const int r = h * 16 + col;
-#pragma unroll
-      for (int m = 0; m < NKS; ++m)
-        ka[m] = load16(kb + r * LD::kRowB + ((4 * m + grp) ^ LD::kswz(r)) * 16);
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < NKS; ++m) {
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = mfma32<DT>(ka[m], q[rb][m], sc[rb][h]);
-      }
-    }
-
-    // The value operands, read transposed: lane l gets dim 16j + l % 16 of
-    // tokens 4(l/16) + 0..3 of each block (the probabilities' k order).
-    // Dim block j = jl + kT jh sits at chunk 2 (jl ^ t) + 2 kT jh (+1 for
-    // the lane's upper 8 dims): kT lane addresses, the rest offsets; the
-    // second block's rows (16 on) have the same swizzle.  The first half is
-    // read while the softmax runs, the second after the first half's
-    // products (the registers of both halves at once would not leave room
-    // for three waves per SIMD).
-    u32x4 va[NDB];
-    constexpr int kT = 4 / LD::kRowsPer256;  // distinct swizzles of the rows
-    static_assert(NDB % kT == 0 && NDB % 2 == 0, "dim blocks in whole swizzle periods");
-    const int r0 = 4 * grp + (col >> 2);
-    const char* vrow =
-        vb + r0 * LD::kRowB + (col & 1) * 8 + ((col & 3) >> 1) * 16;
-    const int vt = LD::vswz(r0) / 2;
-    auto read_v = [&](int j) __attribute__((always_inline)) {
-      const char* a = vrow + 32 * ((j % kT) ^ vt) + 32 * kT * (j / kT);
-      const uint2 lo = read_tr16(a);
-      const uint2 hi = read_tr16(a + 16 * LD::kRowB);
-      va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-    };
-#pragma unroll
-    for (int j = 0; j < NDB / 2; ++j) read_v(j);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // online softmax per row; probabilities packed as the B operand of PV.
-    // Steps that end at or before the wave's earliest row need no mask.
-    const bool masked = step * kKeys + kKeys - 1 > wave_pos0;
-    u32x4 pb[kRB];
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      float x[8];
+      // S^T for both key blocks and both row blocks, one key block's
+      // operands (read from LDS together) at a time
+      floatx4 sc[kRB][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        u32x4 ka[NKS];
+        const int r = h * 16 + col;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[h * 4 + i] = sc[rb][h][i];
+        for (int m = 0; m < NKS; ++m)
+          ka[m] = load16(kb + r * LD::kRowB + ((4 * m + grp) ^ LD::kswz(r)) * 16);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NKS; ++m) {
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) sc[rb][h] = mfma32<DT>(ka[m], q[rb][m], sc[rb][h]);
+        }
       }
-      if (masked) {
-        // key e of the lane is token step kKeys + 4 grp + (e / 4) 16 + e % 4
-        const int d = pos[rb] - 4 * grp - step * kKeys;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (e >> 2) * 16 + (e & 3) <= d ? x[e] : -INFINITY;
-      }
-      // The lane's own maximum decides whether its row's max may need
-      // raising (the row's running max is the same in its four lanes); only
-      // then is the row's maximum taken across them.
-      float mt = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      if (__builtin_amdgcn_ballot_w64(mt * c2 > m_thr[rb])) {  // rescale some rows
-        const float m_tile = max4rows(mt) * c2;
-        const bool grow = m_tile > m_thr[rb];
-        const float m_new = grow ? m_tile : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        m_run[rb] = m_new;
-        m_thr[rb] = m_new + kSlack;
-        lacc[rb] *= alpha;
-#pragma unroll
-        for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
-      }
-      float pe[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_run[rb]));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pb[rb][e] = pack2<DT>(pe[2 * e], pe[2 * e + 1]);
-    }
 
-    // O^T += V^T P^T, one 16-dim block at a time
+      // The value operands, read transposed: lane l gets dim 16j + l % 16 of
+      // tokens 4(l/16) + 0..3 of each block (the probabilities' k order).
+      // Dim block j = jl + kT jh sits at chunk 2 (jl ^ t) + 2 kT jh (+1 for
+      // the lane's upper 8 dims): kT lane addresses, the rest offsets; the
+      // second block's rows (16 on) have the same swizzle.  The first half is
+      // read while the softmax runs, the second after the first half's
+      // products (the registers of both halves at once would not leave room
+      // for three waves per SIMD).
+      u32x4 va[NDB];
+      constexpr int kT = 4 / LD::kRowsPer256;  // distinct swizzles of the rows
+      static_assert(NDB % kT == 0 && NDB % 2 == 0, "dim blocks in whole swizzle periods");
+      const int r0 = 4 * grp + (col >> 2);
+      const char* vrow =
+          vb + r0 * LD::kRowB + (col & 1) * 8 + ((col & 3) >> 1) * 16;
+      const int vt = LD::vswz(r0) / 2;
+      auto read_v = [&](int j) __attribute__((always_inline)) {
+        const char* a = vrow + 32 * ((j % kT) ^ vt) + 32 * kT * (j / kT);
+        const uint2 lo = read_tr16(a);
+        const uint2 hi = read_tr16(a + 16 * LD::kRowB);
+        va[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      };
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) {
-      if (j == NDB / 2) {
+      for (int j = 0; j < NDB / 2; ++j) read_v(j);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // online softmax per row; probabilities packed as the B operand of PV.
+      // Steps that end at or before the wave's earliest row need no mask.
+      const bool masked = step * kKeys + kKeys - 1 > wave_pos0;
+      u32x4 pb[kRB];
 #pragma unroll
-        for (int jj = NDB / 2; jj < NDB; ++jj) read_v(jj);
+      for (int rb = 0; rb < kRB; ++rb) {
+        float x[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[h * 4 + i] = sc[rb][h][i];
+        }
+        if (masked) {
+          // key e of the lane is token step kKeys + 4 grp + (e / 4) 16 + e % 4
+          const int d = pos[rb] - 4 * grp - step * kKeys;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (e >> 2) * 16 + (e & 3) <= d ? x[e] : -INFINITY;
+        }
+        // The lane's own maximum decides whether its row's max may need
+        // raising (the row's running max is the same in its four lanes); only
+        // then is the row's maximum taken across them.
+        float mt = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+        if (__builtin_amdgcn_ballot_w64(mt * c2 > m_thr[rb])) {  // rescale some rows
+          const float m_tile = max4rows(mt) * c2;
+          const bool grow = m_tile > m_thr[rb];
+          const float m_new = grow ? m_tile : m_run[rb];
+          const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          m_run[rb] = m_new;
+          m_thr[rb] = m_new + kSlack;
+          lacc[rb] *= alpha;
+#pragma unroll
+          for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
+        }
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c2, -m_run[rb]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pb[rb][e] = pack2<DT>(pe[2 * e], pe[2 * e + 1]);
+      }
+
+      // O^T += V^T P^T, one 16-dim block at a time
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) {
+        if (j == NDB / 2) {
+#pragma unroll
+          for (int jj = NDB / 2; jj < NDB; ++jj) read_v(jj);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
       }
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
+      for (int rb = 0; rb < kRB; ++rb) lacc[rb] = mfma32<DT>(ones, pb[rb], lacc[rb]);
     }
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) lacc[rb] = mfma32<DT>(ones, pb[rb], lacc[rb]);
 
     // step + 1's tiles have landed (step + 2's, issued after them, stay in
     // flight); made safe where needed, then published
