@@ -88,6 +88,9 @@ constexpr float kSlack = 8.f;
 // D = 128).  Measured on one MI355X: 3-5% faster than two, with the value
 // reads split in halves to fit.
 constexpr int kWavesPerSimd = 3;
+// Batches of up to this many sequences are dealt heaviest first (each
+// workgroup ranks the sequences itself: a loop over them per thread).
+constexpr int kMaxSortSeqs = 256;
 
 // LDS: three buffers of K [32 tokens][D] and V [32 tokens][D], rows
 // unpadded.  Within a row, the pool row's 16-B chunk c sits at chunk
@@ -118,6 +121,7 @@ struct Params {
   int64_t num_blocks;
   int row_tiles;     // 128-row tiles per (sequence, kv head) the grid covers
   int bundle;        // (sequence, kv head) pairs interleaved on an XCD
+  int sort_seqs;     // deal the pairs in the order of their sequences' work
 };
 
 
@@ -134,6 +138,37 @@ __device__ __forceinline__ uint32_t finite_pair(uint32_t w, bool lo, bool hi) {
   const uint32_t fa = (a & kExp) == kExp ? ((nan_a ? 0u : (a & 0x8000u)) | kMax) : a;
   const uint32_t fb = (b & kExp) == kExp ? ((nan_b ? 0u : (b & 0x8000u)) | kMax) : b;
   return (lo ? fa : a) | ((hi ? fb : b) << 16);
+}
+
+// The sequence of rank r when the sequences are ordered by their work
+// (new tokens x average keys they see, heaviest first; ties by index).
+// Every thread of the workgroup takes part; `scratch` (LDS) holds
+// num_seqs floats and an int, and is free again on return.
+__device__ __forceinline__ int seq_of_rank(const Params& p, int r, char* scratch) {
+  float* wk = reinterpret_cast<float*>(scratch);
+  int* pick = reinterpret_cast<int*>(scratch + ((p.num_seqs * 4 + 15) & ~15));
+  const int max_tokens = p.max_blocks * kBlockSize;
+  for (int t = threadIdx.x; t < p.num_seqs; t += kThreads) {
+    const int n = p.query_start_loc[t + 1] - p.query_start_loc[t];
+    int L = p.context_lens[t];
+    L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
+    const float nn = (float)(n > 0 ? n : 0);
+    wk[t] = nn * (2.f * (float)L - nn);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < p.num_seqs; t += kThreads) {
+    const float wt = wk[t];
+    int rank = 0;
+    for (int u = 0; u < p.num_seqs; ++u) {
+      const float wu = wk[u];
+      rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
+    }
+    if (rank == r) *pick = t;
+  }
+  __syncthreads();
+  const int s = *pick;
+  __syncthreads();
+  return s;
 }
 
 // a buffer index as a type (for the unrolled copies of a step)
@@ -168,7 +203,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   // On an XCD, its pairs are taken `bundle` at a time, and within a bundle
   // the row tiles go out latest (heaviest) first across its pairs: the
   // tiles that run together share their keys and values in that XCD's L2,
-  // and the longest ones start first.
+  // and the longest ones start first.  With sort_seqs, the pairs are dealt
+  // in the order of their sequences' work, heaviest first, so the longest
+  // workgroups of the whole grid start first (a batch of prompts of mixed
+  // lengths otherwise ends on a tail of long workgroups).
   const int xcd = blockIdx.x & (kXcds - 1);
   const int k = blockIdx.x / kXcds;
   const int per_bundle = p.bundle * p.row_tiles;
@@ -177,8 +215,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   const int rank = in_b / p.bundle;
   const int sg = ((bdl * p.bundle + (in_b - rank * p.bundle)) * kXcds) + xcd;
   if (sg >= p.num_seqs * p.num_kv_heads) return;  // padding of the grid
-  const int s = sg / p.num_kv_heads;
-  const int g = sg - s * p.num_kv_heads;
+  const int vs = sg / p.num_kv_heads;  // the sequence's place in the dealing order
+  const int g = sg - vs * p.num_kv_heads;
+  const int s = p.sort_seqs ? seq_of_rank(p, vs, lds) : vs;
   const int tile = p.row_tiles - 1 - rank;
 
   const int G = p.num_heads / p.num_kv_heads;
@@ -599,6 +638,7 @@ extern "C" int paged_attention_prefill(void* out, const void* query, const void*
   a.num_blocks = num_blocks;
   a.row_tiles = (int)row_tiles;
   a.bundle = (int)bundle;
+  a.sort_seqs = num_seqs <= kMaxSortSeqs ? 1 : 0;
   (void)hipGetLastError();
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
