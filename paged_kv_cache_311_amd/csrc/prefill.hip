@@ -45,9 +45,10 @@
 //                lane and 16-dim block.
 //                Lane l holds output dims 16j + 4(l/16) .. +3 of row
 //                l % 16, so the rescale by the row's running max and the
-//                final 1/sum are lane-local.  One more product per row
-//                block, of a block of ones with P^T, gives every lane its
-//                row's sum of the probabilities (no VALU sums).
+//                final 1/sum are lane-local.  Each lane sums its own 8
+//                probabilities of the row as packed (two-term dot products
+//                with ones, into float32), and the row's 4 lanes add their
+//                parts once, at the end.
 //   Masking selects only on the steps that reach past a wave's earliest
 //   row.  A row's max is raised only when a step's exceeds it by 2^8 (so
 //   probabilities stay below 256) and the rescale then runs for the wave;
@@ -169,6 +170,19 @@ __device__ __forceinline__ int seq_of_rank(const Params& p, int r, char* scratch
   const int s = *pick;
   __syncthreads();
   return s;
+}
+
+// c + the two 16-bit values of w (float32 sum)
+template <int DT>
+__device__ __forceinline__ float dot2_ones(uint32_t w, float c) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == PKV_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3C003C00u), c,
+                                  false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                           __builtin_bit_cast(b2, 0x3F803F80u), c, false);
 }
 
 // a buffer index as a type (for the unrolled copies of a step)
@@ -383,9 +397,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   float m_run[kRB];
   float m_thr[kRB];  // m_run + kSlack
   floatx4 acc[kRB][NDB];
-  floatx4 lacc[kRB];  // row sums: the product of a block of ones with P^T
-  constexpr uint32_t kOnes = DT == PKV_F16 ? 0x3C003C00u : 0x3F803F80u;
-  const u32x4 ones = u32x4{kOnes, kOnes, kOnes, kOnes};
+  float lsum[kRB];  // the lane's part of its row's sum of probabilities
   const float c2 = p.scale_log2;
   const int wave_pos0 = base + min(R0 + w * kRB * 16, rows - 1) / G;  // earliest row of the wave
   // the wave's latest row: steps that start past it are masked for all its
@@ -395,7 +407,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   for (int rb = 0; rb < kRB; ++rb) {
     m_run[rb] = -1e30f;
     m_thr[rb] = m_run[rb] + kSlack;
-    lacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    lsum[rb] = 0.f;
 #pragma unroll
     for (int j = 0; j < NDB; ++j) acc[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
           const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
           m_run[rb] = m_new;
           m_thr[rb] = m_new + kSlack;
-          lacc[rb] *= alpha;
+          lsum[rb] *= alpha;
 #pragma unroll
           for (int j = 0; j < NDB; ++j) acc[rb][j] *= alpha;
         }
@@ -513,7 +525,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         for (int rb = 0; rb < kRB; ++rb) acc[rb][j] = mfma32<DT>(va[j], pb[rb], acc[rb][j]);
       }
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) lacc[rb] = mfma32<DT>(ones, pb[rb], lacc[rb]);
+      for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lsum[rb] = dot2_ones<DT>(pb[rb][e], lsum[rb]);
+      }
     }
 
     // step + 1's tiles have landed (step + 2's, issued after them, stay in
@@ -551,7 +566,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   // normalize and store: lane l holds dims 16j + 4(l/16) .. +3 of its row
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const float l = lacc[rb][0];
+    const float l = sum4rows(lsum[rb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (row_ok[rb]) {
       char* dst = (char*)p.out + (row_off[rb] + 4 * grp) * 2;
