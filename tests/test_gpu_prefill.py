@@ -88,14 +88,33 @@ def test_prefill_head_grouping_and_types(gpu_lib, dtype, d, hq, hkv):
 
 
 @pytest.mark.parametrize("scale", [-0.125, -0.0883883, 0.0])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_prefill_any_softmax_scale(gpu_lib, dtype, scale):
+def test_prefill_any_softmax_scale(gpu_lib, dtype, d, scale):
     """The softmax scale is any float: a negative one turns each row's
     largest logit into its smallest score (the kernel carries the sign in
     the queries), and zero weighs the visible tokens equally."""
-    w = wl.custom_prefill([0, 37, 130], [45, 20, 70], 8, 2, 128, dtype)
+    w = wl.custom_prefill([0, 37, 130], [45, 20, 70], 8, 2, d, dtype)
     b = wl.make_batch(w, 5, DEV)
     prefill_step_and_check(b, scale=scale)
+
+
+@pytest.mark.parametrize("num_seqs", [200, 300])
+def test_prefill_many_sequences_both_dealing_orders(gpu_lib, num_seqs):
+    """Batches of up to 256 sequences are dealt heaviest sequence first (each
+    workgroup ranks the sequences), larger ones in index order; mixed
+    lengths, ties among them, empty chunks and whole prompts, every output
+    against the oracle, on both sides of that bound."""
+    rng = np.random.default_rng(num_seqs)
+    prefixes = rng.integers(0, 48, size=num_seqs)
+    chunks = rng.integers(0, 9, size=num_seqs)
+    prefixes[::7] = 0          # whole prompts
+    chunks[::11] = 0           # nothing new
+    prefixes[1::13] = 20       # equal work: ties broken by index
+    chunks[1::13] = 5
+    w = wl.custom_prefill(prefixes, chunks, 4, 2, 64, "f16")
+    b = wl.make_batch(w, num_seqs + 1, DEV)
+    prefill_step_and_check(b)
 
 
 def test_prefill_edge_cases(gpu_lib):
