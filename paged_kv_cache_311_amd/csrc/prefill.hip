@@ -382,11 +382,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   };
   // Waits written out, so that no memory access moves across them: a
   // step's tiles have landed while the 2 kDma loads of the next step's
-  // (issued after them) stay in flight.  A step's LDS writes are then
+  // (issued after them) stay in flight; where no later loads were issued
+  // (the last steps), all loads have landed.  A step's LDS writes are then
   // published by a barrier (lgkmcnt(0) first: this wave's LDS operations
   // done).
   auto wait_tiles = []() __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDma) : "memory");
+  };
+  auto wait_loads = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
   auto publish = []() __attribute__((always_inline)) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -423,7 +427,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     constexpr int bnxt = (bcur + 1) % 3;
     constexpr int bfar = (bcur + 2) % 3;
     const int id_nn = read_id(step + 3);
-    dma(id_n, bfar);
+    // (no loads for steps past the last: a wave would wait for them before
+    // it ends, and its workgroup's slot would stay taken meanwhile)
+    const bool issue = step + 2 < nsteps;
+    if (issue) dma(id_n, bfar);
     if (step * kKeys <= wave_pos1) {
       const char* kb = lds_k + bcur * LD::kBuf;
       const char* vb = lds_v + bcur * LD::kBuf;
@@ -534,7 +541,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     // step + 1's tiles have landed (step + 2's, issued after them, stay in
     // flight); made safe where needed, then published
     __builtin_amdgcn_sched_barrier(0);
-    wait_tiles();
+    if (issue)
+      wait_tiles();
+    else
+      wait_loads();  // nothing issued after step + 1's tiles
     fixup(bnxt, step + 1);
     id_n = id_nn;
     publish();
@@ -546,8 +556,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     const int id1 = read_id(1);
     dma(id0, 0);
     id_n = read_id(2);
-    dma(id1, 1);
-    wait_tiles();
+    if (nsteps > 1) {
+      dma(id1, 1);
+      wait_tiles();
+    } else {
+      wait_loads();
+    }
     fixup(0, 0);
   }
   // the queries have arrived (a wait the compiler sees, on either path, so
