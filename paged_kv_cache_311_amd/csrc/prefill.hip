@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   // rows of one pool block, lane l taking the LDS slot l (row l / CPR of the
   // KiB, chunk l % CPR) and reading the pool chunk the swizzle puts there.
   // A wave's KiBs of a step lie in one pool block, so it needs one block id
-  // per step (read from the table with a vector load a step before use).
+  // per step (read from the table with a scalar load a step before use).
   constexpr int kTileBytes = kBlockSize * D * 2;
   constexpr int kRowsPerKiB = 1024 / LD::kRowB;
   constexpr int kDma = kKeys * LD::kRowB / 1024 / kWaves;  // KiBs per wave per tensor
