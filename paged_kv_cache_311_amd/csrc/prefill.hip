@@ -89,12 +89,11 @@ constexpr float kSlack = 8.f;
 // D = 128).  Measured on one MI355X: 3-5% faster than two, with the value
 // reads split in halves to fit.
 constexpr int kWavesPerSimd = 3;
-// Batches of up to this many sequences are dealt heaviest first (each
-// workgroup, empty ones too, ranks the sequences itself: a loop over them
-// per thread, after a round trip for their lengths).  Measured on one
-// MI355X: 16 sequences of mixed prefixes 4% faster; 64 sequences 1%, 128
-// 15% and 256 8-21% slower than dealing in index order.
+// Batches of up to this many sequences are dealt heaviest first (each wave
+// of each workgroup, empty ones too, ranks the sequences itself, a lane per
+// sequence; the loop over them is the cost).
 constexpr int kMaxSortSeqs = 32;
+static_assert(kMaxSortSeqs <= kWave, "a lane per sequence");
 
 // LDS: three buffers of K [32 tokens][D] and V [32 tokens][D], rows
 // unpadded.  Within a row, the pool row's 16-B chunk c sits at chunk
@@ -144,35 +143,38 @@ __device__ __forceinline__ uint32_t finite_pair(uint32_t w, bool lo, bool hi) {
   return (lo ? fa : a) | ((hi ? fb : b) << 16);
 }
 
-// The sequence of rank r when the sequences are ordered by their work
-// (new tokens x average keys they see, heaviest first; ties by index).
-// Every thread of the workgroup takes part; `scratch` (LDS) holds
-// num_seqs floats and an int, and is free again on return.
-__device__ __forceinline__ int seq_of_rank(const Params& p, int r, char* scratch) {
-  float* wk = reinterpret_cast<float*>(scratch);
-  int* pick = reinterpret_cast<int*>(scratch + ((p.num_seqs * 4 + 15) & ~15));
+// A sequence's chunk: its first row, its new tokens, its context length.
+struct SeqInfo {
+  int s, q0, n, L;
+};
+
+// The sequence of rank r when the sequences are ordered by their work (new
+// tokens x average keys they see, heaviest first; ties by index), and its
+// chunk.  Each wave ranks on its own, lane t holding sequence t (at most
+// one wave's worth of sequences), so no LDS or barrier is involved, and
+// the chunk of the chosen sequence comes from the lane that loaded it.
+__device__ __forceinline__ SeqInfo seq_of_rank(const Params& p, int r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool in = lane < p.num_seqs;
+  int q0 = 0, n = 0, L = 0;
+  if (in) {
+    q0 = p.query_start_loc[lane];
+    n = p.query_start_loc[lane + 1] - q0;
+    L = p.context_lens[lane];
+  }
   const int max_tokens = p.max_blocks * kBlockSize;
-  for (int t = threadIdx.x; t < p.num_seqs; t += kThreads) {
-    const int n = p.query_start_loc[t + 1] - p.query_start_loc[t];
-    int L = p.context_lens[t];
-    L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
-    const float nn = (float)(n > 0 ? n : 0);
-    wk[t] = nn * (2.f * (float)L - nn);
+  const float nn = (float)(n > 0 ? n : 0);
+  const float lc = (float)(L < 0 ? 0 : (L > max_tokens ? max_tokens : L));
+  const float wt = nn * (2.f * lc - nn);
+  int rank = 0;
+  for (int u = 0; u < p.num_seqs; ++u) {
+    const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), u));
+    rank += (wu > wt || (wu == wt && u < lane)) ? 1 : 0;
   }
-  __syncthreads();
-  for (int t = threadIdx.x; t < p.num_seqs; t += kThreads) {
-    const float wt = wk[t];
-    int rank = 0;
-    for (int u = 0; u < p.num_seqs; ++u) {
-      const float wu = wk[u];
-      rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
-    }
-    if (rank == r) *pick = t;
-  }
-  __syncthreads();
-  const int s = *pick;
-  __syncthreads();
-  return s;
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(in && rank == r);
+  const int s = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  return SeqInfo{s, __builtin_amdgcn_readlane(q0, s), __builtin_amdgcn_readlane(n, s),
+                 __builtin_amdgcn_readlane(L, s)};
 }
 
 // c + the two 16-bit values of w (float32 sum)
@@ -234,17 +236,26 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
   if (sg >= p.num_seqs * p.num_kv_heads) return;  // padding of the grid
   const int vs = sg / p.num_kv_heads;  // the sequence's place in the dealing order
   const int g = sg - vs * p.num_kv_heads;
-  const int s = p.sort_seqs ? seq_of_rank(p, vs, lds) : vs;
+  SeqInfo si;
+  if (p.sort_seqs) {
+    si = seq_of_rank(p, vs);
+  } else {
+    si.s = vs;
+    si.q0 = p.query_start_loc[vs];
+    si.n = p.query_start_loc[vs + 1] - si.q0;
+    si.L = p.context_lens[vs];
+  }
+  const int s = si.s;
   const int tile = p.row_tiles - 1 - rank;
 
   const int G = p.num_heads / p.num_kv_heads;
-  const int q0 = p.query_start_loc[s];
-  const int n = p.query_start_loc[s + 1] - q0;
+  const int q0 = si.q0;
+  const int n = si.n;
   const int rows = n * G;
   const int R0 = tile * kRows;
   if (n <= 0 || R0 >= rows) return;  // uniform per workgroup
   const int max_tokens = p.max_blocks * kBlockSize;
-  int Lc = p.context_lens[s];
+  int Lc = si.L;
   Lc = Lc < 0 ? 0 : (Lc > max_tokens ? max_tokens : Lc);
   const int base = Lc - n;  // position of the chunk's first token
   const int last_row = min(rows - 1, R0 + kRows - 1);
