@@ -75,11 +75,12 @@ constexpr int kRB = 2;                      // 16-row blocks per wave
 constexpr int kRows = kWaves * kRB * 16;    // rows per workgroup
 constexpr int kKeys = 2 * kBlockSize;       // tokens per step (two pool blocks)
 constexpr int kXcds = 8;                    // accelerator dies (each with its own L2)
-// Pairs interleaved per XCD bundle: about 64 row tiles' worth, at least 4
+// Pairs interleaved per XCD bundle: about 32 row tiles' worth, at least 4
 // pairs (measured on one MI355X: 16 pairs of 4 tiles beat both a
-// one-pair-at-a-time order and a whole-XCD interleave by 13%; with 64 tiles
-// per pair, 4 pairs beat 1 by 7%).
-constexpr int kBundleTiles = 64;
+// one-pair-at-a-time order and a whole-XCD interleave by 13%; with three
+// waves per SIMD, 8 pairs of 4 tiles beat 16 by 3% and 4 or 6 pairs are
+// as fast; with 64 tiles per pair, 4 pairs beat 1 by 7% and 2 by 0.4%).
+constexpr int kBundleTiles = 32;
 constexpr int kMinBundle = 4;
 // A row's running max is raised only when a step's max exceeds it by more
 // than this (log2 units); probabilities then stay below 2^kSlack and the
