@@ -79,7 +79,8 @@ constexpr int kXcds = 8;                    // accelerator dies (each with its o
 // pairs (measured on one MI355X: 16 pairs of 4 tiles beat both a
 // one-pair-at-a-time order and a whole-XCD interleave by 13%; with three
 // waves per SIMD, 8 pairs of 4 tiles beat 16 by 3% and 4 or 6 pairs are
-// as fast; with 64 tiles per pair, 4 pairs beat 1 by 7% and 2 by 0.4%).
+// as fast; with 64 tiles per pair, 4 pairs beat 1 by 7%, 2 by 0.4% and 8
+// by 1.5%).
 constexpr int kBundleTiles = 32;
 constexpr int kMinBundle = 4;
 // A row's running max is raised only when a step's max exceeds it by more
