@@ -572,12 +572,14 @@ PREFILL_CASES = [
 def pin_prefill_torch(o):
     for seed, lens, news, Hq, Hkv, D, dt in PREFILL_CASES:
         c = prefill_case(seed, lens, news, Hq, Hkv, D, dt)
-        scale = np.float32(1.0 / math.sqrt(D))
-        got = run_prefill(o, c, scale)
-        ref = torch_causal(c, scale)
-        assert got.shape == ref.shape
-        err = np.abs(got - ref).max()
-        assert err <= 1e-12, (seed, err)
+        # the usual scale, a negative one and zero (equal weights over the
+        # visible tokens), each against torch's own float64 attention
+        for scale in (np.float32(1.0 / math.sqrt(D)), np.float32(-0.3), np.float32(0.0)):
+            got = run_prefill(o, c, scale)
+            ref = torch_causal(c, scale)
+            assert got.shape == ref.shape
+            err = np.abs(got - ref).max()
+            assert err <= 1e-12, (seed, float(scale), err)
 
 
 def pin_prefill_loops(o):
