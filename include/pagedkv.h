@@ -114,7 +114,9 @@ const char* pkv_build_id(void);
  *                 n >= ceil(L/16) are ignored (any value)
  *   context_lens  int32 [num_seqs]; values are clamped to
  *                 [0, 16*max_blocks_per_seq]
- *   scale         the softmax scale (typically 1/sqrt(head_size))
+ *   scale         the softmax scale (typically 1/sqrt(head_size); any finite
+ *                 float: a negative one weighs the smallest logits most,
+ *                 zero weighs the visible tokens equally)
  *   num_kv_heads  kv heads; num_heads must be a multiple of it
  *   num_blocks    pool size in blocks; block ids outside [0, num_blocks)
  *                 are clamped into it (wrong output, no fault)

@@ -33,17 +33,18 @@ def dev_i64(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(DEV)
 
 
-def run_decode(b, partition_size=None, out=None, flags="batch"):
+def run_decode(b, partition_size=None, out=None, flags="batch", scale=None):
     """The decode call on a batch; `flags`: "batch" passes the batch's
     block_shared flags when it has them, None passes none, or a tensor."""
     w = b["workload"]
+    scale = float(w.scale) if scale is None else float(scale)
     ps = w.partition_size if partition_size is None else partition_size
     out = torch.empty_like(b["query"]) if out is None else out
     if isinstance(flags, str):
         flags = (torch.from_numpy(b["block_shared"]).to(DEV) if "block_shared" in b
                  else None)
     args = (out, b["query"], b["key_cache"], b["value_cache"], dev_i32(b["block_tables"]),
-            dev_i32(b["context_lens"]), float(w.scale))
+            dev_i32(b["context_lens"]), scale)
     if w.fp8:
         pkv.paged_attention_decode_fp8(*args, w.k_scale, w.v_scale, w.num_kv_heads,
                                        partition_size=ps, block_shared=flags)
@@ -118,9 +119,10 @@ def oracle_pool(b, kc_before, vc_before, ids):
     return kc, vc, remap
 
 
-def oracle_decode_subset(b, kc_before, vc_before, seqs):
+def oracle_decode_subset(b, kc_before, vc_before, seqs, scale=None):
     """Oracle outputs [len(seqs), Hq, D] for the chosen sequences."""
     w = b["workload"]
+    scale = w.scale if scale is None else np.float32(scale)
     ids = blocks_read_by(b, seqs)
     if len(ids) == 0:
         ids = np.zeros(1, np.int64)
@@ -133,10 +135,10 @@ def oracle_decode_subset(b, kc_before, vc_before, seqs):
         tables[i, :n] = [remap[int(x)] for x in bt[s, :n]]
     q = wl.to_host(b["query"])[seqs]
     if w.fp8:
-        return oracle.decode_attention(q, kc, vc, tables, lens, w.scale, w.num_kv_heads,
+        return oracle.decode_attention(q, kc, vc, tables, lens, scale, w.num_kv_heads,
                                        w.dtype, kv_dtype="e4m3", k_scale=w.k_scale,
                                        v_scale=w.v_scale)
-    return oracle.decode_attention(q, kc, vc, tables, lens, w.scale, w.num_kv_heads,
+    return oracle.decode_attention(q, kc, vc, tables, lens, scale, w.num_kv_heads,
                                    w.dtype)
 
 

@@ -128,6 +128,22 @@ def test_sharp_softmax(gpu_lib, dtype, hq, hkv):
     assert_close(out, ref, dtype, f"sharp softmax {dtype} {hq}/{hkv}")
 
 
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 1), (32, 2)])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_any_softmax_scale(gpu_lib, dtype, hq, hkv, scale):
+    """The softmax scale is any float: a negative one weighs each sequence's
+    smallest logits most, zero weighs the visible tokens equally; on the
+    vector and the matrix-core paths, split and whole."""
+    lens = [1, 17, 300, 1000, 2047]
+    w = wl.custom(lens, hq, hkv, 128, dtype, max_len=2048, partition_size=512)
+    b = wl.make_batch(w, 3 + hq + hkv, DEV)
+    kc0, vc0 = clone_pools(b)
+    out = run_decode(b, scale=scale)
+    ref = oracle_decode_subset(b, kc0, vc0, list(range(len(lens))), scale=scale)
+    assert_close(out, ref, dtype, f"scale {scale} {dtype} {hq}/{hkv}")
+
+
 @pytest.mark.parametrize("ps", [16, 48])
 @pytest.mark.parametrize("hq,hkv", [(8, 4), (8, 2), (16, 2), (32, 2), (24, 1)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
